@@ -1,0 +1,81 @@
+"""Seeded synthetic inputs for the dense GEMV c = B @ a.
+
+This module is shared by the tests, the benchmark and the smoke check. It holds
+no GEMV arithmetic: it draws random numbers, casts them to the 16-bit input
+dtype and returns raw bit patterns (numpy ``uint16``). The CPU oracle and the
+HIP library then read exactly the same bits.
+
+Recipe (the pages print no input data; their GEMV workloads are LLM weight
+matrices times an activation vector, TileLang Case Studies, Case B.3 "Shapes
+Added"):
+  * ``torch.Generator().manual_seed(seed)``, B drawn first, then a;
+  * "normal":  B = randn(n, k) / sqrt(k),            a = randn(k);
+  * "uniform": B = (2 * rand(n, k) - 1) / sqrt(k),   a = 2 * rand(k) - 1;
+  * drawn in float32, then cast to fp16/bf16 by torch (round to nearest even).
+"""
+import math
+
+import numpy as np
+import torch
+
+F16 = 0
+BF16 = 1
+DTYPE_NAMES = {F16: "f16", BF16: "bf16"}
+_TORCH_DTYPE = {F16: torch.float16, BF16: torch.bfloat16}
+
+
+def torch_dtype(dtype: int) -> torch.dtype:
+    return _TORCH_DTYPE[dtype]
+
+
+def _to_bits(t: torch.Tensor, dtype: int) -> np.ndarray:
+    return t.to(_TORCH_DTYPE[dtype]).contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def random_inputs(n: int, k: int, dtype: int, dist: str = "normal", seed: int = 0):
+    """Return (B_bits (n, k) uint16, a_bits (k,) uint16)."""
+    g = torch.Generator().manual_seed(seed)
+    scale = 1.0 / math.sqrt(k) if k > 0 else 1.0
+    if dist == "normal":
+        B = torch.randn(n, k, generator=g, dtype=torch.float32) * scale
+        a = torch.randn(k, generator=g, dtype=torch.float32)
+    elif dist == "uniform":
+        B = (torch.rand(n, k, generator=g, dtype=torch.float32) * 2 - 1) * scale
+        a = torch.rand(k, generator=g, dtype=torch.float32) * 2 - 1
+    else:
+        raise ValueError("unknown distribution %r" % dist)
+    return _to_bits(B, dtype), _to_bits(a, dtype)
+
+
+def integer_inputs(n: int, k: int, dtype: int, lo: int = -2, hi: int = 2, seed: int = 0):
+    """Integer-valued B and a, uniform over [lo, hi] (exactly representable)."""
+    g = torch.Generator().manual_seed(seed)
+    B = torch.randint(lo, hi + 1, (n, k), generator=g).to(torch.float32)
+    a = torch.randint(lo, hi + 1, (k,), generator=g).to(torch.float32)
+    return _to_bits(B, dtype), _to_bits(a, dtype)
+
+
+def values_to_bits(values, dtype: int) -> np.ndarray:
+    """Cast float values (already representable, e.g. small integers or
+    hand-picked dyadic values) to 16-bit patterns via torch."""
+    t = torch.as_tensor(np.asarray(values, dtype=np.float32))
+    return _to_bits(t, dtype)
+
+
+# The workloads: (name, n, k, dtype, distribution).  Shapes are LLM projection
+# shapes (TileLang Case Studies, Case B and B.3); the ragged/small-n ones
+# exercise the k tails, misaligned rows and the split-k path.
+TINY = ("tiny_256x512_f16", 256, 512, F16, "uniform")
+PROD_F16 = ("gemv_18432x7168_f16", 18432, 7168, F16, "normal")
+PROD_BF16 = ("gemv_7168x16384_bf16", 7168, 16384, BF16, "normal")
+SWEEP_SHAPES = [(4096, 4096), (11008, 4096), (4096, 11008), (14336, 4096), (4096, 14336)]
+SWEEP = [("sweep_%dx%d_%s" % (n, k, DTYPE_NAMES[d]), n, k, d, "normal")
+         for (n, k) in SWEEP_SHAPES for d in (F16, BF16)]
+RAGGED = [("ragged_%dx%d_bf16" % (n, k), n, k, BF16, "normal")
+          for (n, k) in [(64, 65536), (1000, 7000), (18433, 7169)]]
+ALL_WORKLOADS = [TINY, PROD_F16, PROD_BF16] + SWEEP + RAGGED
+
+
+def algorithmic_bytes(n: int, k: int, elem_bytes: int = 2) -> int:
+    """Bytes a GEMV must move at least once: B, a and c."""
+    return elem_bytes * (n * k + k + n)
