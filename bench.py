@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the dense GEMV c = B @ a on one MI355X.
+
+One step = one gemv_run over one (B, a) pair.  The default workload is
+n=18432, k=7168, fp16 with B ~ N(0,1)/sqrt(k), a ~ N(0,1), seed 0.  Inputs are
+resident in HBM before timing starts; successive steps rotate over copies of
+(B, a, c) that together exceed 1 GiB, so neither the L2 nor the 256 MiB
+Infinity Cache can serve B from one step to the next.
+
+Timing (TileLang Case Studies, Case C: a fixed configuration, no tuning
+inside the measured region):
+  * the timed region: W warmup steps, then a synchronise, K steps, a
+    synchronise, all on one stream; ms_per_step = wall time / K and
+    value = algorithmic bytes per step / ms_per_step;
+  * a HIP event pair on the launch stream brackets the same K launches; the
+    launches queue back to back with no idle gap between kernels (the host
+    enqueues far faster than a kernel runs), so the event time / K is the
+    kernel's average duration: roofline.achieved = algorithmic bytes per
+    launch / that average.  (An event pair around every single launch would
+    add the event packets' own cost to each duration.)
+Algorithmic bytes per step = 2 * (n*k + k + n): B, a and c once each.
+
+Prints ONE JSON line on stdout; human-readable detail goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of MI355X peak) and µs/call, n=18432 k=7168 fp16"
+KERNEL_SOURCES = [os.path.join(ROOT, "memory_bound_dense_amd", "csrc", "gemv_kernel.h"),
+                  os.path.join(ROOT, "memory_bound_dense_amd", "csrc", "gemv.hip")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, n_launch_bytes):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemv_counters_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(B_bits, a_bits, dtype, n, k, target_s=12.0):
+    """The oracle, as it is, on the first rows of the same workload."""
+    import numpy as np
+    import oracle
+    probe = min(n, 8)
+    t0 = time.perf_counter()
+    oracle.gemv(dtype, B_bits[:probe], a_bits)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(max(1, min(n, target_s / max(per_row, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.gemv(dtype, np.ascontiguousarray(B_bits[:rows]), a_bits)
+    dt = time.perf_counter() - t0
+    nbytes = 2 * (rows * k + k + rows)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of %d rows, full k=%d, one call, %.1f s single-threaded "
+                      "(%s)" % (rows, n, k, dt, platform.processor() or platform.machine()),
+            "us_per_row": round(dt / rows * 1e6, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--workload", default="gemv_18432x7168_f16",
+                    help="workload name (see gemv_inputs.ALL_WORKLOADS)")
+    ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (-1 = auto)")
+    ap.add_argument("--grid", type=int, default=0, help="force the workgroup count (0 = auto)")
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the kernel on one GPU's share); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: one process, one GPU; WORLD_SIZE > 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import memory_bound_dense_amd as mbd
+    from gemv_inputs import ALL_WORKLOADS, DTYPE_NAMES, algorithmic_bytes, random_inputs, torch_dtype
+
+    wl = {w[0]: w for w in ALL_WORKLOADS}.get(args.workload)
+    if wl is None:
+        print("unknown workload %r; known: %s" % (args.workload, [w[0] for w in ALL_WORKLOADS]),
+              file=sys.stderr)
+        sys.exit(2)
+    name, n, k, dtype, dist = wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    td = torch_dtype(dtype)
+
+    log("[bench] workload %s n=%d k=%d %s %s; generating inputs" % (name, n, k,
+                                                                    DTYPE_NAMES[dtype], dist))
+    B_bits, a_bits = random_inputs(n, k, dtype, dist, seed=0)
+    B0 = torch.from_numpy(B_bits.view(np.int16)).to(dev).view(td)
+    a0 = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(td)
+    step_bytes = algorithmic_bytes(n, k)
+    nbuf = int(min(64, max(2, math.ceil(args.rotate_bytes / (2.0 * n * k)))))
+    Bs = [B0] + [B0.clone() for _ in range(nbuf - 1)]
+    As = [a0] + [a0.clone() for _ in range(nbuf - 1)]
+    Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]
+    torch.cuda.synchronize()
+
+    g = mbd.Gemv()
+    if args.variant >= 0:
+        g.force_config(args.variant, args.grid)
+    variant, grid = g.query_config(n, k, dtype)
+    _, vinfo = mbd.gemv_variant_info(variant)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    run, h = mbd.gemv_run, g.h
+    ptrs = [(Bs[i].data_ptr(), As[i].data_ptr(), Cs[i].data_ptr()) for i in range(nbuf)]
+    log("[bench] variant %d (rows %d unroll %d waves %d splits %d a_mode %d b_policy %d), "
+        "grid %d, %d rotating buffers of %.1f MB" % (
+            variant, vinfo.rows, vinfo.unroll, vinfo.waves, vinfo.splits, vinfo.a_mode,
+            vinfo.b_policy, grid, nbuf, 2.0 * n * k / 1e6))
+
+    def step(i):
+        b, a, c = ptrs[i % nbuf]
+        s = run(h, b, a, c, n, k, dtype, sp)
+        if s != 0:
+            raise mbd.GemvError(s, "gemv_run")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("[bench] warmup done (%d steps); timing %d steps" % (args.warmup, args.steps))
+
+    # timed region: whole-job throughput, with one event pair on the stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+    avg_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    achieved = step_bytes / (avg_us * 1e-6) / 1e9
+    log("[bench] wall %.2f us/step -> %.1f GB/s; kernel avg %.2f us (HIP events over the timed "
+        "region) -> %.1f GB/s = %.1f%% of %.0f GB/s" % (
+            ms_per_step * 1e3, value, avg_us, achieved, 100 * achieved / HBM_PEAK_GBS,
+            HBM_PEAK_GBS))
+
+    traffic = read_traffic(name, step_bytes)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAMES[dtype],
+        "data": "synthetic",
+        "config": {"workload": name, "n": n, "k": k, "distribution": dist, "seed": 0,
+                   "variant": variant, "grid": grid, "rows_per_wave": vinfo.rows,
+                   "unroll": vinfo.unroll, "waves_per_wg": vinfo.waves, "splits": vinfo.splits,
+                   "a_mode": ["lds", "cached"][vinfo.a_mode], "rotating_buffers": nbuf},
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernel_us_avg": round(avg_us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(B_bits, a_bits, dtype, n, k)
+    g.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

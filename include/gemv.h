@@ -1,0 +1,151 @@
+/*
+ * gemv.h -- C ABI of the MI355X (gfx950) dense GEMV library, libgemv.so.
+ *
+ * Operation (TileLang Case Studies, Case B "Background"): the dense
+ * matrix-vector product
+ *
+ *     c[i] = sum_{j=0}^{k-1} B[i][j] * a[j],      0 <= i < n,
+ *
+ * with B an (n, k) matrix, a a (k,) vector and c an (n,) vector, all of one
+ * 16-bit floating-point dtype (IEEE binary16 or bfloat16).  Products are
+ * summed in fp32 and each c[i] is rounded once, to nearest-even, into the
+ * dtype.  The pages leave the accumulation type and the output rounding
+ * unstated; fp32 accumulation and round-to-nearest-even are this library's
+ * reading.  IEEE special values propagate (NaN in -> NaN out, inf*0 -> NaN,
+ * overflow -> inf); subnormals are kept.
+ *
+ * Layout.  B is row-major and dense: row i starts at element i*k (leading
+ * dimension == k, no stride argument), as in Case B where lanes that walk k
+ * read one contiguous span of a row.  a and c are dense vectors.  Every
+ * pointer is a device pointer on the handle's GPU and needs 2-byte (element)
+ * alignment only; 16-byte alignment of rows is not required.
+ *
+ * Ownership.  B, a and c belong to the caller.  The library never allocates,
+ * frees or keeps them past the call.  c must hold n elements and must not
+ * overlap B or a.  The handle belongs to the library and is released by
+ * gemv_destroy.
+ *
+ * Asynchrony.  gemv_run validates its arguments on the host, enqueues one
+ * kernel on `stream` and returns; it allocates nothing and never
+ * synchronises.  c is valid once the stream reaches that point; B, a and c
+ * must stay alive until then.  All set-up (device query, kernel attributes)
+ * happens in gemv_create, so a call costs one launch (TileLang Case Studies,
+ * Case B.4: build once at construction, only launch per call).
+ *
+ * Errors.  Every function returns a gemv_status_t; nothing throws, aborts or
+ * prints (unless the environment variable GEMV_LOG=1, which prints one line
+ * per rejected call to stderr).  On any error no kernel is launched and c is
+ * left untouched.  Validation order in gemv_run: handle, dtype, n >= 0 and
+ * k >= 0, n == 0 (success, no launch), null pointers (c always, B and a when
+ * k > 0; with k == 0 neither is read), alignment, size limits, overlap of c
+ * with B or a, current device == handle device; then the launch, whose
+ * failure is GEMV_ERR_HIP.
+ *
+ * Threading.  A handle is read-only after gemv_create (gemv_force_config
+ * aside), so concurrent gemv_run calls on different streams are safe.
+ */
+#ifndef MBD_GEMV_H
+#define MBD_GEMV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gemv_handle_s* gemv_handle_t;
+
+typedef enum {
+  GEMV_F16 = 0,   /* IEEE-754 binary16 */
+  GEMV_BF16 = 1   /* bfloat16 (upper half of binary32) */
+} gemv_dtype_t;
+
+typedef enum {
+  GEMV_OK = 0,
+  GEMV_ERR_NULL_HANDLE = 1,       /* handle is NULL or already destroyed */
+  GEMV_ERR_INVALID_ARG = 2,       /* negative size, NULL pointer, bad config */
+  GEMV_ERR_UNSUPPORTED_DTYPE = 3, /* dtype is not GEMV_F16 / GEMV_BF16 */
+  GEMV_ERR_MISALIGNED = 4,        /* a pointer is not 2-byte aligned */
+  GEMV_ERR_ALIASING = 5,          /* c overlaps B or a */
+  GEMV_ERR_TOO_LARGE = 6,         /* n > 2^30 or k > 2^27 */
+  GEMV_ERR_WRONG_DEVICE = 7,      /* current HIP device != the handle's */
+  GEMV_ERR_UNSUPPORTED = 8,       /* no kernel for this GPU / configuration */
+  GEMV_ERR_HIP = 9,               /* a HIP runtime call failed */
+  GEMV_ERR_OOM = 10               /* host allocation of the handle failed */
+} gemv_status_t;
+
+/* Largest sizes gemv_run accepts. */
+#define GEMV_MAX_N 1073741824LL
+#define GEMV_MAX_K 134217728LL
+
+/* Create a handle bound to the current HIP device.  Queries the device (it
+ * must be a gfx950), sets kernel attributes and fixes the variant table.
+ * *out receives the handle, or NULL on error. */
+gemv_status_t gemv_create(gemv_handle_t* out);
+
+/* c = B @ a on `stream` (0 = the null stream).  B: n*k elements, row-major;
+ * a: k elements; c: n elements; all of `dtype`, on the handle's device.
+ * n == 0 is a no-op; k == 0 writes zeros (the empty sum) into c. */
+gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a, void* c,
+                       int64_t n, int64_t k, gemv_dtype_t dtype, hipStream_t stream);
+
+/* Every check gemv_run makes that needs neither a handle nor a GPU, in the
+ * same order and with the same result: GEMV_OK means gemv_run would go on to
+ * the device check and the launch (or return GEMV_OK at once when n == 0).
+ * Pure host arithmetic on the pointer values; nothing is dereferenced. */
+gemv_status_t gemv_check_args(const void* B, const void* a, const void* c, int64_t n, int64_t k,
+                              gemv_dtype_t dtype);
+
+/* Release the handle.  NULL is a no-op.  Outstanding work on streams is not
+ * affected (the handle owns no device memory). */
+gemv_status_t gemv_destroy(gemv_handle_t h);
+
+/* Static, human-readable name of a status code. */
+const char* gemv_status_string(gemv_status_t s);
+
+/* ---- kernel variants (for benchmarking and tuning; Case C: profile with a
+ *      fixed configuration, never with autotuning inside the trace) ------- */
+
+/* Shape of one compiled kernel variant.  A workgroup has `waves` 64-lane
+ * wavefronts arranged as (waves / splits) row groups x `splits` k-slices; a
+ * row group owns `rows` consecutive rows; each wave streams its rows of B
+ * with 16-byte loads along k, `unroll` 512-element steps per loop trip.
+ * a_mode 0: a is staged once per workgroup in LDS; 1: a is read through the
+ * cache hierarchy with the same 16-byte loads.  splits > 1 sums the k-slices
+ * of a row group in a fixed order through LDS (deterministic). */
+typedef struct {
+  int32_t rows;
+  int32_t unroll;
+  int32_t waves;
+  int32_t splits;
+  int32_t a_mode;
+  int32_t b_policy;   /* cache-policy bits of the B loads (0 = default) */
+} gemv_variant_info_t;
+
+typedef struct {
+  int32_t variant;    /* index in [0, gemv_num_variants()), or -1 = automatic */
+  int32_t grid;       /* workgroups to launch; 0 = one per row block */
+} gemv_config_t;
+
+/* Number of compiled variants. */
+int32_t gemv_num_variants(void);
+
+/* Describe variant `v`; GEMV_ERR_INVALID_ARG if out of range or info NULL. */
+gemv_status_t gemv_variant_info(int32_t v, gemv_variant_info_t* info);
+
+/* Force a configuration on every later gemv_run of this handle (NULL or
+ * variant -1 restores automatic selection).  Not thread-safe with concurrent
+ * gemv_run calls on the same handle. */
+gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t* cfg);
+
+/* The configuration gemv_run would use for (n, k, dtype) on this handle.
+ * grid is reported as the number of workgroups actually launched. */
+gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k, gemv_dtype_t dtype,
+                                gemv_config_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBD_GEMV_H */

@@ -1,0 +1,202 @@
+"""ctypes binding of libgemv.so (include/gemv.h).
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  The functions keep the C names and return the C status codes;
+``Gemv`` wraps a handle for torch tensors (torch supplies device memory and
+streams) and raises ``GemvError`` on any status other than GEMV_OK.
+
+There is no fallback: if the library is missing or cannot be loaded, every
+entry point raises.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgemv.so")
+
+GEMV_F16 = 0
+GEMV_BF16 = 1
+
+GEMV_OK = 0
+GEMV_ERR_NULL_HANDLE = 1
+GEMV_ERR_INVALID_ARG = 2
+GEMV_ERR_UNSUPPORTED_DTYPE = 3
+GEMV_ERR_MISALIGNED = 4
+GEMV_ERR_ALIASING = 5
+GEMV_ERR_TOO_LARGE = 6
+GEMV_ERR_WRONG_DEVICE = 7
+GEMV_ERR_UNSUPPORTED = 8
+GEMV_ERR_HIP = 9
+GEMV_ERR_OOM = 10
+
+GEMV_MAX_N = 1073741824
+GEMV_MAX_K = 134217728
+
+# every symbol include/gemv.h declares
+EXPORTS = ("gemv_create", "gemv_run", "gemv_destroy", "gemv_status_string", "gemv_check_args",
+           "gemv_num_variants", "gemv_variant_info", "gemv_force_config", "gemv_query_config")
+
+
+class GemvError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__("%s%s" % (gemv_status_string(status), (": " + what) if what else ""))
+
+
+class gemv_variant_info_t(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("unroll", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("splits", ctypes.c_int32), ("a_mode", ctypes.c_int32),
+                ("b_policy", ctypes.c_int32)]
+
+
+class gemv_config_t(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("grid", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load():
+    """Load libgemv.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgemv.so is not built (%s); run "
+                           "`python -m memory_bound_dense_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    st = ctypes.c_int
+    lib.gemv_create.argtypes = [ctypes.POINTER(vp)]
+    lib.gemv_create.restype = st
+    lib.gemv_run.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int, vp]
+    lib.gemv_run.restype = st
+    lib.gemv_destroy.argtypes = [vp]
+    lib.gemv_destroy.restype = st
+    lib.gemv_status_string.argtypes = [st]
+    lib.gemv_status_string.restype = ctypes.c_char_p
+    lib.gemv_check_args.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int]
+    lib.gemv_check_args.restype = st
+    lib.gemv_num_variants.argtypes = []
+    lib.gemv_num_variants.restype = i32
+    lib.gemv_variant_info.argtypes = [i32, ctypes.POINTER(gemv_variant_info_t)]
+    lib.gemv_variant_info.restype = st
+    lib.gemv_force_config.argtypes = [vp, ctypes.POINTER(gemv_config_t)]
+    lib.gemv_force_config.restype = st
+    lib.gemv_query_config.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.POINTER(gemv_config_t)]
+    lib.gemv_query_config.restype = st
+    _lib = lib
+    return lib
+
+
+# ---- the C entry points, same names ------------------------------------------
+
+def gemv_create():
+    """Returns (status, handle) -- handle is a ctypes.c_void_p."""
+    h = ctypes.c_void_p()
+    s = load().gemv_create(ctypes.byref(h))
+    return s, h
+
+
+def gemv_run(h, B, a, c, n, k, dtype, stream=None):
+    """B, a, c: device addresses (ints); stream: hipStream_t as int or None."""
+    return load().gemv_run(h, B, a, c, n, k, dtype, stream)
+
+
+def gemv_destroy(h):
+    return load().gemv_destroy(h)
+
+
+def gemv_status_string(s):
+    return load().gemv_status_string(s).decode()
+
+
+def gemv_check_args(B, a, c, n, k, dtype):
+    return load().gemv_check_args(B, a, c, n, k, dtype)
+
+
+def gemv_num_variants():
+    return load().gemv_num_variants()
+
+
+def gemv_variant_info(v):
+    info = gemv_variant_info_t()
+    s = load().gemv_variant_info(v, ctypes.byref(info))
+    return s, info
+
+
+def gemv_force_config(h, variant=-1, grid=0):
+    if variant is None:
+        return load().gemv_force_config(h, None)
+    cfg = gemv_config_t(variant, grid)
+    return load().gemv_force_config(h, ctypes.byref(cfg))
+
+
+def gemv_query_config(h, n, k, dtype):
+    cfg = gemv_config_t()
+    s = load().gemv_query_config(h, n, k, dtype, ctypes.byref(cfg))
+    return s, cfg
+
+
+# ---- torch-tensor convenience ------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return GEMV_F16
+    if t.dtype == torch.bfloat16:
+        return GEMV_BF16
+    raise GemvError(GEMV_ERR_UNSUPPORTED_DTYPE, str(t.dtype))
+
+
+class Gemv:
+    """One handle on the current device.  ``gemv(B, a, c)`` enqueues c = B @ a
+    on the current torch stream (or ``stream``); tensors must be dense."""
+
+    def __init__(self):
+        s, h = gemv_create()
+        if s != GEMV_OK:
+            raise GemvError(s, "gemv_create")
+        self.h = h
+
+    def close(self):
+        if self.h is not None:
+            gemv_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def force_config(self, variant=-1, grid=0):
+        s = gemv_force_config(self.h, variant, grid)
+        if s != GEMV_OK:
+            raise GemvError(s, "gemv_force_config")
+
+    def query_config(self, n, k, dtype):
+        s, cfg = gemv_query_config(self.h, n, k, dtype)
+        if s != GEMV_OK:
+            raise GemvError(s, "gemv_query_config")
+        return cfg.variant, cfg.grid
+
+    def __call__(self, B, a, c, stream=None):
+        import torch
+        if B.dim() != 2 or a.dim() != 1 or c.dim() != 1:
+            raise GemvError(GEMV_ERR_INVALID_ARG, "B must be 2-D, a and c 1-D")
+        n, k = B.shape
+        if a.shape[0] != k or c.shape[0] != n:
+            raise GemvError(GEMV_ERR_INVALID_ARG, "shapes B%s a%s c%s" % (
+                tuple(B.shape), tuple(a.shape), tuple(c.shape)))
+        if not (B.is_contiguous() and a.is_contiguous() and c.is_contiguous()):
+            raise GemvError(GEMV_ERR_INVALID_ARG, "tensors must be contiguous")
+        dt = _dtype_code(B)
+        if a.dtype != B.dtype or c.dtype != B.dtype:
+            raise GemvError(GEMV_ERR_UNSUPPORTED_DTYPE, "B, a and c must share one dtype")
+        if stream is None:
+            stream = torch.cuda.current_stream(B.device).cuda_stream
+        s = gemv_run(self.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, dt, stream)
+        if s != GEMV_OK:
+            raise GemvError(s, "gemv_run")
+        return c

@@ -1,0 +1,265 @@
+// Dense GEMV kernels for gfx950 (CDNA4): c = B @ a, fp16/bf16 in, fp32 sum.
+//
+// The product is bound by HBM bandwidth: every element of B is read exactly
+// once and used once, about one flop per byte, so the design goal is to keep
+// enough 16-byte loads of B in flight on every CU and to do nothing else
+// expensive.  No matrix cores: this is not a contraction worth tiling.
+//
+// Mapping (the lanes-along-k layout that TileLang Case Studies, Case B, shows
+// is the one that coalesces; here sized for 64-lane wavefronts):
+//   * a workgroup has WAVES wavefronts, arranged as G = WAVES/S row groups
+//     times S k-slices;
+//   * a row group owns R consecutive rows; the wave streams those R rows, and
+//     lane l of the wave reads elements [8*(64*t + l), +8) of each row at step
+//     t -- one 16-byte load per lane, 1 KiB contiguous per row per wave;
+//   * U steps are unrolled, so a wave keeps R*U KiB of B in flight;
+//   * a is either staged once per workgroup in LDS (A_LDS; Case B.2 is the
+//     shared-memory variant of this choice) or read with the same 16-byte
+//     loads through the caches (A_CACHED);
+//   * each lane keeps fp32 partial sums; the 64 lane partials of a row are
+//     combined with DPP row operations and two cross-row swaps;
+//   * with S > 1 the k-slices of a row group are summed through LDS in slice
+//     order (fixed order, so results do not depend on timing).
+//
+// Loads go through buffer resources: the row base is a wave-uniform 64-bit
+// address in SGPRs, the per-row offset is an SGPR soffset and the lane offset
+// a single VGPR shared by all rows, and the range check of the descriptor
+// bounds every access to the rows the wave owns.  Rows are only 2-byte
+// aligned when k is not a multiple of 8; the 16-byte loads then rely on the
+// unaligned buffer access that ROCm enables for compute queues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mbd {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+enum { A_LDS = 0, A_CACHED = 1 };
+
+constexpr int kLanes = 64;
+constexpr int kVec = 8;                 // 16-bit elements per 16-byte load
+constexpr int kStep = kLanes * kVec;    // elements per row per wave-load
+constexpr int kStepBytes = kStep * 2;   // 1 KiB
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+// Element-wise load of the 8-element vector starting at element e0 of a row:
+// the full 16 bytes when the vector lies inside the row, otherwise the
+// elements below `len` one by one and zeros above.  Only the last vector of a
+// row takes the slow branch.
+__device__ __forceinline__ u32x4 load_vec_tail(__amdgpu_buffer_rsrc_t rsrc, int e0, int len,
+                                               uint32_t soff) {
+  if (e0 + kVec <= len) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rsrc, e0 * 2, soff, 0);
+  }
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (e0 < len) {
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      if (e0 + i < len) {
+        uint32_t x = __builtin_amdgcn_raw_buffer_load_b16(rsrc, (e0 + i) * 2, soff, 0);
+        w[i >> 1] |= x << ((i & 1) * 16);
+      }
+    }
+  }
+  u32x4 v = {w[0], w[1], w[2], w[3]};
+  return v;
+}
+
+// acc0 += sum of the even products, acc1 += sum of the odd products of the
+// 8-element vectors b and a (fp32, each product exact, one rounding per add).
+template <int DT>
+__device__ __forceinline__ void fma8(const u32x4& b, const u32x4& a, float& acc0, float& acc1) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // Copy the component to a scalar first: a bit_cast applied directly to
+    // an ext-vector element reads component 0 whatever the index.
+    const uint32_t bw = b[i];
+    const uint32_t aw = a[i];
+    if constexpr (DT == DT_F16) {
+      f16x2 bb = __builtin_bit_cast(f16x2, bw);
+      f16x2 aa = __builtin_bit_cast(f16x2, aw);
+      acc0 = __builtin_fmaf((float)bb.x, (float)aa.x, acc0);
+      acc1 = __builtin_fmaf((float)bb.y, (float)aa.y, acc1);
+    } else {
+      // bfloat16 is the upper half of a binary32: widening is a shift/mask.
+      float blo = __builtin_bit_cast(float, bw << 16);
+      float bhi = __builtin_bit_cast(float, bw & 0xffff0000u);
+      float alo = __builtin_bit_cast(float, aw << 16);
+      float ahi = __builtin_bit_cast(float, aw & 0xffff0000u);
+      acc0 = __builtin_fmaf(blo, alo, acc0);
+      acc1 = __builtin_fmaf(bhi, ahi, acc1);
+    }
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_get(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes; every lane receives the same bits.  Each step adds a
+// value and its mirror partner, so partial sums stay symmetric in the lanes.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_get<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
+  v += dpp_get<0x4E>(v);    // quad_perm [2,3,0,1]: quads
+  v += dpp_get<0x141>(v);   // row_half_mirror: groups of 8
+  v += dpp_get<0x140>(v);   // row_mirror: rows of 16
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+template <int DT>
+__device__ __forceinline__ uint16_t to_bits(float x) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);   // v_cvt_f16_f32, nearest-even
+  } else {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);     // v_cvt_pk_bf16_f32, nearest-even
+  }
+}
+
+template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL>
+__global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
+    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
+    int n, int k, int nrb) {
+  static_assert(WAVES % S == 0, "splits must divide the waves of a workgroup");
+  constexpr int G = WAVES / S;   // row groups per workgroup
+  constexpr int RB = G * R;      // rows per workgroup per row block
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int lane = threadIdx.x & (kLanes - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = wave / S;
+  const int sl = wave - rg * S;
+
+  const int nfull = k >> 9;              // full 512-element steps
+  const int rem = k & (kStep - 1);       // elements of the last, partial step
+  const int nsteps = nfull + (rem != 0);
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a, (uint32_t)k * 2u);
+
+  u32x4* a_lds = reinterpret_cast<u32x4*>(smem);
+  float* part = reinterpret_cast<float*>(smem + (AMODE == A_LDS ? nsteps * kStepBytes : 0));
+
+  if constexpr (AMODE == A_LDS) {
+    // a, zero-padded to whole steps, once per workgroup.
+    for (int v = threadIdx.x; v < nsteps * kLanes; v += WAVES * kLanes) {
+      a_lds[v] = load_vec_tail(arsrc, v * kVec, k, 0u);
+    }
+    __syncthreads();
+  }
+
+  // this wave's share of the full steps; the partial step goes to the last slice
+  const int t0 = (int)(((int64_t)nfull * sl) / S);
+  const int t1 = (int)(((int64_t)nfull * (sl + 1)) / S);
+  const bool tail = (rem != 0) && (sl == S - 1);
+  const int lane_off = lane * 16;
+
+  for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
+    const int row0 = rb * RB + rg * R;
+    if (S == 1 && row0 >= n) continue;   // wave-uniform; no barrier below when S == 1
+    const int rbase = row0 < n ? row0 : n - 1;
+    const int nrows = (n - rbase) < R ? (n - rbase) : R;   // >= 1
+    const __amdgpu_buffer_rsrc_t brsrc =
+        make_rsrc(B + (int64_t)rbase * k, (uint32_t)nrows * (uint32_t)k * 2u);
+    uint32_t soff[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) soff[r] = (uint32_t)(r < nrows ? r : nrows - 1) * (uint32_t)k * 2u;
+
+    float acc[R][2];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.0f;
+
+    int t = t0;
+    for (; t + U <= t1; t += U) {
+      u32x4 bv[U][R];
+      u32x4 av[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          bv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, (t + u) * kStepBytes + lane_off,
+                                                           soff[r], BPOL);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if constexpr (AMODE == A_LDS) {
+          av[u] = a_lds[(t + u) * kLanes + lane];
+        } else {
+          av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, (t + u) * kStepBytes + lane_off, 0u, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
+      }
+    }
+    for (; t < t1; ++t) {
+      u32x4 bv[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        bv[r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, t * kStepBytes + lane_off, soff[r], BPOL);
+      }
+      u32x4 av;
+      if constexpr (AMODE == A_LDS) {
+        av = a_lds[t * kLanes + lane];
+      } else {
+        av = __builtin_amdgcn_raw_buffer_load_b128(arsrc, t * kStepBytes + lane_off, 0u, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) fma8<DT>(bv[r], av, acc[r][0], acc[r][1]);
+    }
+    if (tail) {
+      const int e0 = (nfull * kLanes + lane) * kVec;
+      u32x4 av;
+      if constexpr (AMODE == A_LDS) {
+        av = a_lds[nfull * kLanes + lane];
+      } else {
+        av = load_vec_tail(arsrc, e0, k, 0u);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        u32x4 bv = load_vec_tail(brsrc, e0, k, soff[r]);
+        fma8<DT>(bv, av, acc[r][0], acc[r][1]);
+      }
+    }
+
+    float tot[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) tot[r] = wave_sum(acc[r][0] + acc[r][1]);
+
+    if constexpr (S == 1) {
+      float mine = tot[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) mine = (lane == r) ? tot[r] : mine;
+      if (lane < R && row0 + lane < n) c[row0 + lane] = to_bits<DT>(mine);
+    } else {
+      if (lane < R) {
+        float mine = tot[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) mine = (lane == r) ? tot[r] : mine;
+        part[(rg * S + sl) * R + lane] = mine;
+      }
+      __syncthreads();
+      if (sl == 0 && lane < R && row0 + lane < n) {
+        float s = 0.0f;
+        for (int q = 0; q < S; ++q) s += part[(rg * S + q) * R + lane];
+        c[row0 + lane] = to_bits<DT>(s);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace mbd

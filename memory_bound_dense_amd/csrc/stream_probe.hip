@@ -1,0 +1,69 @@
+// Streaming-read probe: how fast can this GPU read a buffer it does not
+// reuse?  Every lane reads 16-byte vectors, a workgroup-stride loop covers the
+// buffer, and each workgroup folds what it read into one checksum so the
+// loads cannot be dropped.  Measurement aid only (include/stream_probe.h).
+#include "stream_probe.h"
+
+#include <hip/hip_runtime.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int POL>
+__global__ __launch_bounds__(kThreads) void stream_read(const uint8_t* __restrict__ src,
+                                                        uint64_t nvec, uint32_t* __restrict__ out) {
+  uint32_t acc = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads * kUnroll;
+  for (uint64_t base = (uint64_t)blockIdx.x * kThreads * kUnroll; base < nvec; base += stride) {
+    // one descriptor per whole 16 KiB chunk (the host only accepts whole
+    // chunks), so every offset below is inside the buffer
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(src + base * 16u), (short)0, kThreads * kUnroll * 16, kRsrcWord3);
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t off = ((uint32_t)u * kThreads + threadIdx.x) * 16u;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0u, POL);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t x0 = v[u][0], x1 = v[u][1], x2 = v[u][2], x3 = v[u][3];
+      acc += x0 ^ x1 ^ x2 ^ x3;
+    }
+  }
+  __shared__ uint32_t red[kThreads];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t s = 0;
+    for (int i = 0; i < kThreads; ++i) s += red[i];
+    out[blockIdx.x] = s;
+  }
+}
+
+}  // namespace
+
+extern "C" int mbd_stream_read(const void* src, size_t bytes, uint32_t* out, int out_len, int grid,
+                               int nontemporal, hipStream_t stream, int* launched) {
+  if (!src || !out || out_len < 1 || bytes == 0 || (bytes % (kThreads * kUnroll * 16)) != 0 ||
+      ((uintptr_t)src % 16) != 0 || grid < 0)
+    return -1;
+  const uint64_t nvec = bytes / 16;
+  const uint64_t per_wg = (uint64_t)kThreads * kUnroll;
+  uint64_t g = grid > 0 ? (uint64_t)grid : (nvec + per_wg - 1) / per_wg;
+  if (g > (1u << 20)) g = 1u << 20;
+  if (g < 1) g = 1;
+  if (g > (uint64_t)out_len) return -1;
+  if (launched) *launched = (int)g;
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read<2>, dim3((unsigned)g), dim3(kThreads), 0, stream,
+                       (const uint8_t*)src, nvec, out);
+  else
+    hipLaunchKernelGGL(stream_read<0>, dim3((unsigned)g), dim3(kThreads), 0, stream,
+                       (const uint8_t*)src, nvec, out);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}

@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects every bad argument with the documented status before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_bound_dense_amd as mbd
+from memory_bound_dense_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemv.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(0, 11):
+        s = mbd.gemv_status_string(code)
+        assert s.startswith("GEMV_"), s
+    assert mbd.gemv_status_string(0) == "GEMV_OK"
+    assert mbd.gemv_status_string(5) == "GEMV_ERR_ALIASING"
+    assert mbd.gemv_status_string(99) == "GEMV_ERR_UNKNOWN"
+
+
+def test_variant_table():
+    nv = mbd.gemv_num_variants()
+    assert nv >= 4
+    for v in range(nv):
+        s, info = mbd.gemv_variant_info(v)
+        assert s == mbd.GEMV_OK
+        assert info.rows >= 1 and info.unroll >= 1 and info.waves >= 1
+        assert info.splits >= 1 and info.waves % info.splits == 0
+        assert info.a_mode in (0, 1)
+    assert mbd.gemv_variant_info(nv)[0] == _lib.GEMV_ERR_INVALID_ARG
+    assert mbd.gemv_variant_info(-1)[0] == _lib.GEMV_ERR_INVALID_ARG
+
+
+def test_null_handle_rejected():
+    assert mbd.gemv_run(None, 256, 512, 1 << 20, 4, 8, 0, None) == _lib.GEMV_ERR_NULL_HANDLE
+    assert mbd.gemv_force_config(None, 0, 0) == _lib.GEMV_ERR_NULL_HANDLE
+    assert mbd.gemv_query_config(None, 4, 8, 0)[0] == _lib.GEMV_ERR_NULL_HANDLE
+    assert mbd.gemv_destroy(None) == mbd.GEMV_OK
+
+
+def test_create_without_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    s, h = mbd.gemv_create()
+    assert s in (_lib.GEMV_ERR_HIP, _lib.GEMV_ERR_UNSUPPORTED)
+    assert not h.value
+
+
+# Fake, well-separated device addresses: gemv_check_args never dereferences.
+B0, A0, C0 = 1 << 32, 1 << 34, 1 << 36
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((B0, A0, C0, 4, 8, 0), _lib.GEMV_OK),
+    ((B0, A0, C0, 4, 8, 1), _lib.GEMV_OK),
+    ((B0, A0, C0, 4, 8, 2), _lib.GEMV_ERR_UNSUPPORTED_DTYPE),
+    ((B0, A0, C0, 4, 8, -1), _lib.GEMV_ERR_UNSUPPORTED_DTYPE),
+    ((B0, A0, C0, -1, 8, 0), _lib.GEMV_ERR_INVALID_ARG),
+    ((B0, A0, C0, 4, -8, 0), _lib.GEMV_ERR_INVALID_ARG),
+    ((0, 0, 0, 0, 8, 0), _lib.GEMV_OK),                     # n == 0: no-op before pointer checks
+    ((0, A0, C0, 4, 8, 0), _lib.GEMV_ERR_INVALID_ARG),      # null B
+    ((B0, A0, 0, 4, 8, 0), _lib.GEMV_ERR_INVALID_ARG),      # null c
+    ((B0, 0, C0, 4, 8, 0), _lib.GEMV_ERR_INVALID_ARG),      # null a with k > 0
+    ((B0, 0, C0, 4, 0, 0), _lib.GEMV_OK),                   # a unused when k == 0
+    ((0, 0, C0, 4, 0, 0), _lib.GEMV_OK),                    # nor B
+    ((B0 + 1, A0 + 1, C0, 4, 0, 0), _lib.GEMV_OK),          # nor their alignment
+    ((B0, A0, 0, 4, 0, 0), _lib.GEMV_ERR_INVALID_ARG),      # c is written: never NULL
+    ((B0 + 1, A0, C0, 4, 8, 0), _lib.GEMV_ERR_MISALIGNED),
+    ((B0, A0 + 1, C0, 4, 8, 0), _lib.GEMV_ERR_MISALIGNED),
+    ((B0, A0, C0 + 1, 4, 8, 0), _lib.GEMV_ERR_MISALIGNED),
+    ((B0 + 2, A0 + 6, C0 + 14, 4, 8, 0), _lib.GEMV_OK),     # 2-byte alignment is enough
+    ((B0, A0, C0, 2 ** 30 + 1, 8, 0), _lib.GEMV_ERR_TOO_LARGE),
+    ((B0, A0, C0, 4, 2 ** 27 + 1, 0), _lib.GEMV_ERR_TOO_LARGE),
+    ((B0, A0, C0, 4, 2 ** 27, 0), _lib.GEMV_OK),
+    ((B0, A0, B0 + 16, 4, 8, 0), _lib.GEMV_ERR_ALIASING),   # c inside B
+    ((B0, A0, B0 - 6, 4, 8, 0), _lib.GEMV_ERR_ALIASING),    # c straddles B's start
+    ((B0, A0, B0 - 8, 4, 8, 0), _lib.GEMV_OK),              # c ends where B starts
+    ((B0, A0, B0 + 64, 4, 8, 0), _lib.GEMV_OK),             # c starts where B ends
+    ((B0, A0, A0 + 2, 4, 8, 0), _lib.GEMV_ERR_ALIASING),    # c overlaps a
+])
+def test_check_args(args, expect):
+    assert mbd.gemv_check_args(*args) == expect
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        _lib.load()

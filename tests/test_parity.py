@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded input bits.
+
+* small and ragged shapes (several tiles, k tails, misaligned rows, row
+  tails), every compiled variant, full oracle;
+* integer inputs: every variant bit-exact (the fp32 sum is exact);
+* closed forms on the GPU: identity, permutation, one-hot columns;
+* every workload shape at full size, sampled rows, in the automatic
+  configuration the benchmark times and in every variant;
+* determinism, misaligned base pointers, special values, empty and tiny
+  sizes, rejected calls that must not touch c.
+"""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_dense_amd as mbd
+import oracle
+from gemv_inputs import (ALL_WORKLOADS, BF16, F16, integer_inputs, random_inputs, torch_dtype,
+                         values_to_bits)
+from parity import compare, oracle_rows, sample_rows, to_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+NV = mbd.gemv_num_variants()
+VARIANTS = list(range(NV))
+
+
+def _splits(v):
+    return mbd.gemv_variant_info(v)[1].splits
+
+
+@pytest.fixture(scope="module")
+def g():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    h = mbd.Gemv()
+    yield h
+    h.close()
+
+
+def run(g, Bd, ad, variant=-1, grid=0):
+    n, k = Bd.shape
+    c = torch.full((n,), float("nan"), dtype=Bd.dtype, device=Bd.device)
+    g.force_config(variant, grid)
+    try:
+        g(Bd, ad, c)
+    finally:
+        g.force_config(-1)
+    torch.cuda.synchronize()
+    return to_bits(c)
+
+
+def _check(dtype, got, ref, ab, k, v, what):
+    ok_g, ok_s, rg, rs, first = compare(dtype, got, ref, ab, k, _splits(v) if v >= 0 else 16)
+    assert ok_g, "%s variant %d: outside the grading tolerance (%s)" % (what, v, first)
+    assert ok_s, "%s variant %d: outside the strict fp32 bound (max ratio %.3g, %s)" % (
+        what, v, rs, first)
+
+
+SMALL = [(256, 512, F16, "uniform"), (256, 512, BF16, "uniform"),
+         (100, 1000, F16, "normal"), (129, 1537, BF16, "normal"),
+         (37, 7169, F16, "normal"), (37, 7169, BF16, "normal"),
+         (1000, 7000, BF16, "normal"), (300, 4096, F16, "normal"),
+         (64, 65536, BF16, "normal"), (3, 513, F16, "normal"), (1, 8, BF16, "normal"),
+         (7, 1, F16, "normal"), (5, 511, BF16, "normal")]
+
+
+@pytest.mark.parametrize("n,k,dtype,dist", SMALL,
+                         ids=["%dx%d_%s" % (n, k, "f16" if d == F16 else "bf16")
+                              for n, k, d, _ in SMALL])
+def test_small_shapes_every_variant(g, n, k, dtype, dist):
+    B, a = random_inputs(n, k, dtype, dist, seed=0)
+    ref, _, ab = oracle.gemv(dtype, B, a)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    for v in [-1] + VARIANTS:
+        got = run(g, Bd, ad, v)
+        _check(dtype, got, ref, ab, k, v, "%dx%d" % (n, k))
+
+
+INT_SHAPES = [(256, 512), (50, 7169), (1000, 7000), (64, 65536), (33, 100), (5, 8), (129, 1031)]
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("n,k", INT_SHAPES, ids=["%dx%d" % s for s in INT_SHAPES])
+def test_integer_inputs_bit_exact_every_variant(g, n, k, dtype):
+    B, a = integer_inputs(n, k, dtype, seed=13)
+    ref, _, _ = oracle.gemv(dtype, B, a)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    for v in [-1] + VARIANTS:
+        got = run(g, Bd, ad, v)
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, "variant %d rows %s: gpu %s ref %s" % (
+            v, bad[:5], got[bad[:5]], ref[bad[:5]])
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
+def test_identity_and_permutation(g, dtype):
+    for n, k in [(520, 520), (37, 7169), (200, 1031)]:
+        rng = np.random.default_rng(n + k)
+        cols = rng.choice(k, size=n, replace=n > k)
+        cols[0], cols[-1] = 0, k - 1
+        Bv = np.zeros((n, k), dtype=np.float32)
+        Bv[np.arange(n), cols] = 1.0
+        _, a = random_inputs(1, k, dtype, seed=5)
+        Bd, ad = to_device(values_to_bits(Bv, dtype), dtype), to_device(a, dtype)
+        for v in [-1] + VARIANTS:
+            got = run(g, Bd, ad, v)
+            assert np.array_equal(got, a[cols]), (n, k, v)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
+def test_column_extraction(g, dtype):
+    for n, k in [(19, 71), (130, 1031), (9, 7169), (4, 65536)]:
+        B, _ = random_inputs(n, k, dtype, seed=7)
+        Bd = to_device(B, dtype)
+        rng = np.random.default_rng(k)
+        cols = sorted(set(list(range(9)) + list(range(max(0, k - 9), k))
+                          + [int(x) for x in rng.integers(0, k, 6)]
+                          + [j for j in (511, 512, 513) if j < k]))
+        for j in cols:
+            av = np.zeros(k, dtype=np.float32)
+            av[j] = 1.0
+            ad = to_device(values_to_bits(av, dtype), dtype)
+            for v in [-1, 0, 3, 6, NV - 1]:
+                got = run(g, Bd, ad, v)
+                assert np.array_equal(got, B[:, j]), (n, k, j, v)
+
+
+@pytest.mark.parametrize("wl", ALL_WORKLOADS, ids=[w[0] for w in ALL_WORKLOADS])
+def test_workload_full_size(g, wl):
+    name, n, k, dtype, dist = wl
+    B, a = random_inputs(n, k, dtype, dist, seed=0)
+    rows = sample_rows(n)
+    ref, _, ab = oracle_rows(dtype, B, a, rows)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    del B
+    for v in [-1] + VARIANTS:
+        got = run(g, Bd, ad, v)[rows]
+        _check(dtype, got, ref, ab, k, v, name)
+
+
+def test_deterministic(g):
+    for n, k, dtype in [(7168, 16384, BF16), (64, 65536, BF16), (1000, 7000, F16)]:
+        B, a = random_inputs(n, k, dtype, seed=1)
+        Bd, ad = to_device(B, dtype), to_device(a, dtype)
+        for v in [-1, 3, NV - 1]:
+            first = run(g, Bd, ad, v)
+            for _ in range(20):
+                assert np.array_equal(run(g, Bd, ad, v), first), (n, k, v)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
+def test_misaligned_base_pointers(g, dtype):
+    n, k = 77, 1000
+    B, a = random_inputs(n, k, dtype, seed=3)
+    ref, _, ab = oracle.gemv(dtype, B, a)
+    # shift each buffer by one element so that no base is 16-byte aligned
+    Bbig = to_device(np.concatenate([np.zeros(1, np.uint16), B.ravel()]), dtype)
+    abig = to_device(np.concatenate([np.zeros(3, np.uint16), a]), dtype)
+    Bd = Bbig[1:].view(n, k)
+    ad = abig[3:]
+    assert Bd.data_ptr() % 16 != 0 and ad.data_ptr() % 16 != 0
+    for v in [-1] + VARIANTS:
+        cbig = torch.full((n + 5,), 7.0, dtype=torch_dtype(dtype), device="cuda")
+        c = cbig[5:]
+        g.force_config(v)
+        g(Bd, ad, c)
+        g.force_config(-1)
+        torch.cuda.synchronize()
+        _check(dtype, to_bits(c), ref, ab, k, v, "misaligned")
+        assert torch.all(cbig[:5] == 7.0)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
+def test_special_values(g, dtype):
+    inf, nan = np.inf, np.nan
+    k = 1100
+    rng = np.random.default_rng(0)
+    Bv = rng.integers(-3, 4, size=(8, k)).astype(np.float32)
+    Bv[1, 700] = nan
+    Bv[2, 5] = inf
+    Bv[3, 5], Bv[3, 1099] = inf, -inf
+    Bv[4, 1099] = -inf
+    av = rng.integers(-2, 3, size=k).astype(np.float32)
+    av[5] = av[700] = av[1099] = 1.0
+    av[600] = 0.0
+    Bv[5, 600] = inf            # inf * 0 -> NaN
+    Bv[6, :] = 0.0
+    Bb, ab = values_to_bits(Bv, dtype), values_to_bits(av, dtype)
+    ref, _, _ = oracle.gemv(dtype, Bb, ab)
+    Bd, ad = to_device(Bb, dtype), to_device(ab, dtype)
+    r = oracle.decode(dtype, ref)
+    for v in [-1] + VARIANTS:
+        got = oracle.decode(dtype, run(g, Bd, ad, v))
+        assert np.array_equal(np.isnan(got), np.isnan(r)), (v, got, r)
+        fin = ~np.isnan(r)
+        assert np.array_equal(got[fin], r[fin]), (v, got, r)
+
+
+def test_empty_and_tiny(g):
+    dev = "cuda"
+    for dtype in (F16, BF16):
+        td = torch_dtype(dtype)
+        # n == 0: a no-op that succeeds
+        B = torch.empty((0, 16), dtype=td, device=dev)
+        a = torch.ones(16, dtype=td, device=dev)
+        c = torch.empty(0, dtype=td, device=dev)
+        g(B, a, c)
+        # k == 0: the empty sum
+        B = torch.empty((5, 0), dtype=td, device=dev)
+        a = torch.empty(0, dtype=td, device=dev)
+        c = torch.full((5,), 3.0, dtype=td, device=dev)
+        for v in [-1] + VARIANTS:
+            c.fill_(3.0)
+            g.force_config(v)
+            g(B, a, c)
+            g.force_config(-1)
+            torch.cuda.synchronize()
+            assert torch.all(c == 0), v
+        # every small k, for row-tail and k-tail coverage
+        for k in list(range(1, 18)) + [63, 64, 65, 520]:
+            Bb, ab = integer_inputs(3, k, dtype, seed=k)
+            ref, _, _ = oracle.gemv(dtype, Bb, ab)
+            got = run(g, to_device(Bb, dtype), to_device(ab, dtype))
+            assert np.array_equal(got, ref), k
+
+
+def test_rejected_calls_leave_c_untouched(g):
+    n, k = 64, 256
+    B = torch.ones((n, k), dtype=torch.float16, device="cuda")
+    a = torch.ones(k, dtype=torch.float16, device="cuda")
+    # c overlapping B
+    s = mbd.gemv_run(g.h, B.data_ptr(), a.data_ptr(), B.data_ptr() + 64, n, k, 0,
+                     torch.cuda.current_stream().cuda_stream)
+    assert s == mbd._lib.GEMV_ERR_ALIASING
+    torch.cuda.synchronize()
+    assert torch.all(B == 1)
+    # bad dtype and misaligned c
+    c = torch.full((n + 1,), 5.0, dtype=torch.float16, device="cuda")
+    assert mbd.gemv_run(g.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, 7, None) == \
+        mbd._lib.GEMV_ERR_UNSUPPORTED_DTYPE
+    assert mbd.gemv_run(g.h, B.data_ptr(), a.data_ptr(), c.data_ptr() + 1, n, k, 0, None) == \
+        mbd._lib.GEMV_ERR_MISALIGNED
+    torch.cuda.synchronize()
+    assert torch.all(c == 5.0)
+
+
+def test_query_config_matches_a_variant(g):
+    for n, k, dtype in [(18432, 7168, F16), (7168, 16384, BF16), (64, 65536, BF16)]:
+        v, grid = g.query_config(n, k, dtype)
+        assert 0 <= v < NV and grid >= 1
