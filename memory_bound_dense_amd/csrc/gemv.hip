@@ -12,7 +12,7 @@
 
 namespace {
 
-using KernelFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, int, int, int);
+using KernelFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, int, int);
 
 struct Variant {
   gemv_variant_info_t info;
@@ -259,9 +259,7 @@ extern "C" gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a,
   const uint16_t* ap = (const uint16_t*)a;
   uint16_t* cp = (uint16_t*)c;
   int ni = (int)n, ki = (int)k;
-  const int64_t rb = rows_per_block(var.info);
-  int nrb = (int)((n + rb - 1) / rb);
-  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp, (void*)&ni, (void*)&ki, (void*)&nrb};
+  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp, (void*)&ni, (void*)&ki};
   hipError_t e = hipLaunchKernel((const void*)var.fn[dtype], dim3((unsigned)grid),
                                  dim3((unsigned)(var.info.waves * mbd::kLanes)), args, lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));

@@ -131,7 +131,7 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
 template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
-    int n, int k, int nrb) {
+    int n, int k) {
   static_assert(WAVES % S == 0, "splits must divide the waves of a workgroup");
   constexpr int G = WAVES / S;   // row groups per workgroup
   constexpr int RB = G * R;      // rows per workgroup per row block
@@ -164,11 +164,21 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
   const bool tail = (rem != 0) && (sl == S - 1);
   const int lane_off = lane * 16;
 
-  for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
-    const int row0 = rb * RB + rg * R;
-    if (S == 1 && row0 >= n) continue;   // wave-uniform; no barrier below when S == 1
-    const int rbase = row0 < n ? row0 : n - 1;
-    const int nrows = (n - rbase) < R ? (n - rbase) : R;   // >= 1
+  // Rows are dealt out in balanced contiguous ranges, so any grid size is
+  // valid and the ranges differ by at most one row.  S == 1: every wave owns
+  // a range and walks it R rows at a time.  S > 1: every workgroup owns a
+  // range; its row groups take R rows each per trip, its k-slices share them.
+  const int64_t units = S == 1 ? (int64_t)gridDim.x * G : (int64_t)gridDim.x;
+  const int64_t unit = S == 1 ? (int64_t)blockIdx.x * G + rg : (int64_t)blockIdx.x;
+  const int lo = (int)((unit * n) / units);
+  const int hi = (int)(((unit + 1) * n) / units);
+  constexpr int kTrip = S == 1 ? R : RB;
+  const int goff = S == 1 ? 0 : rg * R;
+
+  for (int base = lo; base < hi; base += kTrip) {   // trip count uniform in a workgroup when S > 1
+    const int row0 = base + goff;                    // may lie past hi for S > 1: computed, not stored
+    const int rbase = row0 < hi ? row0 : hi - 1;
+    const int nrows = (hi - rbase) < R ? (hi - rbase) : R;   // >= 1
     const __amdgpu_buffer_rsrc_t brsrc =
         make_rsrc(B + (int64_t)rbase * k, (uint32_t)nrows * (uint32_t)k * 2u);
     uint32_t soff[R];
@@ -243,7 +253,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
       float mine = tot[0];
 #pragma unroll
       for (int r = 1; r < R; ++r) mine = (lane == r) ? tot[r] : mine;
-      if (lane < R && row0 + lane < n) c[row0 + lane] = to_bits<DT>(mine);
+      if (lane < R && row0 + lane < hi) c[row0 + lane] = to_bits<DT>(mine);
     } else {
       if (lane < R) {
         float mine = tot[0];
@@ -252,7 +262,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
         part[(rg * S + sl) * R + lane] = mine;
       }
       __syncthreads();
-      if (sl == 0 && lane < R && row0 + lane < n) {
+      if (sl == 0 && lane < R && row0 + lane < hi) {
         float s = 0.0f;
         for (int q = 0; q < S; ++q) s += part[(rg * S + q) * R + lane];
         c[row0 + lane] = to_bits<DT>(s);
