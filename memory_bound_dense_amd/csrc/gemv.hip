@@ -67,12 +67,6 @@ const Variant kVariants[] = {
 #undef CCH
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
-constexpr int kRowDefault = 4;        // R=2, U=4, 4 waves, a cached, non-temporal B
-constexpr int kSplitSmallN = 40;      // 16 waves share each row
-
-constexpr uint32_t kMagic = 0x47454d56u;   // "GEMV"
-constexpr uint32_t kDead = 0xdeadbeefu;
-
 size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
   const int64_t nsteps = (k + mbd::kStep - 1) / mbd::kStep;
   size_t b = 0;
@@ -82,6 +76,69 @@ size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
 }
 
 int64_t rows_per_block(const gemv_variant_info_t& v) { return (int64_t)(v.waves / v.splits) * v.rows; }
+
+// Shape of a launch plan: a variant shape plus a workgroup count (0 = one
+// row range per wave, i.e. no persistence).
+struct Plan {
+  int rows, unroll, waves, splits, a_mode, policy;
+  int grid;
+};
+
+// Measured on MI355X for the listed workload shapes (several plans lie
+// within a few per cent of each other on these; the fastest median is kept).
+struct TunedShape {
+  int64_t n, k;
+  Plan plan;
+};
+const TunedShape kTuned[] = {
+    {4096, 11008, {1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0}},
+    {4096, 14336, {1, 4, 4, 1, mbd::A_CACHED, kPolNT, 512}},
+};
+
+int find_variant(const Plan& p) {
+  for (int v = 0; v < kNumVariants; ++v) {
+    const gemv_variant_info_t& i = kVariants[v].info;
+    if (i.rows == p.rows && i.unroll == p.unroll && i.waves == p.waves && i.splits == p.splits &&
+        i.a_mode == p.a_mode && i.b_policy == p.policy)
+      return v;
+  }
+  return -1;
+}
+
+// The general rule, for shapes without a measured entry:
+//  * rows whose start is not 16-byte aligned (k % 8 != 0): one row per wave
+//    and a staged in LDS, which keeps the texture path free for the
+//    unaligned B loads;
+//  * otherwise a through the caches and non-temporal B loads; two rows per
+//    wave when both n and k are large;
+//  * k is split inside a workgroup while every wave still streams at least
+//    8 KiB of B, and further (down to two 512-element steps per slice) while
+//    the grid has fewer than 4096 waves.
+Plan rule_plan(int64_t n, int64_t k, size_t max_lds) {
+  if (k % 8 != 0) {
+    Plan p = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 0};
+    if (lds_bytes(kVariants[find_variant(p)].info, k) > max_lds) p.a_mode = mbd::A_CACHED;
+    return p;
+  }
+  const int64_t nfull = k / mbd::kStep;
+  const int R = (n >= 4096 && k >= 6144) ? 2 : 1;
+  const int64_t row_bytes = 2 * k * R;
+  const int smax = R == 1 ? 16 : 8;
+  int S = 1;
+  while (S < smax && row_bytes / (2 * S) >= 8192 && nfull >= 2 * (2 * S)) S *= 2;
+  while (S < smax && ((n + R - 1) / R) * S < 4096 && nfull >= 2 * (2 * S)) S *= 2;
+  const int W = S == 1 ? 4 : (S <= 8 ? 8 : 16);
+  return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0};
+}
+
+Plan auto_plan(int64_t n, int64_t k, size_t max_lds) {
+  for (const TunedShape& t : kTuned)
+    if (t.n == n && t.k == k) return t.plan;
+  return rule_plan(n, k, max_lds);
+}
+
+constexpr uint32_t kMagic = 0x47454d56u;   // "GEMV"
+constexpr uint32_t kDead = 0xdeadbeefu;
 
 }  // namespace
 
@@ -144,26 +201,27 @@ extern "C" gemv_status_t gemv_check_args(const void* B, const void* a, const voi
   return GEMV_OK;
 }
 
-static int auto_variant(const gemv_handle_s* h, int64_t n, int64_t k) {
-  // Small n cannot give every CU a row block of whole rows: let 16 waves
-  // share each row instead.
-  if (n * 4 < (int64_t)h->num_cus * 8) return kSplitSmallN;
-  return kRowDefault;
-}
-
 static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, int* variant,
                              int* grid, size_t* lds) {
-  int v = h->forced.variant >= 0 ? h->forced.variant : auto_variant(h, n, k);
+  int v;
+  int64_t g;
+  if (h->forced.variant >= 0) {
+    v = h->forced.variant;
+    g = h->forced.grid;
+  } else {
+    const Plan p = auto_plan(n, k, h->max_lds);
+    v = find_variant(p);
+    if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
+    g = p.grid;
+  }
   const gemv_variant_info_t& info = kVariants[v].info;
   const int64_t rb = rows_per_block(info);
-  const int64_t nrb = (n + rb - 1) / rb;
-  int64_t g = h->forced.variant >= 0 && h->forced.grid > 0 ? h->forced.grid : nrb;
-  if (g > nrb) g = nrb;
-  // the kernels loop over row blocks, so a smaller grid is always valid; keep
-  // the launch's work-item count well inside 32 bits
+  const int64_t nrb = (n + rb - 1) / rb;       // one row range per wave (or workgroup)
+  if (g <= 0 || g > nrb) g = nrb;
+  // the kernels walk their row ranges, so a smaller grid is always valid;
+  // keep the launch's work-item count well inside 32 bits
   const int64_t gmax = (int64_t)1 << 24;
   if (g > gmax) g = gmax;
-  if (g < 1) g = 1;
   const size_t l = lds_bytes(info, k);
   if (l > h->max_lds) return GEMV_ERR_UNSUPPORTED;
   *variant = v;

@@ -1,0 +1,207 @@
+"""Profiling helper: programs to run under rocprofv3, and summarisers that turn
+rocprofv3's CSV output into the short text summaries kept under profiles/.
+
+Programs (run as the profiled program, after ``rocprofv3 ... --``):
+
+  python3 -m memory_bound_dense_amd.profile_counters gemv --workload NAME --launches N
+      N launches of the GEMV in its automatic configuration, rotating over
+      copies of the inputs that exceed 1 GiB (as bench.py does).
+  python3 -m memory_bound_dense_amd.profile_counters copy --bytes X --launches N
+      N device-to-device copies of X bytes (a plain copy kernel of known
+      traffic: X bytes read and X bytes written), to calibrate the counters.
+
+Summarisers (run anywhere, on the CSV files rocprofv3 wrote):
+
+  ... summarize-trace --stats DIR/.._kernel_stats.csv --trace DIR/.._kernel_trace.csv
+                      --command "..." --out profiles/NAME.txt
+  ... summarize-counters --workload NAME --fetch CSV --write CSV --copy-fetch CSV
+                      --copy-write CSV --copy-bytes X --commands "..." --out profiles/...
+
+FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  The copy kernel's reading
+fixes a scale factor per counter (known bytes / counted bytes) that is applied
+to the GEMV kernel's reading.
+"""
+import argparse
+import csv
+import hashlib
+import math
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", "gemv_kernel.h"), os.path.join(PKG, "csrc", "gemv.hip")]
+GEMV_KERNEL = "gemv_kernel"
+COPY_KERNEL = "copyBuffer"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---- programs ----------------------------------------------------------------
+
+def run_gemv(workload, launches):
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+    import memory_bound_dense_amd as mbd
+    from gemv_inputs import ALL_WORKLOADS, random_inputs, torch_dtype
+    name, n, k, dtype, dist = {w[0]: w for w in ALL_WORKLOADS}[workload]
+    dev = torch.device("cuda", 0)
+    td = torch_dtype(dtype)
+    B_bits, a_bits = random_inputs(n, k, dtype, dist, seed=0)
+    B0 = torch.from_numpy(B_bits.view(np.int16)).to(dev).view(td)
+    a0 = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(td)
+    nbuf = int(min(64, max(2, math.ceil((1 << 30) / (2.0 * n * k)))))
+    Bs = [B0] + [B0.clone() for _ in range(nbuf - 1)]
+    As = [a0] + [a0.clone() for _ in range(nbuf - 1)]
+    Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]
+    torch.cuda.synchronize()
+    g = mbd.Gemv()
+    v, grid = g.query_config(n, k, dtype)
+    for i in range(launches):
+        g(Bs[i % nbuf], As[i % nbuf], Cs[i % nbuf])
+    torch.cuda.synchronize()
+    g.close()
+    print("gemv %s: %d launches, variant %d grid %d" % (name, launches, v, grid), flush=True)
+
+
+def run_copy(nbytes, launches):
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("copy: %d launches of %d bytes" % (launches, nbytes), flush=True)
+
+
+# ---- summarisers ---------------------------------------------------------------
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError("none of %s in %s" % (names, list(row)))
+
+
+def counter_per_dispatch(path, kernel_substr, counter):
+    vals = []
+    for r in _rows(path):
+        if kernel_substr in _col(r, "Kernel_Name", "Kernel-Name") and \
+                _col(r, "Counter_Name", "Counter-Name") == counter:
+            vals.append(float(_col(r, "Counter_Value", "Counter-Value")))
+    if not vals:
+        raise ValueError("no %s rows for a kernel matching %r in %s" % (counter, kernel_substr, path))
+    return vals
+
+
+def summarize_trace(stats_csv, trace_csv, command, out):
+    lines = ["# rocprofv3 kernel trace summary", "command: %s" % command,
+             "kernel_source_sha256_16: %s" % kernel_source_hash(), ""]
+    stats = _rows(stats_csv)
+    keys = list(stats[0].keys()) if stats else []
+    lines.append("kernel_stats.csv (all kernels):")
+    lines.append("  " + " | ".join(keys))
+    for r in stats:
+        lines.append("  " + " | ".join(r[k] for k in keys))
+    if trace_csv:
+        durs = {}
+        for r in _rows(trace_csv):
+            nm = _col(r, "Kernel_Name", "Kernel-Name")
+            d = (int(_col(r, "End_Timestamp", "End-Timestamp")) -
+                 int(_col(r, "Start_Timestamp", "Start-Timestamp"))) / 1000.0
+            durs.setdefault(nm, []).append(d)
+        lines.append("")
+        lines.append("per-kernel durations from kernel_trace.csv (us):")
+        for nm, d in durs.items():
+            lines.append("  %s: dispatches %d avg %.3f median %.3f min %.3f max %.3f" % (
+                nm, len(d), statistics.fmean(d), statistics.median(d), min(d), max(d)))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters(workload, fetch, write, copy_fetch, copy_write, copy_bytes, commands, out):
+    sys.path.insert(0, ROOT)
+    from gemv_inputs import ALL_WORKLOADS, algorithmic_bytes
+    name, n, k, dtype, dist = {w[0]: w for w in ALL_WORKLOADS}[workload]
+    alg = algorithmic_bytes(n, k)
+    f_g = statistics.median(counter_per_dispatch(fetch, GEMV_KERNEL, "FETCH_SIZE")) * 1024
+    w_g = statistics.median(counter_per_dispatch(write, GEMV_KERNEL, "WRITE_SIZE")) * 1024
+    f_c = statistics.median(counter_per_dispatch(copy_fetch, COPY_KERNEL, "FETCH_SIZE")) * 1024
+    w_c = statistics.median(counter_per_dispatch(copy_write, COPY_KERNEL, "WRITE_SIZE")) * 1024
+    sf, sw = copy_bytes / f_c, copy_bytes / w_c
+    traffic = f_g * sf + w_g * sw
+    lines = [
+        "# HBM traffic of the GEMV kernel from rocprofv3 counters (median per dispatch)",
+        "workload: %s (n=%d k=%d)" % (name, n, k),
+        "commands:",
+    ] + ["  " + c for c in commands] + [
+        "kernel_source_sha256_16: %s" % kernel_source_hash(),
+        "copy_kernel_bytes: %d" % copy_bytes,
+        "copy_fetch_counted_bytes: %.0f" % f_c,
+        "copy_write_counted_bytes: %.0f" % w_c,
+        "fetch_scale: %.5f" % sf,
+        "write_scale: %.5f" % sw,
+        "gemv_fetch_counted_bytes: %.0f" % f_g,
+        "gemv_write_counted_bytes: %.0f" % w_g,
+        "algorithmic_bytes_per_launch: %d" % alg,
+        "hbm_bytes_per_launch: %.0f" % traffic,
+        "traffic_over_algorithmic: %.4f" % (traffic / alg),
+    ]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    p = sub.add_parser("gemv")
+    p.add_argument("--workload", default="gemv_18432x7168_f16")
+    p.add_argument("--launches", type=int, default=20)
+    p = sub.add_parser("copy")
+    p.add_argument("--bytes", type=int, default=256 << 20)
+    p.add_argument("--launches", type=int, default=10)
+    p = sub.add_parser("summarize-trace")
+    p.add_argument("--stats", required=True)
+    p.add_argument("--trace", default="")
+    p.add_argument("--command", required=True)
+    p.add_argument("--out", required=True)
+    p = sub.add_parser("summarize-counters")
+    p.add_argument("--workload", required=True)
+    p.add_argument("--fetch", required=True)
+    p.add_argument("--write", required=True)
+    p.add_argument("--copy-fetch", required=True)
+    p.add_argument("--copy-write", required=True)
+    p.add_argument("--copy-bytes", type=int, required=True)
+    p.add_argument("--commands", nargs="+", required=True)
+    p.add_argument("--out", required=True)
+    a = ap.parse_args()
+    if a.cmd == "gemv":
+        run_gemv(a.workload, a.launches)
+    elif a.cmd == "copy":
+        run_copy(a.bytes, a.launches)
+    elif a.cmd == "summarize-trace":
+        summarize_trace(a.stats, a.trace, a.command, a.out)
+    else:
+        summarize_counters(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes,
+                           a.commands, a.out)
+
+
+if __name__ == "__main__":
+    main()
