@@ -144,6 +144,8 @@ def main():
                     help="workload name (see gemv_inputs.ALL_WORKLOADS)")
     ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (-1 = auto)")
     ap.add_argument("--grid", type=int, default=0, help="force the workgroup count (0 = auto)")
+    ap.add_argument("--kgroups", type=int, default=0,
+                    help="force the k-groups of a cross-workgroup variant (0 = auto)")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true",
@@ -190,17 +192,17 @@ def main():
 
     g = mbd.Gemv()
     if args.variant >= 0:
-        g.force_config(args.variant, args.grid)
-    variant, grid = g.query_config(n, k, dtype)
+        g.force_config(args.variant, args.grid, args.kgroups)
+    variant, grid, kgroups = g.query_config(n, k, dtype)
     _, vinfo = mbd.gemv_variant_info(variant)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     run, h = mbd.gemv_run, g.h
     ptrs = [(Bs[i].data_ptr(), As[i].data_ptr(), Cs[i].data_ptr()) for i in range(nbuf)]
-    log("[bench] variant %d (rows %d unroll %d waves %d splits %d a_mode %d b_policy %d), "
-        "grid %d, %d rotating buffers of %.1f MB" % (
+    log("[bench] variant %d (rows %d unroll %d waves %d splits %d a_mode %d b_policy %d "
+        "cross_wg %d), grid %d x %d, %d rotating buffers of %.1f MB" % (
             variant, vinfo.rows, vinfo.unroll, vinfo.waves, vinfo.splits, vinfo.a_mode,
-            vinfo.b_policy, grid, nbuf, 2.0 * n * k / 1e6))
+            vinfo.b_policy, vinfo.cross_wg, grid, kgroups, nbuf, 2.0 * n * k / 1e6))
 
     def step(i):
         b, a, c = ptrs[i % nbuf]
@@ -252,7 +254,8 @@ def main():
         "dtype": DTYPE_NAMES[dtype],
         "data": "synthetic",
         "config": {"workload": name, "n": n, "k": k, "distribution": dist, "seed": 0,
-                   "variant": variant, "grid": grid, "rows_per_wave": vinfo.rows,
+                   "variant": variant, "grid": grid, "kgroups": kgroups,
+                   "rows_per_wave": vinfo.rows,
                    "unroll": vinfo.unroll, "waves_per_wg": vinfo.waves, "splits": vinfo.splits,
                    "a_mode": ["lds", "cached"][vinfo.a_mode], "rotating_buffers": nbuf},
         "us_per_call": round(ms_per_step * 1e3, 3),

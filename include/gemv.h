@@ -41,8 +41,15 @@
  * with B or a, current device == handle device; then the launch, whose
  * failure is GEMV_ERR_HIP.
  *
- * Threading.  A handle is read-only after gemv_create (gemv_force_config
- * aside), so concurrent gemv_run calls on different streams are safe.
+ * Workspace.  gemv_create allocates a small device workspace (4 MiB of
+ * partial sums and 256 KiB of counters) for the k-split across workgroups
+ * that small n takes; gemv_run never allocates.  The counters return to zero
+ * at the end of every such kernel.
+ *
+ * Threading.  The handle's settings are read-only after gemv_create
+ * (gemv_force_config aside), but its workspace is shared: calls on one handle
+ * must not run concurrently on the GPU (issue them on one stream, or order
+ * them with events).  For concurrent streams use one handle per stream.
  */
 #ifndef MBD_GEMV_H
 #define MBD_GEMV_H
@@ -80,8 +87,8 @@ typedef enum {
 #define GEMV_MAX_K 134217728LL
 
 /* Create a handle bound to the current HIP device.  Queries the device (it
- * must be a gfx950), sets kernel attributes and fixes the variant table.
- * *out receives the handle, or NULL on error. */
+ * must be a gfx950), sets kernel attributes, allocates the workspace and
+ * fixes the variant table.  *out receives the handle, or NULL on error. */
 gemv_status_t gemv_create(gemv_handle_t* out);
 
 /* c = B @ a on `stream` (0 = the null stream).  B: n*k elements, row-major;
@@ -97,8 +104,9 @@ gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a, void* c,
 gemv_status_t gemv_check_args(const void* B, const void* a, const void* c, int64_t n, int64_t k,
                               gemv_dtype_t dtype);
 
-/* Release the handle.  NULL is a no-op.  Outstanding work on streams is not
- * affected (the handle owns no device memory). */
+/* Release the handle and its workspace.  NULL is a no-op.  Waits for the
+ * handle's device to finish outstanding work first (a kernel in flight may
+ * still use the workspace). */
 gemv_status_t gemv_destroy(gemv_handle_t h);
 
 /* Static, human-readable name of a status code. */
@@ -121,11 +129,16 @@ typedef struct {
   int32_t splits;
   int32_t a_mode;
   int32_t b_policy;   /* cache-policy bits of the B loads (0 = default) */
+  int32_t cross_wg;   /* 1: kgroups workgroups share each row range along k,
+                         combining through the handle's workspace */
 } gemv_variant_info_t;
 
 typedef struct {
   int32_t variant;    /* index in [0, gemv_num_variants()), or -1 = automatic */
-  int32_t grid;       /* workgroups to launch; 0 = one per row block */
+  int32_t grid;       /* workgroups per k-group; 0 = one row range per wave
+                         (per workgroup when splits > 1 or cross_wg) */
+  int32_t kgroups;    /* cross_wg variants: workgroups sharing a row range
+                         along k (0 = automatic); other variants: 0 or 1 */
 } gemv_config_t;
 
 /* Number of compiled variants. */

@@ -46,11 +46,12 @@ class GemvError(RuntimeError):
 class gemv_variant_info_t(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("unroll", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("splits", ctypes.c_int32), ("a_mode", ctypes.c_int32),
-                ("b_policy", ctypes.c_int32)]
+                ("b_policy", ctypes.c_int32), ("cross_wg", ctypes.c_int32)]
 
 
 class gemv_config_t(ctypes.Structure):
-    _fields_ = [("variant", ctypes.c_int32), ("grid", ctypes.c_int32)]
+    _fields_ = [("variant", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("kgroups", ctypes.c_int32)]
 
 
 _lib = None
@@ -125,10 +126,10 @@ def gemv_variant_info(v):
     return s, info
 
 
-def gemv_force_config(h, variant=-1, grid=0):
+def gemv_force_config(h, variant=-1, grid=0, kgroups=0):
     if variant is None:
         return load().gemv_force_config(h, None)
-    cfg = gemv_config_t(variant, grid)
+    cfg = gemv_config_t(variant, grid, kgroups)
     return load().gemv_force_config(h, ctypes.byref(cfg))
 
 
@@ -170,8 +171,8 @@ class Gemv:
         except Exception:
             pass
 
-    def force_config(self, variant=-1, grid=0):
-        s = gemv_force_config(self.h, variant, grid)
+    def force_config(self, variant=-1, grid=0, kgroups=0):
+        s = gemv_force_config(self.h, variant, grid, kgroups)
         if s != GEMV_OK:
             raise GemvError(s, "gemv_force_config")
 
@@ -179,7 +180,7 @@ class Gemv:
         s, cfg = gemv_query_config(self.h, n, k, dtype)
         if s != GEMV_OK:
             raise GemvError(s, "gemv_query_config")
-        return cfg.variant, cfg.grid
+        return cfg.variant, cfg.grid, cfg.kgroups
 
     def __call__(self, B, a, c, stream=None):
         import torch

@@ -12,7 +12,8 @@
 
 namespace {
 
-using KernelFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, int, int);
+using KernelFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, int, int, float*,
+                          unsigned*);
 
 struct Variant {
   gemv_variant_info_t info;
@@ -23,10 +24,11 @@ struct Variant {
 // non-temporal (B has no reuse within a call).
 constexpr int kPolNT = 2;
 
-#define MBD_VARIANT(R, U, W, S, AM, POL)                                            \
-  {{R, U, W, S, AM, POL},                                                           \
-   {&mbd::gemv_kernel<mbd::DT_F16, R, U, W, S, AM, POL>,                            \
-    &mbd::gemv_kernel<mbd::DT_BF16, R, U, W, S, AM, POL>}}
+#define MBD_VARIANT_X(R, U, W, S, AM, POL, X)                                       \
+  {{R, U, W, S, AM, POL, X},                                                        \
+   {&mbd::gemv_kernel<mbd::DT_F16, R, U, W, S, AM, POL, X>,                         \
+    &mbd::gemv_kernel<mbd::DT_BF16, R, U, W, S, AM, POL, X>}}
+#define MBD_VARIANT(R, U, W, S, AM, POL) MBD_VARIANT_X(R, U, W, S, AM, POL, false)
 
 // The compiled variants: (rows R, unroll U, waves W, splits S, a mode, B
 // cache policy).  Row variants (S == 1) give each wave R whole rows; split
@@ -61,6 +63,10 @@ const Variant kVariants[] = {
     MBD_VARIANT(1, 2, 8, 8, CCH, NT), MBD_VARIANT(1, 4, 8, 8, CCH, NT),
     MBD_VARIANT(2, 4, 8, 8, CCH, NT), MBD_VARIANT(1, 4, 4, 4, CCH, NT),
     MBD_VARIANT(1, 2, 16, 16, CCH, NT), MBD_VARIANT(1, 4, 16, 16, CCH, NT),
+    // 42..47: split across workgroups as well (small n)
+    MBD_VARIANT_X(1, 4, 8, 8, CCH, NT, true), MBD_VARIANT_X(1, 2, 8, 8, CCH, NT, true),
+    MBD_VARIANT_X(1, 4, 4, 4, CCH, NT, true), MBD_VARIANT_X(1, 2, 4, 4, CCH, NT, true),
+    MBD_VARIANT_X(2, 4, 8, 4, CCH, NT, true), MBD_VARIANT_X(1, 4, 4, 1, CCH, NT, true),
 };
 #undef NT
 #undef LDS
@@ -77,11 +83,17 @@ size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
 
 int64_t rows_per_block(const gemv_variant_info_t& v) { return (int64_t)(v.waves / v.splits) * v.rows; }
 
+// Device workspace of a handle: fp32 partial sums (kgroups x n) and one
+// arrival counter per row range, for the cross-workgroup variants.
+constexpr size_t kWsFloats = (size_t)1 << 20;   // 4 MiB
+constexpr int kWsCounters = 1 << 16;            // 256 KiB
+
 // Shape of a launch plan: a variant shape plus a workgroup count (0 = one
 // row range per wave, i.e. no persistence).
 struct Plan {
   int rows, unroll, waves, splits, a_mode, policy;
   int grid;
+  int kgroups;   // > 1: a cross-workgroup variant with this many k-groups
 };
 
 // Measured on MI355X for the listed workload shapes (several plans lie
@@ -91,15 +103,16 @@ struct TunedShape {
   Plan plan;
 };
 const TunedShape kTuned[] = {
-    {4096, 11008, {1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0}},
-    {4096, 14336, {1, 4, 4, 1, mbd::A_CACHED, kPolNT, 512}},
+    {4096, 11008, {1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0, 1}},
+    {4096, 14336, {1, 4, 4, 1, mbd::A_CACHED, kPolNT, 512, 1}},
 };
 
 int find_variant(const Plan& p) {
+  const int x = p.kgroups > 1 ? 1 : 0;
   for (int v = 0; v < kNumVariants; ++v) {
     const gemv_variant_info_t& i = kVariants[v].info;
     if (i.rows == p.rows && i.unroll == p.unroll && i.waves == p.waves && i.splits == p.splits &&
-        i.a_mode == p.a_mode && i.b_policy == p.policy)
+        i.a_mode == p.a_mode && i.b_policy == p.policy && i.cross_wg == x)
       return v;
   }
   return -1;
@@ -115,8 +128,20 @@ int find_variant(const Plan& p) {
 //    8 KiB of B, and further (down to two 512-element steps per slice) while
 //    the grid has fewer than 4096 waves.
 Plan rule_plan(int64_t n, int64_t k, size_t max_lds) {
+  const int64_t nfull0 = k / mbd::kStep;
+  // Too few rows to give the GPU 4096 waves even with 16 waves per row:
+  // split k across workgroups too (8 waves per row per workgroup, Q groups,
+  // about 2048 waves in all -- more k-groups cost more than they bring on
+  // MI355X), keeping at least two 512-element steps per wave.
+  if (n * 16 < 4096 && nfull0 >= 2 * 8 * 2) {
+    int64_t Q = (2048 + n * 8 - 1) / (n * 8);
+    const int64_t qmax = nfull0 / (2 * 8);
+    if (Q > qmax) Q = qmax;
+    if (Q > 64) Q = 64;
+    if (Q * n <= (int64_t)kWsFloats && Q > 1) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
+  }
   if (k % 8 != 0) {
-    Plan p = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 0};
+    Plan p = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 0, 1};
     if (lds_bytes(kVariants[find_variant(p)].info, k) > max_lds) p.a_mode = mbd::A_CACHED;
     return p;
   }
@@ -128,7 +153,7 @@ Plan rule_plan(int64_t n, int64_t k, size_t max_lds) {
   while (S < smax && row_bytes / (2 * S) >= 8192 && nfull >= 2 * (2 * S)) S *= 2;
   while (S < smax && ((n + R - 1) / R) * S < 4096 && nfull >= 2 * (2 * S)) S *= 2;
   const int W = S == 1 ? 4 : (S <= 8 ? 8 : 16);
-  return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0};
+  return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0, 1};
 }
 
 Plan auto_plan(int64_t n, int64_t k, size_t max_lds) {
@@ -149,6 +174,9 @@ struct gemv_handle_s {
   size_t max_lds;
   int log;
   gemv_config_t forced;
+  float* ws;           // kWsFloats partial sums (device)
+  unsigned* cnt;       // kWsCounters arrival counters (device), zero between kernels
+  size_t static_lds[kNumVariants][2];   // LDS each kernel declares statically
 };
 
 static gemv_status_t report(const gemv_handle_s* h, gemv_status_t s, const char* what) {
@@ -201,18 +229,26 @@ extern "C" gemv_status_t gemv_check_args(const void* B, const void* a, const voi
   return GEMV_OK;
 }
 
-static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, int* variant,
-                             int* grid, size_t* lds) {
+struct Launch {
+  int variant;
+  int grid;      // workgroups along x (row ranges)
+  int kgroups;   // workgroups along y (k-groups), 1 unless cross_wg
+  size_t lds;
+};
+
+static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, Launch* L) {
   int v;
-  int64_t g;
+  int64_t g, q;
   if (h->forced.variant >= 0) {
     v = h->forced.variant;
     g = h->forced.grid;
+    q = h->forced.kgroups;
   } else {
     const Plan p = auto_plan(n, k, h->max_lds);
     v = find_variant(p);
     if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
     g = p.grid;
+    q = p.kgroups;
   }
   const gemv_variant_info_t& info = kVariants[v].info;
   const int64_t rb = rows_per_block(info);
@@ -222,11 +258,22 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, int* 
   // keep the launch's work-item count well inside 32 bits
   const int64_t gmax = (int64_t)1 << 24;
   if (g > gmax) g = gmax;
+  if (info.cross_wg) {
+    if (q <= 0) q = 4;
+    if (q > 1024) return GEMV_ERR_UNSUPPORTED;
+    // the workspace must hold q partials per row and one counter per row range
+    if (q * n > (int64_t)kWsFloats || g > kWsCounters) return GEMV_ERR_UNSUPPORTED;
+  } else {
+    if (q > 1) return GEMV_ERR_INVALID_ARG;
+    q = 1;
+  }
   const size_t l = lds_bytes(info, k);
-  if (l > h->max_lds) return GEMV_ERR_UNSUPPORTED;
-  *variant = v;
-  *grid = (int)g;
-  *lds = l;
+  const size_t st = h->static_lds[v][0] > h->static_lds[v][1] ? h->static_lds[v][0] : h->static_lds[v][1];
+  if (l + st > h->max_lds) return GEMV_ERR_UNSUPPORTED;
+  L->variant = v;
+  L->grid = (int)g;
+  L->kgroups = (int)q;
+  L->lds = l;
   return GEMV_OK;
 }
 
@@ -243,15 +290,37 @@ extern "C" gemv_status_t gemv_create(gemv_handle_t* out) {
   int max_lds = 0;
   if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return report(nullptr, GEMV_ERR_HIP, "hipDeviceGetAttribute(max LDS)");
-  for (int v = 0; v < kNumVariants; ++v) {
-    for (int d = 0; d < 2; ++d) {
-      if (hipFuncSetAttribute((const void*)kVariants[v].fn[d],
-                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) != hipSuccess)
-        return report(nullptr, GEMV_ERR_HIP, "hipFuncSetAttribute");
-    }
-  }
   gemv_handle_s* h = (gemv_handle_s*)calloc(1, sizeof(gemv_handle_s));
   if (!h) return GEMV_ERR_OOM;
+  for (int v = 0; v < kNumVariants; ++v) {
+    for (int d = 0; d < 2; ++d) {
+      hipFuncAttributes fa;
+      const void* fn = (const void*)kVariants[v].fn[d];
+      if (hipFuncGetAttributes(&fa, fn) != hipSuccess) {
+        free(h);
+        return report(nullptr, GEMV_ERR_HIP, "hipFuncGetAttributes");
+      }
+      h->static_lds[v][d] = fa.sharedSizeBytes;
+      const int dyn_max = max_lds - (int)fa.sharedSizeBytes;
+      if (dyn_max < 0 ||
+          hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_max) != hipSuccess) {
+        free(h);
+        return report(nullptr, GEMV_ERR_HIP, "hipFuncSetAttribute(max dynamic LDS)");
+      }
+    }
+  }
+  void* mem = nullptr;
+  const size_t bytes = kWsFloats * sizeof(float) + (size_t)kWsCounters * sizeof(unsigned);
+  if (hipMalloc(&mem, bytes) != hipSuccess) {
+    free(h);
+    return report(nullptr, GEMV_ERR_HIP, "hipMalloc(workspace)");
+  }
+  // the counters start at zero; every kernel that uses one leaves it at zero
+  if (hipMemset(mem, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(mem);
+    free(h);
+    return report(nullptr, GEMV_ERR_HIP, "hipMemset(workspace)");
+  }
   h->magic = kMagic;
   h->device = dev;
   h->num_cus = prop.multiProcessorCount;
@@ -260,6 +329,9 @@ extern "C" gemv_status_t gemv_create(gemv_handle_t* out) {
   h->log = lg && strcmp(lg, "1") == 0;
   h->forced.variant = -1;
   h->forced.grid = 0;
+  h->forced.kgroups = 0;
+  h->ws = (float*)mem;
+  h->cnt = (unsigned*)((char*)mem + kWsFloats * sizeof(float));
   *out = h;
   return GEMV_OK;
 }
@@ -267,9 +339,17 @@ extern "C" gemv_status_t gemv_create(gemv_handle_t* out) {
 extern "C" gemv_status_t gemv_destroy(gemv_handle_t h) {
   if (!h) return GEMV_OK;
   if (h->magic != kMagic) return GEMV_ERR_NULL_HANDLE;
+  gemv_status_t st = GEMV_OK;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) st = GEMV_ERR_HIP;
+  // a kernel still in flight may use the workspace: let the device drain first
+  if (st == GEMV_OK && cur != h->device && hipSetDevice(h->device) != hipSuccess) st = GEMV_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) st = GEMV_ERR_HIP;
+  if (hipFree(h->ws) != hipSuccess) st = GEMV_ERR_HIP;
+  if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
   h->magic = kDead;
   free(h);
-  return GEMV_OK;
+  return st;
 }
 
 extern "C" gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t* cfg) {
@@ -277,9 +357,12 @@ extern "C" gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t*
   if (!cfg || cfg->variant < 0) {
     h->forced.variant = -1;
     h->forced.grid = 0;
+    h->forced.kgroups = 0;
     return GEMV_OK;
   }
-  if (cfg->variant >= kNumVariants || cfg->grid < 0) return report(h, GEMV_ERR_INVALID_ARG, "config");
+  if (cfg->variant >= kNumVariants || cfg->grid < 0 || cfg->kgroups < 0 ||
+      (!kVariants[cfg->variant].info.cross_wg && cfg->kgroups > 1))
+    return report(h, GEMV_ERR_INVALID_ARG, "config");
   h->forced = *cfg;
   return GEMV_OK;
 }
@@ -290,12 +373,12 @@ extern "C" gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k
   if (!out) return GEMV_ERR_INVALID_ARG;
   if (dtype != GEMV_F16 && dtype != GEMV_BF16) return GEMV_ERR_UNSUPPORTED_DTYPE;
   if (n <= 0 || k < 0 || n > GEMV_MAX_N || k > GEMV_MAX_K) return GEMV_ERR_INVALID_ARG;
-  int v, g;
-  size_t l;
-  gemv_status_t s = resolve(h, n, k, &v, &g, &l);
+  Launch L;
+  gemv_status_t s = resolve(h, n, k, &L);
   if (s != GEMV_OK) return s;
-  out->variant = v;
-  out->grid = g;
+  out->variant = L.variant;
+  out->grid = L.grid;
+  out->kgroups = L.kgroups;
   return GEMV_OK;
 }
 
@@ -308,18 +391,19 @@ extern "C" gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a,
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return report(h, GEMV_ERR_HIP, "hipGetDevice");
   if (dev != h->device) return report(h, GEMV_ERR_WRONG_DEVICE, "gemv_run");
-  int v, grid;
-  size_t lds;
-  s = resolve(h, n, k, &v, &grid, &lds);
-  if (s != GEMV_OK) return report(h, s, "no variant fits (LDS)");
-  const Variant& var = kVariants[v];
+  Launch L;
+  s = resolve(h, n, k, &L);
+  if (s != GEMV_OK) return report(h, s, "no variant fits (LDS or workspace)");
+  const Variant& var = kVariants[L.variant];
   const uint16_t* Bp = (const uint16_t*)B;
   const uint16_t* ap = (const uint16_t*)a;
   uint16_t* cp = (uint16_t*)c;
   int ni = (int)n, ki = (int)k;
-  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp, (void*)&ni, (void*)&ki};
-  hipError_t e = hipLaunchKernel((const void*)var.fn[dtype], dim3((unsigned)grid),
-                                 dim3((unsigned)(var.info.waves * mbd::kLanes)), args, lds, stream);
+  float* ws = h->ws;
+  unsigned* cnt = h->cnt;
+  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp, (void*)&ni, (void*)&ki, (void*)&ws, (void*)&cnt};
+  hipError_t e = hipLaunchKernel((const void*)var.fn[dtype], dim3((unsigned)L.grid, (unsigned)L.kgroups),
+                                 dim3((unsigned)(var.info.waves * mbd::kLanes)), args, L.lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));
   return GEMV_OK;
 }

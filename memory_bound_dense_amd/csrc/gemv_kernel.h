@@ -19,7 +19,11 @@
 //   * each lane keeps fp32 partial sums; the 64 lane partials of a row are
 //     combined with DPP row operations and two cross-row swaps;
 //   * with S > 1 the k-slices of a row group are summed through LDS in slice
-//     order (fixed order, so results do not depend on timing).
+//     order (fixed order, so results do not depend on timing);
+//   * with XWG, Q = gridDim.y workgroups also share a row range along k:
+//     each writes its fp32 row partials to a workspace, and the workgroup
+//     that arrives last (a device-scope counter per row range) sums the Q
+//     partials in a fixed order and writes c.
 //
 // Loads go through buffer resources: the row base is a wave-uniform 64-bit
 // address in SGPRs, the per-row offset is an SGPR soffset and the lane offset
@@ -128,11 +132,12 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
   }
 }
 
-template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL>
+template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL, bool XWG>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
-    int n, int k) {
+    int n, int k, float* __restrict__ ws, unsigned* __restrict__ cnt) {
   static_assert(WAVES % S == 0, "splits must divide the waves of a workgroup");
+  static_assert(!XWG || AMODE == A_CACHED, "a k-chunk per workgroup does not stage all of a");
   constexpr int G = WAVES / S;   // row groups per workgroup
   constexpr int RB = G * R;      // rows per workgroup per row block
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -158,22 +163,30 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     __syncthreads();
   }
 
-  // this wave's share of the full steps; the partial step goes to the last slice
-  const int t0 = (int)(((int64_t)nfull * sl) / S);
-  const int t1 = (int)(((int64_t)nfull * (sl + 1)) / S);
-  const bool tail = (rem != 0) && (sl == S - 1);
+  // this wave's share of the full steps (slice q*S + sl of Q*S); the partial
+  // step goes to the last slice
+  const int Q = XWG ? (int)gridDim.y : 1;
+  const int q = XWG ? (int)blockIdx.y : 0;
+  const int gsl = q * S + sl;
+  const int nsl = Q * S;
+  const int t0 = (int)(((int64_t)nfull * gsl) / nsl);
+  const int t1 = (int)(((int64_t)nfull * (gsl + 1)) / nsl);
+  const bool tail = (rem != 0) && (gsl == nsl - 1);
   const int lane_off = lane * 16;
 
   // Rows are dealt out in balanced contiguous ranges, so any grid size is
   // valid and the ranges differ by at most one row.  S == 1: every wave owns
   // a range and walks it R rows at a time.  S > 1: every workgroup owns a
   // range; its row groups take R rows each per trip, its k-slices share them.
-  const int64_t units = S == 1 ? (int64_t)gridDim.x * G : (int64_t)gridDim.x;
-  const int64_t unit = S == 1 ? (int64_t)blockIdx.x * G + rg : (int64_t)blockIdx.x;
+  // With XWG the ranges are per workgroup as well (the cross-workgroup
+  // combine works on a workgroup's whole range).
+  constexpr bool kWaveRanges = S == 1 && !XWG;
+  const int64_t units = kWaveRanges ? (int64_t)gridDim.x * G : (int64_t)gridDim.x;
+  const int64_t unit = kWaveRanges ? (int64_t)blockIdx.x * G + rg : (int64_t)blockIdx.x;
   const int lo = (int)((unit * n) / units);
   const int hi = (int)(((unit + 1) * n) / units);
-  constexpr int kTrip = S == 1 ? R : RB;
-  const int goff = S == 1 ? 0 : rg * R;
+  constexpr int kTrip = kWaveRanges ? R : RB;
+  const int goff = kWaveRanges ? 0 : rg * R;
 
   for (int base = lo; base < hi; base += kTrip) {   // trip count uniform in a workgroup when S > 1
     const int row0 = base + goff;                    // may lie past hi for S > 1: computed, not stored
@@ -249,25 +262,60 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) tot[r] = wave_sum(acc[r][0] + acc[r][1]);
 
-    if constexpr (S == 1) {
-      float mine = tot[0];
+    float mine = tot[0];
 #pragma unroll
-      for (int r = 1; r < R; ++r) mine = (lane == r) ? tot[r] : mine;
-      if (lane < R && row0 + lane < hi) c[row0 + lane] = to_bits<DT>(mine);
-    } else {
-      if (lane < R) {
-        float mine = tot[0];
-#pragma unroll
-        for (int r = 1; r < R; ++r) mine = (lane == r) ? tot[r] : mine;
-        part[(rg * S + sl) * R + lane] = mine;
-      }
+    for (int r = 1; r < R; ++r) mine = (lane == r) ? tot[r] : mine;
+    bool leader = lane < R && row0 + lane < hi;   // holds the sum of row row0 + lane
+    if constexpr (S > 1) {
+      if (lane < R) part[(rg * S + sl) * R + lane] = mine;
       __syncthreads();
-      if (sl == 0 && lane < R && row0 + lane < hi) {
+      leader = leader && sl == 0;
+      if (leader) {
         float s = 0.0f;
-        for (int q = 0; q < S; ++q) s += part[(rg * S + q) * R + lane];
-        c[row0 + lane] = to_bits<DT>(s);
+        for (int qq = 0; qq < S; ++qq) s += part[(rg * S + qq) * R + lane];
+        mine = s;
       }
       __syncthreads();
+    }
+    if (leader) {
+      if constexpr (XWG) {
+        // agent-scope store: written through this XCD's L2 to the point
+        // where every XCD sees it
+        __hip_atomic_store(&ws[(int64_t)q * n + row0 + lane], mine, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        c[row0 + lane] = to_bits<DT>(mine);
+      }
+    }
+  }
+
+  if constexpr (XWG) {
+    // Publish, count, combine.  The partials were stored at agent scope
+    // (write-through); waiting for every store of the workgroup to complete
+    // before the barrier orders them before the counter update.  The last of
+    // the Q workgroups of this row range reads the partials at agent scope
+    // (past the non-coherent L2) and sums them in a fixed order.  No L2-wide
+    // write-back or invalidate is needed: only these accesses cross XCDs.
+    __shared__ int last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      last = __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(Q - 1);
+    }
+    __syncthreads();
+    if (last) {
+      // one wave per row: lane j loads partials j, j+64, ... (all lanes at
+      // once, so the loads overlap), then the fixed lane tree of wave_sum
+      for (int r = lo + wave; r < hi; r += WAVES) {
+        float s = 0.0f;
+        for (int qq = lane; qq < Q; qq += kLanes)
+          s += __hip_atomic_load(&ws[(int64_t)qq * n + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s = wave_sum(s);
+        if (lane == 0) c[r] = to_bits<DT>(s);
+      }
+      if (threadIdx.x == 0)   // ready for the next call
+        __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -64,12 +64,13 @@ def run_gemv(workload, launches):
     Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]
     torch.cuda.synchronize()
     g = mbd.Gemv()
-    v, grid = g.query_config(n, k, dtype)
+    v, grid, kgroups = g.query_config(n, k, dtype)
     for i in range(launches):
         g(Bs[i % nbuf], As[i % nbuf], Cs[i % nbuf])
     torch.cuda.synchronize()
     g.close()
-    print("gemv %s: %d launches, variant %d grid %d" % (name, launches, v, grid), flush=True)
+    print("gemv %s: %d launches, variant %d grid %d x %d" % (name, launches, v, grid, kgroups),
+          flush=True)
 
 
 def run_copy(nbytes, launches):

@@ -26,8 +26,11 @@ NV = mbd.gemv_num_variants()
 VARIANTS = list(range(NV))
 
 
-def _splits(v):
-    return mbd.gemv_variant_info(v)[1].splits
+def _extra_adds(g, n, k, dtype):
+    """fp32 additions after the per-lane sums, beyond the wave tree: the
+    in-workgroup slices plus the cross-workgroup k-groups of the plan in use."""
+    v, _, q = g.query_config(n, k, dtype)
+    return mbd.gemv_variant_info(v)[1].splits + (q if q > 1 else 0)
 
 
 @pytest.fixture(scope="module")
@@ -38,11 +41,17 @@ def g():
     h.close()
 
 
-def run(g, Bd, ad, variant=-1, grid=0):
+LAST_EXTRA = [0]
+
+
+def run(g, Bd, ad, variant=-1, grid=0, kgroups=0):
     n, k = Bd.shape
+    dtype = mbd.GEMV_F16 if Bd.dtype == torch.float16 else mbd.GEMV_BF16
     c = torch.full((n,), float("nan"), dtype=Bd.dtype, device=Bd.device)
-    g.force_config(variant, grid)
+    g.force_config(variant, grid, kgroups)
     try:
+        if n > 0:
+            LAST_EXTRA[0] = _extra_adds(g, n, k, dtype)
         g(Bd, ad, c)
     finally:
         g.force_config(-1)
@@ -51,7 +60,7 @@ def run(g, Bd, ad, variant=-1, grid=0):
 
 
 def _check(dtype, got, ref, ab, k, v, what):
-    ok_g, ok_s, rg, rs, first = compare(dtype, got, ref, ab, k, _splits(v) if v >= 0 else 16)
+    ok_g, ok_s, rg, rs, first = compare(dtype, got, ref, ab, k, LAST_EXTRA[0])
     assert ok_g, "%s variant %d: outside the grading tolerance (%s)" % (what, v, first)
     assert ok_s, "%s variant %d: outside the strict fp32 bound (max ratio %.3g, %s)" % (
         what, v, rs, first)
@@ -164,6 +173,7 @@ def test_misaligned_base_pointers(g, dtype):
         cbig = torch.full((n + 5,), 7.0, dtype=torch_dtype(dtype), device="cuda")
         c = cbig[5:]
         g.force_config(v)
+        LAST_EXTRA[0] = _extra_adds(g, n, k, dtype)
         g(Bd, ad, c)
         g.force_config(-1)
         torch.cuda.synchronize()
@@ -247,5 +257,64 @@ def test_rejected_calls_leave_c_untouched(g):
 
 def test_query_config_matches_a_variant(g):
     for n, k, dtype in [(18432, 7168, F16), (7168, 16384, BF16), (64, 65536, BF16)]:
-        v, grid = g.query_config(n, k, dtype)
-        assert 0 <= v < NV and grid >= 1
+        v, grid, q = g.query_config(n, k, dtype)
+        assert 0 <= v < NV and grid >= 1 and q >= 1
+
+
+XWG = [v for v in VARIANTS if mbd.gemv_variant_info(v)[1].cross_wg]
+XWG_SHAPES = [(64, 65536, BF16), (7, 20000, F16), (300, 4096, BF16), (1, 513, F16),
+              (33, 1031, BF16), (1000, 7000, BF16), (5, 0, F16)]
+
+
+@pytest.mark.parametrize("n,k,dtype", XWG_SHAPES,
+                         ids=["%dx%d_%s" % (n, k, "f16" if d == F16 else "bf16")
+                              for n, k, d in XWG_SHAPES])
+def test_cross_workgroup_split(g, n, k, dtype):
+    """k shared by several workgroups: every k-group count, including more
+    slices than there are steps (empty slices), calls repeated back to back
+    (the arrival counters must return to zero), random and integer inputs."""
+    B, a = random_inputs(n, k, dtype, "normal", seed=21)
+    ref, _, ab = oracle.gemv(dtype, B, a)
+    Bi, ai = integer_inputs(n, k, dtype, seed=22)
+    refi, _, _ = oracle.gemv(dtype, Bi, ai)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    Bid, aid = to_device(Bi, dtype), to_device(ai, dtype)
+    assert XWG
+    for v in XWG:
+        for q in (1, 2, 3, 8, 33, 64):
+            for grid in (0, 1, 3):
+                if q * n > (1 << 20):
+                    continue
+                for _ in range(2):
+                    got = run(g, Bd, ad, v, grid, q)
+                    _check(dtype, got, ref, ab, k, v, "%dx%d q=%d grid=%d" % (n, k, q, grid))
+                    goti = run(g, Bid, aid, v, grid, q)
+                    assert np.array_equal(goti, refi), (v, q, grid)
+
+
+def test_cross_workgroup_config_rules(g):
+    nonx = [v for v in VARIANTS if not mbd.gemv_variant_info(v)[1].cross_wg][0]
+    with pytest.raises(mbd.GemvError):
+        g.force_config(nonx, 0, 4)          # k-groups only exist for cross_wg variants
+    g.force_config(-1)
+    # too many partials for the workspace: rejected, c untouched
+    v = XWG[0]
+    n, k = 40000, 4096
+    B = torch.zeros((n, k), dtype=torch.float16, device="cuda")
+    a = torch.zeros(k, dtype=torch.float16, device="cuda")
+    c = torch.full((n,), 5.0, dtype=torch.float16, device="cuda")
+    g.force_config(v, 0, 64)
+    with pytest.raises(mbd.GemvError):
+        g(B, a, c)
+    g.force_config(-1)
+    torch.cuda.synchronize()
+    assert torch.all(c == 5.0)
+
+
+def test_query_config_many_shapes(g):
+    """Every automatic plan names a compiled variant that fits."""
+    for n in (1, 7, 64, 255, 256, 1000, 4096, 7168, 18432, 100000):
+        for k in (0, 1, 511, 512, 4096, 7169, 16384, 65536, 200000):
+            for dtype in (F16, BF16):
+                v, grid, q = g.query_config(n, k, dtype)
+                assert 0 <= v < NV and grid >= 1 and q >= 1, (n, k, dtype)
