@@ -120,8 +120,11 @@ const char* gemv_status_string(gemv_status_t s);
  * row group owns `rows` consecutive rows; each wave streams its rows of B
  * with 16-byte loads along k, `unroll` 512-element steps per loop trip.
  * a_mode 0: a is staged once per workgroup in LDS; 1: a is read through the
- * cache hierarchy with the same 16-byte loads.  splits > 1 sums the k-slices
- * of a row group in a fixed order through LDS (deterministic). */
+ * cache hierarchy with the same 16-byte loads; 2: for rows that do not start
+ * on a 16-byte boundary, B is read in aligned 16-byte granules and a is
+ * staged in LDS twice (shifted by 0 and 1 element) to line up with them.
+ * splits > 1 sums the k-slices of a row group in a fixed order through LDS
+ * (deterministic). */
 typedef struct {
   int32_t rows;
   int32_t unroll;
@@ -152,8 +155,9 @@ gemv_status_t gemv_variant_info(int32_t v, gemv_variant_info_t* info);
  * gemv_run calls on the same handle. */
 gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t* cfg);
 
-/* The configuration gemv_run would use for (n, k, dtype) on this handle.
- * grid is reported as the number of workgroups actually launched. */
+/* The configuration gemv_run would use for (n, k, dtype) on this handle,
+ * for a 16-byte-aligned B (gemv_run also looks at B's alignment).  grid is
+ * reported as the number of workgroups actually launched. */
 gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k, gemv_dtype_t dtype,
                                 gemv_config_t* out);
 

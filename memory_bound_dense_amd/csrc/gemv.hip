@@ -29,6 +29,10 @@ constexpr int kPolNT = 2;
    {&mbd::gemv_kernel<mbd::DT_F16, R, U, W, S, AM, POL, X>,                         \
     &mbd::gemv_kernel<mbd::DT_BF16, R, U, W, S, AM, POL, X>}}
 #define MBD_VARIANT(R, U, W, S, AM, POL) MBD_VARIANT_X(R, U, W, S, AM, POL, false)
+#define MBD_REALIGN(U, W, POL)                                                      \
+  {{1, U, W, 1, mbd::A_LDS_SHIFTED, POL, 0},                                        \
+   {&mbd::gemv_realign_kernel<mbd::DT_F16, U, W, POL>,                              \
+    &mbd::gemv_realign_kernel<mbd::DT_BF16, U, W, POL>}}
 
 // The compiled variants: (rows R, unroll U, waves W, splits S, a mode, B
 // cache policy).  Row variants (S == 1) give each wave R whole rows; split
@@ -67,6 +71,8 @@ const Variant kVariants[] = {
     MBD_VARIANT_X(1, 4, 8, 8, CCH, NT, true), MBD_VARIANT_X(1, 2, 8, 8, CCH, NT, true),
     MBD_VARIANT_X(1, 4, 4, 4, CCH, NT, true), MBD_VARIANT_X(1, 2, 4, 4, CCH, NT, true),
     MBD_VARIANT_X(2, 4, 8, 4, CCH, NT, true), MBD_VARIANT_X(1, 4, 4, 1, CCH, NT, true),
+    // 48..51: rows not 16-byte aligned: aligned B granules, a realigned in LDS
+    MBD_REALIGN(4, 4, NT), MBD_REALIGN(2, 4, NT), MBD_REALIGN(4, 8, NT), MBD_REALIGN(8, 4, NT),
 };
 #undef NT
 #undef LDS
@@ -75,6 +81,10 @@ constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
 size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
   const int64_t nsteps = (k + mbd::kStep - 1) / mbd::kStep;
+  if (v.a_mode == mbd::A_LDS_SHIFTED) {   // two shifted, zero-padded copies of a
+    const int64_t len = mbd::kPadA + (k + 7 + mbd::kStep - 1) / mbd::kStep * mbd::kStep + 8;
+    return (size_t)(4 * len);
+  }
   size_t b = 0;
   if (v.a_mode == mbd::A_LDS) b += (size_t)nsteps * mbd::kStepBytes;
   if (v.splits > 1) b += (size_t)v.waves * v.rows * sizeof(float);
@@ -127,8 +137,16 @@ int find_variant(const Plan& p) {
 //  * k is split inside a workgroup while every wave still streams at least
 //    8 KiB of B, and further (down to two 512-element steps per slice) while
 //    the grid has fewer than 4096 waves.
-Plan rule_plan(int64_t n, int64_t k, size_t max_lds) {
+Plan rule_plan(int64_t n, int64_t k, size_t max_lds, bool b_aligned) {
   const int64_t nfull0 = k / mbd::kStep;
+  // Rows that do not start on 16-byte boundaries: aligned granules of B and a
+  // realigned through LDS (persistent grid: a is staged once per workgroup).
+  // As fast as unaligned 16-byte loads on MI355X and needs no unaligned
+  // access at all.
+  if (k > 0 && (k % 8 != 0 || !b_aligned)) {
+    Plan p = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
+    if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
+  }
   // Too few rows to give the GPU 4096 waves even with 16 waves per row:
   // split k across workgroups too (8 waves per row per workgroup, Q groups,
   // about 2048 waves in all -- more k-groups cost more than they bring on
@@ -156,10 +174,11 @@ Plan rule_plan(int64_t n, int64_t k, size_t max_lds) {
   return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0, 1};
 }
 
-Plan auto_plan(int64_t n, int64_t k, size_t max_lds) {
-  for (const TunedShape& t : kTuned)
-    if (t.n == n && t.k == k) return t.plan;
-  return rule_plan(n, k, max_lds);
+Plan auto_plan(int64_t n, int64_t k, size_t max_lds, bool b_aligned) {
+  if (b_aligned)
+    for (const TunedShape& t : kTuned)
+      if (t.n == n && t.k == k) return t.plan;
+  return rule_plan(n, k, max_lds, b_aligned);
 }
 
 constexpr uint32_t kMagic = 0x47454d56u;   // "GEMV"
@@ -236,7 +255,8 @@ struct Launch {
   size_t lds;
 };
 
-static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, Launch* L) {
+static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, bool b_aligned,
+                             Launch* L) {
   int v;
   int64_t g, q;
   if (h->forced.variant >= 0) {
@@ -244,7 +264,7 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, Launc
     g = h->forced.grid;
     q = h->forced.kgroups;
   } else {
-    const Plan p = auto_plan(n, k, h->max_lds);
+    const Plan p = auto_plan(n, k, h->max_lds, b_aligned);
     v = find_variant(p);
     if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
     g = p.grid;
@@ -374,7 +394,7 @@ extern "C" gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k
   if (dtype != GEMV_F16 && dtype != GEMV_BF16) return GEMV_ERR_UNSUPPORTED_DTYPE;
   if (n <= 0 || k < 0 || n > GEMV_MAX_N || k > GEMV_MAX_K) return GEMV_ERR_INVALID_ARG;
   Launch L;
-  gemv_status_t s = resolve(h, n, k, &L);
+  gemv_status_t s = resolve(h, n, k, true, &L);
   if (s != GEMV_OK) return s;
   out->variant = L.variant;
   out->grid = L.grid;
@@ -392,7 +412,7 @@ extern "C" gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a,
   if (hipGetDevice(&dev) != hipSuccess) return report(h, GEMV_ERR_HIP, "hipGetDevice");
   if (dev != h->device) return report(h, GEMV_ERR_WRONG_DEVICE, "gemv_run");
   Launch L;
-  s = resolve(h, n, k, &L);
+  s = resolve(h, n, k, ((uintptr_t)B & 15u) == 0, &L);
   if (s != GEMV_OK) return report(h, s, "no variant fits (LDS or workspace)");
   const Variant& var = kVariants[L.variant];
   const uint16_t* Bp = (const uint16_t*)B;

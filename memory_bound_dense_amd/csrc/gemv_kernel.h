@@ -42,7 +42,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
-enum { A_LDS = 0, A_CACHED = 1 };
+enum { A_LDS = 0, A_CACHED = 1, A_LDS_SHIFTED = 2 };
 
 constexpr int kLanes = 64;
 constexpr int kVec = 8;                 // 16-bit elements per 16-byte load
@@ -317,6 +317,131 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
       if (threadIdx.x == 0)   // ready for the next call
         __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rows that do not start on a 16-byte boundary (k % 8 != 0, or B itself not
+// 16-byte aligned).  Instead of unaligned 16-byte loads, B is read in aligned
+// 16-byte granules and a is shifted to match: vector v of row i covers row
+// elements [8v - o, 8v - o + 8), o = the row's offset in elements from the
+// granule boundary (0..7), so it needs a[8v - o .. 8v - o + 7].  LDS holds a
+// twice, shifted by 0 and by 1 element behind kPadA zero elements, which makes
+// that window start on a 4-byte boundary for either parity of o (two
+// ds_read2_b32).  The first and last vectors of a row are masked element by
+// element, so nothing from a neighbouring row (a NaN or inf included) enters
+// the sum.  A granule that holds at least one byte of B never crosses a page
+// boundary, so the aligned reads past a row's ends stay in mapped memory.
+// One row per wave, rows dealt to waves in balanced contiguous ranges.
+constexpr int kPadA = 8;
+
+__device__ __forceinline__ uint32_t keep_mask(int j0, int k) {
+  // element j0 in the low half, j0 + 1 in the high half; keep those in [0, k)
+  return ((j0 >= 0 && j0 < k) ? 0x0000ffffu : 0u) | ((j0 + 1 >= 0 && j0 + 1 < k) ? 0xffff0000u : 0u);
+}
+
+template <int DT, int U, int WAVES, int BPOL>
+__global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
+    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
+    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & (kLanes - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // copy 0: a_0[kPadA + x] = a[x]; copy 1: a_1[kPadA + x] = a[x - 1]; zeros elsewhere
+  const int nsteps_max = (k + 7 + kStep - 1) / kStep;
+  const int len = kPadA + nsteps_max * kStep + 8;        // elements per copy, a multiple of 8
+  uint32_t* a0w = reinterpret_cast<uint32_t*>(smem);      // len / 2 dwords each
+  uint32_t* a1w = a0w + len / 2;
+  {
+    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a, (uint32_t)k * 2u);
+    u32x4* a0v = reinterpret_cast<u32x4*>(smem);
+    const bool a16 = ((uintptr_t)a & 15u) == 0;
+    for (int v = threadIdx.x; v < len / kVec; v += WAVES * kLanes) {
+      const int e0 = v * kVec - kPadA;                   // a index of the vector's first element
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (a16 && e0 >= 0) {
+        x = load_vec_tail(arsrc, e0, k, 0u);
+      } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+          const int j = e0 + i;
+          if (j >= 0 && j < k) {
+            uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(arsrc, j * 2, 0u, 0);
+            w[i >> 1] |= h << ((i & 1) * 16);
+          }
+        }
+        x[0] = w[0]; x[1] = w[1]; x[2] = w[2]; x[3] = w[3];
+      }
+      a0v[v] = x;
+    }
+    __syncthreads();
+    for (int w = threadIdx.x; w < len / 2; w += WAVES * kLanes) {
+      const uint32_t cur = a0w[w];
+      const uint32_t prev = w > 0 ? a0w[w - 1] : 0u;
+      a1w[w] = (cur << 16) | (prev >> 16);               // a_1[x] = a_0[x - 1]
+    }
+    __syncthreads();
+  }
+
+  const int64_t units = (int64_t)gridDim.x * WAVES;
+  const int64_t unit = (int64_t)blockIdx.x * WAVES + wave;
+  const int lo = (int)((unit * n) / units);
+  const int hi = (int)(((unit + 1) * n) / units);
+
+  for (int row = lo; row < hi; ++row) {
+    const uint16_t* rowp = B + (int64_t)row * k;
+    const int o = (int)(((uintptr_t)rowp >> 1) & 7u);   // wave-uniform
+    const int nv = (o + k + kVec - 1) / kVec;            // granules touching the row
+    const __amdgpu_buffer_rsrc_t brsrc = make_rsrc(rowp - o, (uint32_t)nv * 16u);
+    const uint32_t* aw = (o & 1) ? a1w : a0w;
+    // dword of the a copy that lines up with element 0 of granule v: (8v - o + (o & 1) + kPadA) / 2
+    const int abase = (kPadA - o + (o & 1)) >> 1;
+    const int nsteps = (nv + kLanes - 1) / kLanes;
+    const int tmid = ((k + o) / kVec) / kLanes;          // steps [1, tmid) need no masks
+    float acc0 = 0.0f, acc1 = 0.0f;
+
+    auto masked_step = [&](int t) {
+      const int v = t * kLanes + lane;
+      u32x4 bv = {0u, 0u, 0u, 0u};
+      if (v < nv) bv = __builtin_amdgcn_raw_buffer_load_b128(brsrc, v * 16, 0u, BPOL);
+      const int j0 = v * kVec - o;                       // row element of the granule's first half-word
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = bv[i];
+        bv[i] = w & keep_mask(j0 + 2 * i, k);
+      }
+      const int d = abase + v * 4;
+      u32x4 av = {aw[d], aw[d + 1], aw[d + 2], aw[d + 3]};
+      fma8<DT>(bv, av, acc0, acc1);
+    };
+
+    masked_step(0);
+    int t = 1;
+    for (; t + U <= tmid; t += U) {
+      u32x4 bv[U], av[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        bv[u] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, ((t + u) * kLanes + lane) * 16, 0u, BPOL);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int d = abase + ((t + u) * kLanes + lane) * 4;
+        av[u][0] = aw[d]; av[u][1] = aw[d + 1]; av[u][2] = aw[d + 2]; av[u][3] = aw[d + 3];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) fma8<DT>(bv[u], av[u], acc0, acc1);
+    }
+    for (; t < tmid; ++t) {
+      const u32x4 bv = __builtin_amdgcn_raw_buffer_load_b128(brsrc, (t * kLanes + lane) * 16, 0u, BPOL);
+      const int d = abase + (t * kLanes + lane) * 4;
+      u32x4 av = {aw[d], aw[d + 1], aw[d + 2], aw[d + 3]};
+      fma8<DT>(bv, av, acc0, acc1);
+    }
+    for (; t < nsteps; ++t) masked_step(t);
+
+    const float tot = wave_sum(acc0 + acc1);
+    if (lane == 0) c[row] = to_bits<DT>(tot);
   }
 }
 

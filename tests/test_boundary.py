@@ -47,7 +47,12 @@ def test_variant_table():
         assert s == mbd.GEMV_OK
         assert info.rows >= 1 and info.unroll >= 1 and info.waves >= 1
         assert info.splits >= 1 and info.waves % info.splits == 0
-        assert info.a_mode in (0, 1)
+        assert info.a_mode in (0, 1, 2)
+        assert info.cross_wg in (0, 1)
+        if info.cross_wg:
+            assert info.a_mode == 1      # a k-chunk per workgroup reads a through the caches
+        if info.a_mode == 2:
+            assert info.rows == 1 and info.splits == 1 and not info.cross_wg
     assert mbd.gemv_variant_info(nv)[0] == _lib.GEMV_ERR_INVALID_ARG
     assert mbd.gemv_variant_info(-1)[0] == _lib.GEMV_ERR_INVALID_ARG
 
