@@ -114,25 +114,25 @@ def stream_probe(nbytes, steps, dev):
     out = torch.empty(1 << 20, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     best = None
-    for grid in (0, 512, 1024, 2048):
+    for grid, xcd in ((0, False), (512, False), (512, True), (1024, False), (2048, False)):
         for i in range(10):
             probe.stream_read(bufs[i % nbuf].data_ptr(), nbytes, out.data_ptr(), out.numel(), grid,
-                              True, stream.cuda_stream)
+                              True, stream.cuda_stream, xcd)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
         for i in range(steps):
             probe.stream_read(bufs[i % nbuf].data_ptr(), nbytes, out.data_ptr(), out.numel(), grid,
-                              True, stream.cuda_stream)
+                              True, stream.cuda_stream, xcd)
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / steps
         if best is None or us < best[0]:
-            best = (us, grid)
+            best = (us, grid, xcd)
     del bufs
     return {"bytes": nbytes, "us": round(best[0], 3), "gbs": round(nbytes / best[0] / 1e3, 1),
-            "grid": best[1]}
+            "grid": best[1], "xcd_contiguous": best[2]}
 
 
 def main():
@@ -215,6 +215,17 @@ def main():
     torch.cuda.synchronize()
     log("[bench] warmup done (%d steps); timing %d steps" % (args.warmup, args.steps))
 
+    # host cost of one gemv_run (validation, plan lookup, launch; ctypes
+    # included), measured on launches that queue behind a busy GPU
+    torch.cuda.synchronize()
+    host = 0.0
+    for i in range(args.steps):
+        t = time.perf_counter()
+        step(i)
+        host += time.perf_counter() - t
+    torch.cuda.synchronize()
+    host_us = host / args.steps * 1e6
+
     # timed region: whole-job throughput, with one event pair on the stream
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -261,6 +272,7 @@ def main():
         "us_per_call": round(ms_per_step * 1e3, 3),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernel_us_avg": round(avg_us, 3),
+        "host_us_per_call": round(host_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -142,7 +142,14 @@ typedef struct {
                          (per workgroup when splits > 1 or cross_wg) */
   int32_t kgroups;    /* cross_wg variants: workgroups sharing a row range
                          along k (0 = automatic); other variants: 0 or 1 */
+  int32_t flags;      /* GEMV_FLAG_* bits */
 } gemv_config_t;
+
+/* Workgroups are dispatched round-robin over the GPU's 8 XCDs.  With this
+ * flag the row ranges are renumbered so that the workgroups of one XCD own
+ * one contiguous block of rows (measured: no gain for the automatic plans,
+ * a gain for some persistent grids). */
+#define GEMV_FLAG_XCD_CONTIGUOUS 1
 
 /* Number of compiled variants. */
 int32_t gemv_num_variants(void);

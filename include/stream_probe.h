@@ -22,13 +22,15 @@ extern "C" {
  * non-zero multiple of 16 KiB) with 16-byte loads, `grid` workgroups of 256
  * lanes that each read 16 KiB per loop trip (0 = one trip per workgroup,
  * capped at 2^20 workgroups),
- * `nontemporal` != 0 marks the loads non-temporal.  Each workgroup writes one
+ * `nontemporal` != 0 marks the loads non-temporal; `xcd_contiguous` != 0
+ * (with a grid that is a multiple of 8) lets the workgroups of each XCD read
+ * one contiguous eighth of the buffer instead of every grid-th chunk.  Each workgroup writes one
  * 32-bit checksum to out[blockIdx] (out holds >= the launched grid; pass
  * out_len to bound it).  Enqueued on `stream`; returns 0 on success, -1 on a
  * bad argument, -2 if the launch failed.  *launched receives the grid used
  * (may be NULL). */
 int mbd_stream_read(const void* src, size_t bytes, uint32_t* out, int out_len, int grid,
-                    int nontemporal, hipStream_t stream, int* launched);
+                    int nontemporal, int xcd_contiguous, hipStream_t stream, int* launched);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,8 @@ GEMV_ERR_UNSUPPORTED = 8
 GEMV_ERR_HIP = 9
 GEMV_ERR_OOM = 10
 
+GEMV_FLAG_XCD_CONTIGUOUS = 1
+
 GEMV_MAX_N = 1073741824
 GEMV_MAX_K = 134217728
 
@@ -51,7 +53,7 @@ class gemv_variant_info_t(ctypes.Structure):
 
 class gemv_config_t(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("kgroups", ctypes.c_int32)]
+                ("kgroups", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 _lib = None
@@ -126,10 +128,10 @@ def gemv_variant_info(v):
     return s, info
 
 
-def gemv_force_config(h, variant=-1, grid=0, kgroups=0):
+def gemv_force_config(h, variant=-1, grid=0, kgroups=0, flags=0):
     if variant is None:
         return load().gemv_force_config(h, None)
-    cfg = gemv_config_t(variant, grid, kgroups)
+    cfg = gemv_config_t(variant, grid, kgroups, flags)
     return load().gemv_force_config(h, ctypes.byref(cfg))
 
 
@@ -171,8 +173,8 @@ class Gemv:
         except Exception:
             pass
 
-    def force_config(self, variant=-1, grid=0, kgroups=0):
-        s = gemv_force_config(self.h, variant, grid, kgroups)
+    def force_config(self, variant=-1, grid=0, kgroups=0, flags=0):
+        s = gemv_force_config(self.h, variant, grid, kgroups, flags)
         if s != GEMV_OK:
             raise GemvError(s, "gemv_force_config")
 

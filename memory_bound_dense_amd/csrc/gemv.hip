@@ -13,7 +13,7 @@
 namespace {
 
 using KernelFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, int, int, float*,
-                          unsigned*);
+                          unsigned*, int);
 
 struct Variant {
   gemv_variant_info_t info;
@@ -252,17 +252,21 @@ struct Launch {
   int variant;
   int grid;      // workgroups along x (row ranges)
   int kgroups;   // workgroups along y (k-groups), 1 unless cross_wg
+  int flags;     // kernel flags
   size_t lds;
 };
+static_assert(GEMV_FLAG_XCD_CONTIGUOUS == mbd::kFlagXcdContiguous, "flag values agree");
 
 static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, bool b_aligned,
                              Launch* L) {
   int v;
   int64_t g, q;
+  int flags = 0;
   if (h->forced.variant >= 0) {
     v = h->forced.variant;
     g = h->forced.grid;
     q = h->forced.kgroups;
+    flags = h->forced.flags;
   } else {
     const Plan p = auto_plan(n, k, h->max_lds, b_aligned);
     v = find_variant(p);
@@ -293,6 +297,7 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, bool 
   L->variant = v;
   L->grid = (int)g;
   L->kgroups = (int)q;
+  L->flags = flags;
   L->lds = l;
   return GEMV_OK;
 }
@@ -350,6 +355,7 @@ extern "C" gemv_status_t gemv_create(gemv_handle_t* out) {
   h->forced.variant = -1;
   h->forced.grid = 0;
   h->forced.kgroups = 0;
+  h->forced.flags = 0;
   h->ws = (float*)mem;
   h->cnt = (unsigned*)((char*)mem + kWsFloats * sizeof(float));
   *out = h;
@@ -378,9 +384,11 @@ extern "C" gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t*
     h->forced.variant = -1;
     h->forced.grid = 0;
     h->forced.kgroups = 0;
+    h->forced.flags = 0;
     return GEMV_OK;
   }
   if (cfg->variant >= kNumVariants || cfg->grid < 0 || cfg->kgroups < 0 ||
+      (cfg->flags & ~GEMV_FLAG_XCD_CONTIGUOUS) != 0 ||
       (!kVariants[cfg->variant].info.cross_wg && cfg->kgroups > 1))
     return report(h, GEMV_ERR_INVALID_ARG, "config");
   h->forced = *cfg;
@@ -399,6 +407,7 @@ extern "C" gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k
   out->variant = L.variant;
   out->grid = L.grid;
   out->kgroups = L.kgroups;
+  out->flags = L.flags;
   return GEMV_OK;
 }
 
@@ -421,7 +430,9 @@ extern "C" gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a,
   int ni = (int)n, ki = (int)k;
   float* ws = h->ws;
   unsigned* cnt = h->cnt;
-  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp, (void*)&ni, (void*)&ki, (void*)&ws, (void*)&cnt};
+  int flags = L.flags;
+  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp, (void*)&ni, (void*)&ki, (void*)&ws, (void*)&cnt,
+                  (void*)&flags};
   hipError_t e = hipLaunchKernel((const void*)var.fn[dtype], dim3((unsigned)L.grid, (unsigned)L.kgroups),
                                  dim3((unsigned)(var.info.waves * mbd::kLanes)), args, L.lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));

@@ -105,6 +105,19 @@ __device__ __forceinline__ void fma8(const u32x4& b, const u32x4& a, float& acc0
   }
 }
 
+// Workgroups are dispatched round-robin over the XCDs (workgroup b runs on
+// XCD b % 8).  With kFlagXcdContiguous the row ranges are renumbered so that
+// each XCD's workgroups own one contiguous block of rows: XCD x takes units
+// [start(x), start(x) + count(x)) with count(x) = G/8 (+1 for x < G % 8).
+constexpr int kXcds = 8;
+constexpr int kFlagXcdContiguous = 1;
+
+__device__ __forceinline__ int64_t xcd_unit(int64_t b, int64_t G) {
+  const int64_t x = b % kXcds, i = b / kXcds;
+  const int64_t q = G / kXcds, r = G % kXcds;
+  return x * q + (x < r ? x : r) + i;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_get(float v) {
   return __builtin_bit_cast(
@@ -135,7 +148,7 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
 template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL, bool XWG>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
-    int n, int k, float* __restrict__ ws, unsigned* __restrict__ cnt) {
+    int n, int k, float* __restrict__ ws, unsigned* __restrict__ cnt, int flags) {
   static_assert(WAVES % S == 0, "splits must divide the waves of a workgroup");
   static_assert(!XWG || AMODE == A_CACHED, "a k-chunk per workgroup does not stage all of a");
   constexpr int G = WAVES / S;   // row groups per workgroup
@@ -181,8 +194,9 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
   // With XWG the ranges are per workgroup as well (the cross-workgroup
   // combine works on a workgroup's whole range).
   constexpr bool kWaveRanges = S == 1 && !XWG;
+  const int64_t wg = (flags & kFlagXcdContiguous) ? xcd_unit(blockIdx.x, gridDim.x) : blockIdx.x;
   const int64_t units = kWaveRanges ? (int64_t)gridDim.x * G : (int64_t)gridDim.x;
-  const int64_t unit = kWaveRanges ? (int64_t)blockIdx.x * G + rg : (int64_t)blockIdx.x;
+  const int64_t unit = kWaveRanges ? wg * G + rg : wg;
   const int lo = (int)((unit * n) / units);
   const int hi = (int)(((unit + 1) * n) / units);
   constexpr int kTrip = kWaveRanges ? R : RB;
@@ -343,7 +357,7 @@ __device__ __forceinline__ uint32_t keep_mask(int j0, int k) {
 template <int DT, int U, int WAVES, int BPOL>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
-    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/) {
+    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/, int flags) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & (kLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -385,8 +399,9 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
     __syncthreads();
   }
 
+  const int64_t wg = (flags & kFlagXcdContiguous) ? xcd_unit(blockIdx.x, gridDim.x) : blockIdx.x;
   const int64_t units = (int64_t)gridDim.x * WAVES;
-  const int64_t unit = (int64_t)blockIdx.x * WAVES + wave;
+  const int64_t unit = wg * WAVES + wave;
   const int lo = (int)((unit * n) / units);
   const int hi = (int)(((unit + 1) * n) / units);
 

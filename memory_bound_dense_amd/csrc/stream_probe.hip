@@ -13,12 +13,26 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 constexpr int kRsrcWord3 = 0x00020000;
 
+// xcd != 0: workgroup b (dispatched to XCD b % 8) reads the chunks of a
+// contiguous eighth of the buffer instead of every gridDim-th chunk.
 template <int POL>
 __global__ __launch_bounds__(kThreads) void stream_read(const uint8_t* __restrict__ src,
-                                                        uint64_t nvec, uint32_t* __restrict__ out) {
+                                                        uint64_t nvec, uint32_t* __restrict__ out,
+                                                        int xcd) {
   uint32_t acc = 0;
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads * kUnroll;
-  for (uint64_t base = (uint64_t)blockIdx.x * kThreads * kUnroll; base < nvec; base += stride) {
+  const uint64_t per = (uint64_t)kThreads * kUnroll;
+  const uint64_t nchunks = nvec / per;
+  uint64_t first = blockIdx.x, step = gridDim.x, stop = nchunks;
+  if (xcd && gridDim.x % 8 == 0) {
+    // XCD x = blockIdx % 8 owns chunks [x*nchunks/8, (x+1)*nchunks/8)
+    const uint64_t x = blockIdx.x % 8, i = blockIdx.x / 8, g8 = gridDim.x / 8;
+    const uint64_t lo = x * nchunks / 8, hi = (x + 1) * nchunks / 8;
+    first = lo + i;
+    step = g8;
+    stop = hi;
+  }
+  for (uint64_t ch = first; ch < stop; ch += step) {
+    const uint64_t base = ch * per;
     // one descriptor per whole 16 KiB chunk (the host only accepts whole
     // chunks), so every offset below is inside the buffer
     __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -48,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void stream_read(const uint8_t* __restric
 }  // namespace
 
 extern "C" int mbd_stream_read(const void* src, size_t bytes, uint32_t* out, int out_len, int grid,
-                               int nontemporal, hipStream_t stream, int* launched) {
+                               int nontemporal, int xcd, hipStream_t stream, int* launched) {
   if (!src || !out || out_len < 1 || bytes == 0 || (bytes % (kThreads * kUnroll * 16)) != 0 ||
       ((uintptr_t)src % 16) != 0 || grid < 0)
     return -1;
@@ -61,9 +75,9 @@ extern "C" int mbd_stream_read(const void* src, size_t bytes, uint32_t* out, int
   if (launched) *launched = (int)g;
   if (nontemporal)
     hipLaunchKernelGGL(stream_read<2>, dim3((unsigned)g), dim3(kThreads), 0, stream,
-                       (const uint8_t*)src, nvec, out);
+                       (const uint8_t*)src, nvec, out, xcd);
   else
     hipLaunchKernelGGL(stream_read<0>, dim3((unsigned)g), dim3(kThreads), 0, stream,
-                       (const uint8_t*)src, nvec, out);
+                       (const uint8_t*)src, nvec, out, xcd);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

@@ -19,18 +19,19 @@ def load():
                                "`python -m memory_bound_dense_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
         lib.mbd_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                        ctypes.POINTER(ctypes.c_int)]
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
         lib.mbd_stream_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
 
-def stream_read(src_ptr, nbytes, out_ptr, out_len, grid=0, nontemporal=True, stream=None):
+def stream_read(src_ptr, nbytes, out_ptr, out_len, grid=0, nontemporal=True, stream=None,
+                xcd_contiguous=False):
     """Enqueue one streaming read; returns the workgroup count launched."""
     launched = ctypes.c_int(0)
     rc = load().mbd_stream_read(src_ptr, nbytes, out_ptr, out_len, grid, int(bool(nontemporal)),
-                                stream, ctypes.byref(launched))
+                                int(bool(xcd_contiguous)), stream, ctypes.byref(launched))
     if rc != 0:
         raise RuntimeError("mbd_stream_read failed (%d)" % rc)
     return launched.value

@@ -1,0 +1,101 @@
+"""GPU: gemv_run under HIP graph capture and from several streams.
+
+* capture: calls enqueued while torch captures a HIP graph (one shape on
+  each path: rows, in-workgroup split, cross-workgroup split, realigned
+  rows) replay correctly, every replay checked against the eager result,
+  with eager work and synchronisations between replays;
+* streams: two handles driving two streams (default priority) with host
+  delays in between give bitwise the same c as a quiet run.
+"""
+import random
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_dense_amd as mbd
+from gemv_inputs import BF16, F16, random_inputs
+from parity import to_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(18432, 7168, F16), (7168, 16384, BF16), (64, 65536, BF16), (1000, 7001, BF16),
+          (256, 512, F16)]
+
+
+def _inputs():
+    out = []
+    for i, (n, k, dtype) in enumerate(SHAPES):
+        B, a = random_inputs(n, k, dtype, seed=100 + i)
+        out.append((to_device(B, dtype), to_device(a, dtype)))
+    return out
+
+
+def test_graph_capture_replays():
+    g = mbd.Gemv()
+    ins = _inputs()
+    eager = []
+    for Bd, ad in ins:
+        c = torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda")
+        g(Bd, ad, c)
+        eager.append(c)
+    torch.cuda.synchronize()
+    ref = [to_bits(c) for c in eager]
+    outs = [torch.zeros(Bd.shape[0], dtype=Bd.dtype, device="cuda") for Bd, _ in ins]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for (Bd, ad), c in zip(ins, outs):
+                g(Bd, ad, c)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(5):
+        for c in outs:
+            c.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, c in enumerate(outs):
+            assert np.array_equal(to_bits(c), ref[i]), (rep, SHAPES[i])
+        # an eager call between replays must not disturb the next replay
+        Bd, ad = ins[2]
+        g(Bd, ad, eager[2])
+        torch.cuda.synchronize()
+        del junk
+    g.close()
+
+
+def test_two_streams_two_handles_repeatable():
+    ins = _inputs()
+    g1, g2 = mbd.Gemv(), mbd.Gemv()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ref = []
+    for Bd, ad in ins:
+        c = torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda")
+        g1(Bd, ad, c)
+        torch.cuda.synchronize()
+        ref.append(to_bits(c))
+    rng = random.Random(0)
+    outs1 = [torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda") for Bd, _ in ins]
+    outs2 = [torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda") for Bd, _ in ins]
+    for it in range(40):
+        order = list(range(len(ins)))
+        rng.shuffle(order)
+        for i in order:
+            Bd, ad = ins[i]
+            with torch.cuda.stream(s1):
+                g1(Bd, ad, outs1[i])
+            if rng.random() < 0.3:
+                time.sleep(rng.random() * 1e-4)
+            with torch.cuda.stream(s2):
+                g2(Bd, ad, outs2[i])
+        torch.cuda.synchronize()
+        for i in range(len(ins)):
+            assert np.array_equal(to_bits(outs1[i]), ref[i]), (it, SHAPES[i])
+            assert np.array_equal(to_bits(outs2[i]), ref[i]), (it, SHAPES[i])
+    g1.close()
+    g2.close()
