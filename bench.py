@@ -141,7 +141,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="gemv_18432x7168_f16",
-                    help="workload name (see gemv_inputs.ALL_WORKLOADS)")
+                    help="workload name (gemv_inputs.ALL_WORKLOADS / EXTRA_WORKLOADS)")
+    ap.add_argument("--shape", default="", help="ad-hoc shape 'n,k,f16|bf16' instead of --workload")
     ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (-1 = auto)")
     ap.add_argument("--grid", type=int, default=0, help="force the workgroup count (0 = auto)")
     ap.add_argument("--kgroups", type=int, default=0,
@@ -163,12 +164,13 @@ def main():
     import numpy as np
     import torch
     import memory_bound_dense_amd as mbd
-    from gemv_inputs import ALL_WORKLOADS, DTYPE_NAMES, algorithmic_bytes, random_inputs, torch_dtype
+    from gemv_inputs import (ALL_WORKLOADS, DTYPE_NAMES, EXTRA_WORKLOADS, algorithmic_bytes,
+                             find_workload, random_inputs, shape_workload, torch_dtype)
 
-    wl = {w[0]: w for w in ALL_WORKLOADS}.get(args.workload)
+    wl = shape_workload(args.shape) if args.shape else find_workload(args.workload)
     if wl is None:
-        print("unknown workload %r; known: %s" % (args.workload, [w[0] for w in ALL_WORKLOADS]),
-              file=sys.stderr)
+        print("unknown workload %r; known: %s" % (
+            args.workload, [w[0] for w in ALL_WORKLOADS + EXTRA_WORKLOADS]), file=sys.stderr)
         sys.exit(2)
     name, n, k, dtype, dist = wl
     if not torch.cuda.is_available():

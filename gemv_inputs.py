@@ -75,6 +75,28 @@ RAGGED = [("ragged_%dx%d_bf16" % (n, k), n, k, BF16, "normal")
           for (n, k) in [(64, 65536), (1000, 7000), (18433, 7169)]]
 ALL_WORKLOADS = [TINY, PROD_F16, PROD_BF16] + SWEEP + RAGGED
 
+# Larger production shapes (TileLang Case Studies, Case B.3 "Shapes Added":
+# an MLP gate/up projection and an aggregated MoE output) and the small
+# square shape of the Case B results table.
+LARGE = [("large_%dx%d_%s" % (n, k, DTYPE_NAMES[d]), n, k, d, "normal")
+         for (n, k) in [(28672, 8192), (57344, 7168)] for d in (F16, BF16)]
+SQUARE = [("square_1024x1024_f16", 1024, 1024, F16, "normal")]
+EXTRA_WORKLOADS = LARGE + SQUARE
+
+
+def find_workload(name):
+    for w in ALL_WORKLOADS + EXTRA_WORKLOADS:
+        if w[0] == name:
+            return w
+    return None
+
+
+def shape_workload(spec):
+    """'n,k,f16|bf16' -> an ad-hoc workload tuple (normal distribution)."""
+    n, k, d = spec.split(",")
+    dt = {"f16": F16, "bf16": BF16}[d]
+    return ("shape_%sx%s_%s" % (n, k, d), int(n), int(k), dt, "normal")
+
 
 def algorithmic_bytes(n: int, k: int, elem_bytes: int = 2) -> int:
     """Bytes a GEMV must move at least once: B, a and c."""

@@ -134,6 +134,10 @@ typedef struct {
   int32_t b_policy;   /* cache-policy bits of the B loads (0 = default) */
   int32_t cross_wg;   /* 1: kgroups workgroups share each row range along k,
                          combining through the handle's workspace */
+  int32_t layout;     /* 0: lanes along k (coalesced); 1: one row per lane,
+                         one element per step -- the uncoalesced layout of
+                         TileLang Case Studies, Case B, kept for measurement
+                         and never chosen automatically */
 } gemv_variant_info_t;
 
 typedef struct {

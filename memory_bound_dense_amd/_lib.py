@@ -48,7 +48,8 @@ class GemvError(RuntimeError):
 class gemv_variant_info_t(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("unroll", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("splits", ctypes.c_int32), ("a_mode", ctypes.c_int32),
-                ("b_policy", ctypes.c_int32), ("cross_wg", ctypes.c_int32)]
+                ("b_policy", ctypes.c_int32), ("cross_wg", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class gemv_config_t(ctypes.Structure):

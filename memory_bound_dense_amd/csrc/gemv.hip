@@ -23,14 +23,15 @@ struct Variant {
 // Cache-policy bits of the B loads on gfx950: bit 1 marks the access
 // non-temporal (B has no reuse within a call).
 constexpr int kPolNT = 2;
+constexpr int kLanesPerWave = 64;
 
 #define MBD_VARIANT_X(R, U, W, S, AM, POL, X)                                       \
-  {{R, U, W, S, AM, POL, X},                                                        \
+  {{R, U, W, S, AM, POL, X, 0},                                                     \
    {&mbd::gemv_kernel<mbd::DT_F16, R, U, W, S, AM, POL, X>,                         \
     &mbd::gemv_kernel<mbd::DT_BF16, R, U, W, S, AM, POL, X>}}
 #define MBD_VARIANT(R, U, W, S, AM, POL) MBD_VARIANT_X(R, U, W, S, AM, POL, false)
 #define MBD_REALIGN(U, W, POL)                                                      \
-  {{1, U, W, 1, mbd::A_LDS_SHIFTED, POL, 0},                                        \
+  {{1, U, W, 1, mbd::A_LDS_SHIFTED, POL, 0, 0},                                     \
    {&mbd::gemv_realign_kernel<mbd::DT_F16, U, W, POL>,                              \
     &mbd::gemv_realign_kernel<mbd::DT_BF16, U, W, POL>}}
 
@@ -73,6 +74,9 @@ const Variant kVariants[] = {
     MBD_VARIANT_X(2, 4, 8, 4, CCH, NT, true), MBD_VARIANT_X(1, 4, 4, 1, CCH, NT, true),
     // 48..51: rows not 16-byte aligned: aligned B granules, a realigned in LDS
     MBD_REALIGN(4, 4, NT), MBD_REALIGN(2, 4, NT), MBD_REALIGN(4, 8, NT), MBD_REALIGN(8, 4, NT),
+    // 52: one row per lane, one element per step (the uncoalesced layout; study only)
+    {{kLanesPerWave, 1, 4, 1, mbd::A_CACHED, 0, 0, 1},
+     {&mbd::gemv_rowlane_kernel<mbd::DT_F16, 4>, &mbd::gemv_rowlane_kernel<mbd::DT_BF16, 4>}},
 };
 #undef NT
 #undef LDS
@@ -92,6 +96,7 @@ size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
 }
 
 int64_t rows_per_block(const gemv_variant_info_t& v) { return (int64_t)(v.waves / v.splits) * v.rows; }
+// (for layout 1, rows == 64: one row per lane)
 
 // Device workspace of a handle: fp32 partial sums (kgroups x n) and one
 // arrival counter per row range, for the cross-workgroup variants.
@@ -122,7 +127,7 @@ int find_variant(const Plan& p) {
   for (int v = 0; v < kNumVariants; ++v) {
     const gemv_variant_info_t& i = kVariants[v].info;
     if (i.rows == p.rows && i.unroll == p.unroll && i.waves == p.waves && i.splits == p.splits &&
-        i.a_mode == p.a_mode && i.b_policy == p.policy && i.cross_wg == x)
+        i.a_mode == p.a_mode && i.b_policy == p.policy && i.cross_wg == x && i.layout == 0)
       return v;
   }
   return -1;
@@ -282,6 +287,8 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, bool 
   // keep the launch's work-item count well inside 32 bits
   const int64_t gmax = (int64_t)1 << 24;
   if (g > gmax) g = gmax;
+  if (info.layout == 1 && (int64_t)kLanesPerWave * k * 2 >= ((int64_t)1 << 32))
+    return GEMV_ERR_UNSUPPORTED;   // a wave's 64 rows must fit one buffer descriptor
   if (info.cross_wg) {
     if (q <= 0) q = 4;
     if (q > 1024) return GEMV_ERR_UNSUPPORTED;

@@ -460,4 +460,44 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The uncoalesced layout, kept for measurement only (TileLang Case Studies,
+// Case B "Root Cause": the thread index that varies fastest within a warp
+// walked the rows, so neighbouring lanes read addresses a row apart).  Here
+// lane l of a wave owns one row and walks k one element at a time: the 64
+// loads of one wave instruction land 2k bytes apart.  Never chosen by the
+// automatic plan.
+template <int DT, int WAVES>
+__global__ __launch_bounds__(WAVES * kLanes) void gemv_rowlane_kernel(
+    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
+    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/, int /*flags*/) {
+  const int lane = threadIdx.x & (kLanes - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a, (uint32_t)k * 2u);
+  // rows of this wave: [row0, row0 + 64); the descriptor starts at row0
+  for (int64_t row0 = ((int64_t)blockIdx.x * WAVES + wave) * kLanes; row0 < n;
+       row0 += (int64_t)gridDim.x * WAVES * kLanes) {
+    const int nrows = (n - row0) < kLanes ? (int)(n - row0) : kLanes;
+    const int r = lane < nrows ? lane : nrows - 1;
+    const __amdgpu_buffer_rsrc_t brsrc =
+        make_rsrc(B + row0 * k, (uint32_t)nrows * (uint32_t)k * 2u);
+    const uint32_t roff = (uint32_t)r * (uint32_t)k * 2u;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t bb = __builtin_amdgcn_raw_buffer_load_b16(brsrc, roff + j * 2, 0u, 0);
+      const uint32_t aa = __builtin_amdgcn_raw_buffer_load_b16(arsrc, j * 2, 0u, 0);
+      float bf, af;
+      if constexpr (DT == DT_F16) {
+        bf = (float)__builtin_bit_cast(_Float16, (uint16_t)bb);
+        af = (float)__builtin_bit_cast(_Float16, (uint16_t)aa);
+      } else {
+        bf = __builtin_bit_cast(float, bb << 16);
+        af = __builtin_bit_cast(float, aa << 16);
+      }
+      acc = __builtin_fmaf(bf, af, acc);
+    }
+    if (lane < nrows) c[row0 + lane] = to_bits<DT>(acc);
+  }
+}
+
 }  // namespace mbd

@@ -51,8 +51,8 @@ def run_gemv(workload, launches):
     import numpy as np
     import torch
     import memory_bound_dense_amd as mbd
-    from gemv_inputs import ALL_WORKLOADS, random_inputs, torch_dtype
-    name, n, k, dtype, dist = {w[0]: w for w in ALL_WORKLOADS}[workload]
+    from gemv_inputs import find_workload, random_inputs, torch_dtype
+    name, n, k, dtype, dist = find_workload(workload)
     dev = torch.device("cuda", 0)
     td = torch_dtype(dtype)
     B_bits, a_bits = random_inputs(n, k, dtype, dist, seed=0)
@@ -138,8 +138,8 @@ def summarize_trace(stats_csv, trace_csv, command, out):
 
 def summarize_counters(workload, fetch, write, copy_fetch, copy_write, copy_bytes, commands, out):
     sys.path.insert(0, ROOT)
-    from gemv_inputs import ALL_WORKLOADS, algorithmic_bytes
-    name, n, k, dtype, dist = {w[0]: w for w in ALL_WORKLOADS}[workload]
+    from gemv_inputs import algorithmic_bytes, find_workload
+    name, n, k, dtype, dist = find_workload(workload)
     alg = algorithmic_bytes(n, k)
     f_g = statistics.median(counter_per_dispatch(fetch, GEMV_KERNEL, "FETCH_SIZE")) * 1024
     w_g = statistics.median(counter_per_dispatch(write, GEMV_KERNEL, "WRITE_SIZE")) * 1024

@@ -53,6 +53,9 @@ def test_variant_table():
             assert info.a_mode == 1      # a k-chunk per workgroup reads a through the caches
         if info.a_mode == 2:
             assert info.rows == 1 and info.splits == 1 and not info.cross_wg
+        assert info.layout in (0, 1)
+        if info.layout == 1:
+            assert info.rows == 64 and info.splits == 1 and not info.cross_wg
     assert mbd.gemv_variant_info(nv)[0] == _lib.GEMV_ERR_INVALID_ARG
     assert mbd.gemv_variant_info(-1)[0] == _lib.GEMV_ERR_INVALID_ARG
 

@@ -16,8 +16,8 @@ import torch
 
 import memory_bound_dense_amd as mbd
 import oracle
-from gemv_inputs import (ALL_WORKLOADS, BF16, F16, integer_inputs, random_inputs, torch_dtype,
-                         values_to_bits)
+from gemv_inputs import (ALL_WORKLOADS, BF16, EXTRA_WORKLOADS, F16, integer_inputs, random_inputs,
+                         torch_dtype, values_to_bits)
 from parity import compare, oracle_rows, sample_rows, to_bits, to_device
 
 pytestmark = pytest.mark.gpu
@@ -159,7 +159,8 @@ def test_column_extraction(g, dtype):
                 assert got is None or np.array_equal(got, B[:, j]), (n, k, j, v)
 
 
-@pytest.mark.parametrize("wl", ALL_WORKLOADS, ids=[w[0] for w in ALL_WORKLOADS])
+@pytest.mark.parametrize("wl", ALL_WORKLOADS + EXTRA_WORKLOADS,
+                         ids=[w[0] for w in ALL_WORKLOADS + EXTRA_WORKLOADS])
 def test_workload_full_size(g, wl):
     name, n, k, dtype, dist = wl
     B, a = random_inputs(n, k, dtype, dist, seed=0)
