@@ -45,6 +45,9 @@ def _load():
     lib.oracle_gemv.argtypes = [ctypes.c_int, u16p, u16p, ctypes.c_int64, ctypes.c_int64,
                                 u16p, dp, dp, dp]
     lib.oracle_gemv.restype = ctypes.c_int
+    lib.oracle_gemv_epilogue.argtypes = [ctypes.c_int, u16p, u16p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_float, u16p, u16p, dp, dp, dp]
+    lib.oracle_gemv_epilogue.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -102,3 +105,34 @@ def gemv(dtype: int, B, a):
     if rc != 0:
         raise ValueError("oracle.gemv: bad argument")
     return c, s, ab
+
+
+def gemv_epilogue(dtype: int, B, a, alpha: float, bias=None):
+    """c = round(alpha * (B @ a) + bias) on 16-bit patterns; alpha is taken as
+    a float32 value, bias (n,) uint16 patterns or None.
+    Returns (c_bits, y float64 = alpha*s + bias before rounding, abs = sum_j |B_ij a_j|)."""
+    import numpy as np
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    if B.ndim != 2 or a.ndim != 1 or B.shape[1] != a.shape[0]:
+        raise ValueError("oracle.gemv_epilogue: B must be (n, k) and a (k,)")
+    n, k = B.shape
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    dp = ctypes.POINTER(ctypes.c_double)
+    bp = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+        if bias.shape != (n,):
+            raise ValueError("oracle.gemv_epilogue: bias must be (n,)")
+        bp = bias.ctypes.data_as(u16p)
+    c = np.empty(n, dtype=np.uint16)
+    y = np.empty(n, dtype=np.float64)
+    ab = np.empty(n, dtype=np.float64)
+    scratch = np.empty(max(k, 1), dtype=np.float64)
+    rc = _load().oracle_gemv_epilogue(dtype, B.ctypes.data_as(u16p), a.ctypes.data_as(u16p), n, k,
+                                      float(np.float32(alpha)), bp, c.ctypes.data_as(u16p),
+                                      y.ctypes.data_as(dp), ab.ctypes.data_as(dp),
+                                      scratch.ctypes.data_as(dp))
+    if rc != 0:
+        raise ValueError("oracle.gemv_epilogue: bad argument")
+    return c, y, ab

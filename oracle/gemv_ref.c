@@ -135,6 +135,15 @@ void oracle_encode_array(int dtype, const double* x, uint16_t* out, int64_t coun
 
 /* ---- the GEMV ------------------------------------------------------------ */
 
+/* With an epilogue (page "Optimizing TileLang Programs", epilogue fusion:
+ * post-operations applied before the single write of the result):
+ *     c[i] = round_to_dtype( alpha * sum_j B[i][j] a[j] + bias[i] )
+ * alpha is a float32 value (exact in double), bias[i] a `dtype` value (exact
+ * in double); the expression is evaluated in double and rounded once. */
+int oracle_gemv_epilogue(int dtype, const uint16_t* B, const uint16_t* a, int64_t n, int64_t k,
+                         float alpha, const uint16_t* bias, uint16_t* c, double* s,
+                         double* abs_out, double* a_scratch);
+
 /* B: n*k 16-bit patterns, row-major (row i starts at B + i*k).
  * a: k patterns.  Outputs, per row i:
  *   c[i]   rounded result (16-bit pattern of `dtype`),
@@ -157,6 +166,29 @@ int oracle_gemv(int dtype, const uint16_t* B, const uint16_t* a, int64_t n, int6
     }
     c[i] = oracle_encode(dtype, sum);
     if (s) s[i] = sum;
+    if (abs_out) abs_out[i] = asum;
+  }
+  return 0;
+}
+
+int oracle_gemv_epilogue(int dtype, const uint16_t* B, const uint16_t* a, int64_t n, int64_t k,
+                         float alpha, const uint16_t* bias, uint16_t* c, double* s,
+                         double* abs_out, double* a_scratch) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  if (n < 0 || k < 0) return -1;
+  for (int64_t j = 0; j < k; ++j) a_scratch[j] = oracle_decode(dtype, a[j]);
+  for (int64_t i = 0; i < n; ++i) {
+    const uint16_t* row = B + i * k;
+    double sum = 0.0, asum = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      double p = oracle_decode(dtype, row[j]) * a_scratch[j];
+      sum += p;
+      asum += fabs(p);
+    }
+    double y = (double)alpha * sum;
+    if (bias) y += oracle_decode(dtype, bias[i]);
+    c[i] = oracle_encode(dtype, y);
+    if (s) s[i] = y;
     if (abs_out) abs_out[i] = asum;
   }
   return 0;

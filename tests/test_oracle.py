@@ -278,3 +278,52 @@ def test_inputs_are_seeded():
     # N(0,1)/sqrt(k) rows: the row norm is near 1
     v = oracle.decode(F16, B1)
     assert 0.5 < float(np.sqrt((v ** 2).sum(axis=1)).mean()) < 1.5
+
+
+# ---- epilogue: c = round(alpha * (B @ a) + bias) --------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_epilogue_identity_settings_match_plain(dtype):
+    """alpha = 1 and no bias is the plain product, bit for bit."""
+    B, a = random_inputs(40, 1031, dtype, seed=31)
+    c0, s0, _ = oracle.gemv(dtype, B, a)
+    c1, y1, _ = oracle.gemv_epilogue(dtype, B, a, 1.0, None)
+    assert np.array_equal(c0, c1) and np.array_equal(s0, y1)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_epilogue_integer_exact(dtype):
+    """Integer B, a, bias and a power-of-two alpha: the result is the exact
+    integer expression, rounded once (checked with Python integers)."""
+    n, k = 50, 700
+    B, a = integer_inputs(n, k, dtype, seed=33)
+    g = np.random.default_rng(3)
+    bias_v = g.integers(-40, 41, size=n).astype(np.float64)
+    bias = values_to_bits(bias_v, dtype)
+    Bi = oracle.decode(dtype, B).astype(np.int64)
+    ai = oracle.decode(dtype, a).astype(np.int64)
+    exact = Bi @ ai
+    for alpha in (1.0, 2.0, -0.5, 0.25):
+        c, y, _ = oracle.gemv_epilogue(dtype, B, a, alpha, bias)
+        want = [alpha * float(e) + float(b) for e, b in zip(exact, bias_v)]
+        assert np.array_equal(y, np.array(want))
+        assert np.array_equal(c, np.array([refround.round_bits(dtype, w) for w in want],
+                                          dtype=np.uint16))
+
+
+def test_epilogue_hand_case():
+    """By hand (fp16): B = [[1, 2], [3, 4]], a = [1, 1], alpha = 0.5,
+    bias = [10, -1]: c = [0.5*3 + 10, 0.5*7 - 1] = [11.5, 2.5]."""
+    B = values_to_bits(np.array([[1.0, 2.0], [3.0, 4.0]]), F16)
+    a = values_to_bits(np.array([1.0, 1.0]), F16)
+    bias = values_to_bits(np.array([10.0, -1.0]), F16)
+    c, _, _ = oracle.gemv_epilogue(F16, B, a, 0.5, bias)
+    assert list(oracle.decode(F16, c)) == [11.5, 2.5]
+
+
+def test_epilogue_alpha_is_float32():
+    """alpha is taken at float32 precision: 0.1 becomes 0.100000001490116..."""
+    B = values_to_bits(np.array([[1.0]]), F16)
+    a = values_to_bits(np.array([1024.0]), F16)
+    _, y, _ = oracle.gemv_epilogue(F16, B, a, 0.1, None)
+    assert y[0] == float(np.float32(0.1)) * 1024.0
