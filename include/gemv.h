@@ -97,12 +97,33 @@ gemv_status_t gemv_create(gemv_handle_t* out);
 gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a, void* c,
                        int64_t n, int64_t k, gemv_dtype_t dtype, hipStream_t stream);
 
+/* The fused epilogue (page "Optimizing TileLang Programs", epilogue fusion:
+ * post-operations applied in registers before the single write of c):
+ *     c[i] = round_to_dtype( alpha * sum_j B[i][j] a[j] + bias[i] )
+ * computed as one fp32 FMA on the fp32 row sum (alpha * sum without bias).
+ * bias: n elements of the same dtype (2-byte aligned) or NULL; it may be c
+ * itself (accumulate in place) but must not partly overlap c. */
+typedef struct {
+  float alpha;
+  const void* bias;
+} gemv_epilogue_t;
+
+/* gemv_run with an epilogue; ep == NULL is exactly gemv_run.  Validation as
+ * gemv_run, then the bias checks (GEMV_ERR_MISALIGNED, GEMV_ERR_ALIASING). */
+gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void* a, void* c,
+                          int64_t n, int64_t k, gemv_dtype_t dtype, const gemv_epilogue_t* ep,
+                          hipStream_t stream);
+
 /* Every check gemv_run makes that needs neither a handle nor a GPU, in the
  * same order and with the same result: GEMV_OK means gemv_run would go on to
  * the device check and the launch (or return GEMV_OK at once when n == 0).
  * Pure host arithmetic on the pointer values; nothing is dereferenced. */
 gemv_status_t gemv_check_args(const void* B, const void* a, const void* c, int64_t n, int64_t k,
                               gemv_dtype_t dtype);
+
+/* The same for gemv_run_ex (ep may be NULL). */
+gemv_status_t gemv_check_args_ex(const void* B, const void* a, const void* c, int64_t n, int64_t k,
+                                 gemv_dtype_t dtype, const gemv_epilogue_t* ep);
 
 /* Release the handle and its workspace.  NULL is a no-op.  Waits for the
  * handle's device to finish outstanding work first (a kernel in flight may

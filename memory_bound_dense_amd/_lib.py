@@ -35,8 +35,9 @@ GEMV_MAX_N = 1073741824
 GEMV_MAX_K = 134217728
 
 # every symbol include/gemv.h declares
-EXPORTS = ("gemv_create", "gemv_run", "gemv_destroy", "gemv_status_string", "gemv_check_args",
-           "gemv_num_variants", "gemv_variant_info", "gemv_force_config", "gemv_query_config")
+EXPORTS = ("gemv_create", "gemv_run", "gemv_run_ex", "gemv_destroy", "gemv_status_string",
+           "gemv_check_args", "gemv_check_args_ex", "gemv_num_variants", "gemv_variant_info",
+           "gemv_force_config", "gemv_query_config")
 
 
 class GemvError(RuntimeError):
@@ -50,6 +51,10 @@ class gemv_variant_info_t(ctypes.Structure):
                 ("splits", ctypes.c_int32), ("a_mode", ctypes.c_int32),
                 ("b_policy", ctypes.c_int32), ("cross_wg", ctypes.c_int32),
                 ("layout", ctypes.c_int32)]
+
+
+class gemv_epilogue_t(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_float), ("bias", ctypes.c_void_p)]
 
 
 class gemv_config_t(ctypes.Structure):
@@ -75,6 +80,12 @@ def load():
     lib.gemv_create.restype = st
     lib.gemv_run.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int, vp]
     lib.gemv_run.restype = st
+    lib.gemv_run_ex.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int,
+                                ctypes.POINTER(gemv_epilogue_t), vp]
+    lib.gemv_run_ex.restype = st
+    lib.gemv_check_args_ex.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int,
+                                       ctypes.POINTER(gemv_epilogue_t)]
+    lib.gemv_check_args_ex.restype = st
     lib.gemv_destroy.argtypes = [vp]
     lib.gemv_destroy.restype = st
     lib.gemv_status_string.argtypes = [st]
@@ -105,6 +116,19 @@ def gemv_create():
 def gemv_run(h, B, a, c, n, k, dtype, stream=None):
     """B, a, c: device addresses (ints); stream: hipStream_t as int or None."""
     return load().gemv_run(h, B, a, c, n, k, dtype, stream)
+
+
+def gemv_run_ex(h, B, a, c, n, k, dtype, alpha=1.0, bias=None, stream=None):
+    """gemv_run with the epilogue c = alpha * (B @ a) + bias (bias: address or None)."""
+    ep = gemv_epilogue_t(alpha, bias)
+    return load().gemv_run_ex(h, B, a, c, n, k, dtype, ctypes.byref(ep), stream)
+
+
+def gemv_check_args_ex(B, a, c, n, k, dtype, alpha=None, bias=None):
+    if alpha is None and bias is None:
+        return load().gemv_check_args_ex(B, a, c, n, k, dtype, None)
+    ep = gemv_epilogue_t(1.0 if alpha is None else alpha, bias)
+    return load().gemv_check_args_ex(B, a, c, n, k, dtype, ctypes.byref(ep))
 
 
 def gemv_destroy(h):
@@ -185,7 +209,9 @@ class Gemv:
             raise GemvError(s, "gemv_query_config")
         return cfg.variant, cfg.grid, cfg.kgroups
 
-    def __call__(self, B, a, c, stream=None):
+    def __call__(self, B, a, c, stream=None, alpha=None, bias=None):
+        """c = B @ a, or c = alpha * (B @ a) + bias when alpha or bias is given
+        (bias: an (n,) tensor of the same dtype, possibly c itself)."""
         import torch
         if B.dim() != 2 or a.dim() != 1 or c.dim() != 1:
             raise GemvError(GEMV_ERR_INVALID_ARG, "B must be 2-D, a and c 1-D")
@@ -200,7 +226,17 @@ class Gemv:
             raise GemvError(GEMV_ERR_UNSUPPORTED_DTYPE, "B, a and c must share one dtype")
         if stream is None:
             stream = torch.cuda.current_stream(B.device).cuda_stream
-        s = gemv_run(self.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, dt, stream)
+        if alpha is None and bias is None:
+            s = gemv_run(self.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, dt, stream)
+        else:
+            bp = None
+            if bias is not None:
+                if bias.dim() != 1 or bias.shape[0] != n or bias.dtype != B.dtype or \
+                        not bias.is_contiguous():
+                    raise GemvError(GEMV_ERR_INVALID_ARG, "bias must be a dense (n,) tensor of B's dtype")
+                bp = bias.data_ptr()
+            s = gemv_run_ex(self.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, dt,
+                            1.0 if alpha is None else float(alpha), bp, stream)
         if s != GEMV_OK:
             raise GemvError(s, "gemv_run")
         return c

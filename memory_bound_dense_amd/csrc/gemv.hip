@@ -13,7 +13,7 @@
 namespace {
 
 using KernelFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, int, int, float*,
-                          unsigned*, int);
+                          unsigned*, int, float, const uint16_t*);
 
 struct Variant {
   gemv_variant_info_t info;
@@ -237,6 +237,12 @@ extern "C" gemv_status_t gemv_variant_info(int32_t v, gemv_variant_info_t* info)
 // Every check of gemv_run that needs neither the handle nor the GPU.
 extern "C" gemv_status_t gemv_check_args(const void* B, const void* a, const void* c, int64_t n,
                                          int64_t k, gemv_dtype_t dtype) {
+  return gemv_check_args_ex(B, a, c, n, k, dtype, nullptr);
+}
+
+extern "C" gemv_status_t gemv_check_args_ex(const void* B, const void* a, const void* c,
+                                            int64_t n, int64_t k, gemv_dtype_t dtype,
+                                            const gemv_epilogue_t* ep) {
   if (dtype != GEMV_F16 && dtype != GEMV_BF16) return GEMV_ERR_UNSUPPORTED_DTYPE;
   if (n < 0 || k < 0) return GEMV_ERR_INVALID_ARG;
   if (n == 0) return GEMV_OK;
@@ -249,6 +255,12 @@ extern "C" gemv_status_t gemv_check_args(const void* B, const void* a, const voi
     const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)n * (uintptr_t)k * 2u;
     const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)k * 2u;
     if ((c0 < b1 && b0 < c1) || (c0 < a1 && a0 < c1)) return GEMV_ERR_ALIASING;
+  }
+  if (ep && ep->bias) {
+    const uintptr_t z0 = (uintptr_t)ep->bias, z1 = z0 + (uintptr_t)n * 2u;
+    if (z0 & 1u) return GEMV_ERR_MISALIGNED;
+    // bias may be c itself (accumulate in place), but must not partly overlap it
+    if (z0 != c0 && z0 < c1 && c0 < z1) return GEMV_ERR_ALIASING;
   }
   return GEMV_OK;
 }
@@ -420,8 +432,14 @@ extern "C" gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k
 
 extern "C" gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a, void* c,
                                   int64_t n, int64_t k, gemv_dtype_t dtype, hipStream_t stream) {
+  return gemv_run_ex(h, B, a, c, n, k, dtype, nullptr, stream);
+}
+
+extern "C" gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void* a, void* c,
+                                     int64_t n, int64_t k, gemv_dtype_t dtype,
+                                     const gemv_epilogue_t* ep, hipStream_t stream) {
   if (!h || h->magic != kMagic) return report(nullptr, GEMV_ERR_NULL_HANDLE, "gemv_run");
-  gemv_status_t s = gemv_check_args(B, a, c, n, k, dtype);
+  gemv_status_t s = gemv_check_args_ex(B, a, c, n, k, dtype, ep);
   if (s != GEMV_OK) return report(h, s, "gemv_run arguments");
   if (n == 0) return GEMV_OK;
   int dev = -1;
@@ -437,9 +455,11 @@ extern "C" gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a,
   int ni = (int)n, ki = (int)k;
   float* ws = h->ws;
   unsigned* cnt = h->cnt;
-  int flags = L.flags;
-  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp, (void*)&ni, (void*)&ki, (void*)&ws, (void*)&cnt,
-                  (void*)&flags};
+  int flags = L.flags | (ep ? mbd::kFlagEpilogue : 0);
+  float alpha = ep ? ep->alpha : 1.0f;
+  const uint16_t* bias = ep ? (const uint16_t*)ep->bias : nullptr;
+  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp,    (void*)&ni,    (void*)&ki,
+                  (void*)&ws, (void*)&cnt, (void*)&flags, (void*)&alpha, (void*)&bias};
   hipError_t e = hipLaunchKernel((const void*)var.fn[dtype], dim3((unsigned)L.grid, (unsigned)L.kgroups),
                                  dim3((unsigned)(var.info.waves * mbd::kLanes)), args, L.lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));

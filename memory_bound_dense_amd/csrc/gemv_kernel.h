@@ -111,6 +111,9 @@ __device__ __forceinline__ void fma8(const u32x4& b, const u32x4& a, float& acc0
 // [start(x), start(x) + count(x)) with count(x) = G/8 (+1 for x < G % 8).
 constexpr int kXcds = 8;
 constexpr int kFlagXcdContiguous = 1;
+// The fused epilogue (page "Optimizing TileLang Programs", epilogue fusion):
+// c = alpha * sum + bias, one fp32 FMA on the row sum before the store.
+constexpr int kFlagEpilogue = 2;
 
 __device__ __forceinline__ int64_t xcd_unit(int64_t b, int64_t G) {
   const int64_t x = b % kXcds, i = b / kXcds;
@@ -145,10 +148,29 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
   }
 }
 
+template <int DT>
+__device__ __forceinline__ float widen(uint16_t x) {
+  if constexpr (DT == DT_F16) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  } else {
+    return __builtin_bit_cast(float, (uint32_t)x << 16);
+  }
+}
+
+// The value stored for a row: the sum itself, or alpha * sum (+ bias[row]).
+// bias may be c itself: a row's bias is read by the lane that then writes it.
+template <int DT>
+__device__ __forceinline__ float finish(float s, int flags, float alpha,
+                                        const uint16_t* __restrict__ bias, int64_t row) {
+  if (!(flags & kFlagEpilogue)) return s;
+  return bias ? __builtin_fmaf(alpha, s, widen<DT>(bias[row])) : alpha * s;
+}
+
 template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL, bool XWG>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
-    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
-    int n, int k, float* __restrict__ ws, unsigned* __restrict__ cnt, int flags) {
+    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* c,
+    int n, int k, float* __restrict__ ws, unsigned* __restrict__ cnt, int flags, float alpha,
+    const uint16_t* bias) {
   static_assert(WAVES % S == 0, "splits must divide the waves of a workgroup");
   static_assert(!XWG || AMODE == A_CACHED, "a k-chunk per workgroup does not stage all of a");
   constexpr int G = WAVES / S;   // row groups per workgroup
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
         __hip_atomic_store(&ws[(int64_t)q * n + row0 + lane], mine, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       } else {
-        c[row0 + lane] = to_bits<DT>(mine);
+        c[row0 + lane] = to_bits<DT>(finish<DT>(mine, flags, alpha, bias, row0 + lane));
       }
     }
   }
@@ -326,7 +348,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
         for (int qq = lane; qq < Q; qq += kLanes)
           s += __hip_atomic_load(&ws[(int64_t)qq * n + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s = wave_sum(s);
-        if (lane == 0) c[r] = to_bits<DT>(s);
+        if (lane == 0) c[r] = to_bits<DT>(finish<DT>(s, flags, alpha, bias, r));
       }
       if (threadIdx.x == 0)   // ready for the next call
         __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -356,8 +378,9 @@ __device__ __forceinline__ uint32_t keep_mask(int j0, int k) {
 
 template <int DT, int U, int WAVES, int BPOL>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
-    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
-    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/, int flags) {
+    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* c,
+    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/, int flags,
+    float alpha, const uint16_t* bias) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & (kLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -456,7 +479,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
     for (; t < nsteps; ++t) masked_step(t);
 
     const float tot = wave_sum(acc0 + acc1);
-    if (lane == 0) c[row] = to_bits<DT>(tot);
+    if (lane == 0) c[row] = to_bits<DT>(finish<DT>(tot, flags, alpha, bias, row));
   }
 }
 
@@ -469,8 +492,9 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
 // automatic plan.
 template <int DT, int WAVES>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_rowlane_kernel(
-    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* __restrict__ c,
-    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/, int /*flags*/) {
+    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* c,
+    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/, int flags,
+    float alpha, const uint16_t* bias) {
   const int lane = threadIdx.x & (kLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a, (uint32_t)k * 2u);
@@ -496,7 +520,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_rowlane_kernel(
       }
       acc = __builtin_fmaf(bf, af, acc);
     }
-    if (lane < nrows) c[row0 + lane] = to_bits<DT>(acc);
+    if (lane < nrows) c[row0 + lane] = to_bits<DT>(finish<DT>(acc, flags, alpha, bias, row0 + lane));
   }
 }
 

@@ -117,3 +117,19 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         _lib.load()
+
+
+@pytest.mark.parametrize("bias,expect", [
+    (None, _lib.GEMV_OK),
+    (1 << 38, _lib.GEMV_OK),
+    ((1 << 38) + 1, _lib.GEMV_ERR_MISALIGNED),
+    (C0, _lib.GEMV_OK),                      # bias == c: accumulate in place
+    (C0 + 2, _lib.GEMV_ERR_ALIASING),        # partial overlap with c
+    (C0 - 6, _lib.GEMV_ERR_ALIASING),
+    (C0 - 8, _lib.GEMV_OK),                  # ends where c starts (n = 4)
+])
+def test_check_args_epilogue(bias, expect):
+    assert mbd.gemv_check_args_ex(B0, A0, C0, 4, 8, 0, 0.5, bias) == expect
+    # the plain checks still come first
+    assert mbd.gemv_check_args_ex(B0 + 1, A0, C0, 4, 8, 0, 0.5, bias) == _lib.GEMV_ERR_MISALIGNED
+    assert mbd.gemv_check_args_ex(B0, A0, C0, 4, 8, 0) == _lib.GEMV_OK

@@ -395,3 +395,78 @@ def test_auto_plan_realigns_misaligned_rows(g):
         v, grid, q = g.query_config(n, k, BF16)
         info = mbd.gemv_variant_info(v)[1]
         assert info.a_mode == (2 if k % 8 else 1), (n, k, v)
+
+
+def run_ex(g, Bd, ad, alpha, bias, variant=-1, c=None):
+    n, k = Bd.shape
+    dtype = mbd.GEMV_F16 if Bd.dtype == torch.float16 else mbd.GEMV_BF16
+    if not fits(g, variant, n, k, dtype):
+        return None
+    if c is None:
+        c = torch.full((n,), float("nan"), dtype=Bd.dtype, device=Bd.device)
+    g.force_config(variant)
+    try:
+        if n > 0:
+            LAST_EXTRA[0] = _extra_adds(g, n, k, dtype)
+        g(Bd, ad, c, alpha=alpha, bias=bias)
+    finally:
+        g.force_config(-1)
+    torch.cuda.synchronize()
+    return to_bits(c)
+
+
+EPI_SHAPES = [(300, 4096, F16), (129, 1537, BF16), (64, 65536, BF16), (37, 7169, F16)]
+
+
+@pytest.mark.parametrize("n,k,dtype", EPI_SHAPES,
+                         ids=["%dx%d_%s" % (n, k, "f16" if d == F16 else "bf16")
+                              for n, k, d in EPI_SHAPES])
+def test_epilogue_every_variant(g, n, k, dtype):
+    """c = alpha * (B @ a) + bias against the oracle: every variant, with and
+    without bias; the bound adds |alpha| to the fp32 sum term and one fp32
+    rounding of the FMA."""
+    B, a = random_inputs(n, k, dtype, seed=41)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    rng = np.random.default_rng(5)
+    bias_bits = values_to_bits(rng.normal(size=n).astype(np.float32), dtype)
+    biasd = to_device(bias_bits, dtype)
+    for alpha in (1.0, -0.5, 0.1):
+        for with_bias in (False, True):
+            ref, y, ab = oracle.gemv_epilogue(dtype, B, a, alpha, bias_bits if with_bias else None)
+            a32 = abs(float(np.float32(alpha)))
+            for v in [-1] + VARIANTS:
+                got = run_ex(g, Bd, ad, alpha, biasd if with_bias else None, v)
+                if got is None:
+                    continue
+                gv, rv = oracle.decode(dtype, got), oracle.decode(dtype, ref)
+                from parity import ulp
+                u = ulp(dtype, np.maximum(np.abs(gv), np.abs(rv)))
+                strict = u + 2.0 ** -24 * ((np.ceil(k / 64) + 8 + LAST_EXTRA[0]) * a32 * ab
+                                           + np.abs(y))
+                grade = 4e-3 * a32 * ab + ulp(dtype, rv)
+                d = np.abs(gv - rv)
+                assert np.all(d <= grade), (alpha, with_bias, v)
+                assert np.all(d <= strict), (alpha, with_bias, v, float((d / strict).max()))
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
+def test_epilogue_integer_exact_and_in_place(g, dtype):
+    """Integer B, a, bias and a power-of-two alpha: every variant bit-exact;
+    bias == c accumulates in place."""
+    n, k = 200, 3000
+    B, a = integer_inputs(n, k, dtype, seed=43)
+    rng = np.random.default_rng(7)
+    bias_bits = values_to_bits(rng.integers(-30, 31, size=n).astype(np.float32), dtype)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    for alpha in (2.0, -0.25):
+        ref, _, _ = oracle.gemv_epilogue(dtype, B, a, alpha, bias_bits)
+        for v in [-1] + VARIANTS:
+            biasd = to_device(bias_bits, dtype)
+            got = run_ex(g, Bd, ad, alpha, biasd, v)
+            if got is None:
+                continue
+            assert np.array_equal(got, ref), (alpha, v)
+            # in place: c starts as the bias
+            c = to_device(bias_bits, dtype)
+            got = run_ex(g, Bd, ad, alpha, c, v, c=c)
+            assert np.array_equal(got, ref), ("in place", alpha, v)
