@@ -101,3 +101,27 @@ def shape_workload(spec):
 def algorithmic_bytes(n: int, k: int, elem_bytes: int = 2) -> int:
     """Bytes a GEMV must move at least once: B, a and c."""
     return elem_bytes * (n * k + k + n)
+
+
+# ---- one GLA decode step (TileLang Case Studies, Case D; decode shape of
+# Case G: batch 1, 32 heads, DK = DV = 128) ----------------------------------
+#
+# Recipe: q, k ~ N(0,1)/sqrt(DK); v ~ N(0,1); gk = logsigmoid(N(0,1)) (log
+# decays, <= 0); S ~ N(0,1) in float32; drawn in that order from one seeded
+# generator, q/k/v/gk cast to the 16-bit dtype.
+
+def gla_inputs(bh: int, dk: int, dv: int, dtype: int, seed: int = 0):
+    """Return (q, k, v, gk) uint16 patterns and S float32 (bh, dk, dv)."""
+    g = torch.Generator().manual_seed(seed)
+    s = 1.0 / math.sqrt(dk) if dk > 0 else 1.0
+    q = torch.randn(bh, dk, generator=g) * s
+    k = torch.randn(bh, dk, generator=g) * s
+    v = torch.randn(bh, dv, generator=g)
+    gk = torch.nn.functional.logsigmoid(torch.randn(bh, dk, generator=g))
+    S = torch.randn(bh, dk, dv, generator=g, dtype=torch.float32)
+    return (_to_bits(q, dtype), _to_bits(k, dtype), _to_bits(v, dtype), _to_bits(gk, dtype),
+            S.numpy())
+
+
+GLA_DECODE = ("gla_decode_b1h32_128x128_bf16", 32, 128, 128, BF16)
+GLA_BATCHED = ("gla_decode_b64h32_128x128_bf16", 64 * 32, 128, 128, BF16)

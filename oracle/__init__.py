@@ -28,8 +28,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB) or (
-            os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+    if not os.path.exists(_build.LIB) or any(
+            os.path.getmtime(_build.LIB) < os.path.getmtime(src) for src in _build.SRCS):
         _build.build()
     lib = ctypes.CDLL(_build.LIB)
     u16p = ctypes.POINTER(ctypes.c_uint16)
@@ -48,6 +48,11 @@ def _load():
     lib.oracle_gemv_epilogue.argtypes = [ctypes.c_int, u16p, u16p, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_float, u16p, u16p, dp, dp, dp]
     lib.oracle_gemv_epilogue.restype = ctypes.c_int
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_gla_decode.argtypes = [ctypes.c_int, u16p, u16p, u16p, u16p, fp, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_float, fp, u16p,
+                                      dp, dp, dp]
+    lib.oracle_gla_decode.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -136,3 +141,35 @@ def gemv_epilogue(dtype: int, B, a, alpha: float, bias=None):
     if rc != 0:
         raise ValueError("oracle.gemv_epilogue: bad argument")
     return c, y, ab
+
+
+def gla_decode(dtype: int, q, k, v, gk, S, scale: float):
+    """One GLA decode step (TileLang Case Studies, Case D):
+    S_new = diag(exp(gk)) S + outer(k, v), o = scale * q^T S_new, per head.
+
+    q, k, gk: (BH, DK) uint16 patterns; v: (BH, DV) patterns; S: (BH, DK, DV)
+    float32.  Returns (S_new float32, o uint16 patterns (BH, DV), S_new before
+    rounding (float64), o before rounding (float64), |scale| sum_i |q_i S_new|)."""
+    import numpy as np
+    q, k, v, gk = (np.ascontiguousarray(x, dtype=np.uint16) for x in (q, k, v, gk))
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    bh, dk, dv = S.shape
+    if q.shape != (bh, dk) or k.shape != (bh, dk) or gk.shape != (bh, dk) or v.shape != (bh, dv):
+        raise ValueError("oracle.gla_decode: shapes do not match S %s" % (S.shape,))
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    fp = ctypes.POINTER(ctypes.c_float)
+    dp = ctypes.POINTER(ctypes.c_double)
+    Sn = np.empty_like(S)
+    o = np.empty((bh, dv), dtype=np.uint16)
+    s64 = np.empty(S.shape, dtype=np.float64)
+    o64 = np.empty((bh, dv), dtype=np.float64)
+    oabs = np.empty((bh, dv), dtype=np.float64)
+    rc = _load().oracle_gla_decode(dtype, q.ctypes.data_as(u16p), k.ctypes.data_as(u16p),
+                                   v.ctypes.data_as(u16p), gk.ctypes.data_as(u16p),
+                                   S.ctypes.data_as(fp), bh, dk, dv, float(np.float32(scale)),
+                                   Sn.ctypes.data_as(fp), o.ctypes.data_as(u16p),
+                                   s64.ctypes.data_as(dp), o64.ctypes.data_as(dp),
+                                   oabs.ctypes.data_as(dp))
+    if rc != 0:
+        raise ValueError("oracle.gla_decode: bad argument")
+    return Sn, o, s64, o64, oabs

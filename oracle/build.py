@@ -1,6 +1,6 @@
 """Build the CPU oracle shared library (test infrastructure only).
 
-Compiles ``oracle/gemv_ref.c`` with the host C compiler into
+Compiles ``oracle/gemv_ref.c`` and ``oracle/gla_ref.c`` with the host C compiler into
 ``oracle/libgemv_ref.so``.  Plain ``-O2`` with IEEE semantics kept
 (``-fno-fast-math``, no FMA contraction), single-threaded code.
 """
@@ -10,6 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gemv_ref.c")
+SRCS = [SRC, os.path.join(HERE, "gla_ref.c")]
 LIB = os.path.join(HERE, "libgemv_ref.so")
 
 
@@ -17,7 +18,7 @@ def build(verbose: bool = False) -> str:
     cc = os.environ.get("CC", "gcc")
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [cc, "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-Wall",
-           "-Wextra", "-shared", "-fPIC", SRC, "-o", tmp, "-lm"]
+           "-Wextra", "-shared", "-fPIC"] + SRCS + ["-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
