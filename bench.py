@@ -135,6 +135,70 @@ def stream_probe(nbytes, steps, dev):
             "grid": best[1], "xcd_contiguous": best[2]}
 
 
+def gla_bench(args):
+    """One GLA decode step per step (include/gla_decode.h), the state updated
+    in place as a decode loop does; copies of the state rotate over > 1 GiB."""
+    import numpy as np
+    import torch
+    import memory_bound_dense_amd as mbd
+    from gemv_inputs import DTYPE_NAMES, GLA_BATCHED, GLA_DECODE, gla_inputs, torch_dtype
+    wl = {w[0]: w for w in (GLA_DECODE, GLA_BATCHED)}.get(args.workload, GLA_DECODE)
+    name, bh, dk, dv, dtype = wl
+    dev = torch.device("cuda", 0)
+    td = torch_dtype(dtype)
+    q, k, v, gk, S = gla_inputs(bh, dk, dv, dtype, seed=0)
+    t = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(td)
+    qd, kd, vd, gd = t(q), t(k), t(v), t(gk)
+    S0 = torch.from_numpy(S).to(dev)
+    state_bytes = 4 * bh * dk * dv
+    nbuf = int(min(64, max(2, math.ceil((1 << 30) / state_bytes))))
+    Ss = [S0] + [S0.clone() for _ in range(nbuf - 1)]
+    os_ = [torch.empty((bh, dv), dtype=td, device=dev) for _ in range(nbuf)]
+    step_bytes = 2 * state_bytes + 2 * bh * (3 * dk + 2 * dv)
+    g = mbd.Gemv()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    scale = 1.0 / math.sqrt(dk)
+    P = [(Ss[i].data_ptr(), os_[i].data_ptr()) for i in range(nbuf)]
+
+    def step(i):
+        s_, o_ = P[i % nbuf]
+        rc = mbd.gla_decode_step(g.h, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), gd.data_ptr(),
+                                 s_, s_, o_, bh, dk, dv, scale, dtype, sp)
+        if rc != 0:
+            raise mbd.GemvError(rc, "gla_decode_step")
+
+    for i in range(args.warmup):
+        step(i)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    value = step_bytes / (wall / args.steps) / 1e9
+    log("[bench] %s: wall %.2f us/step, kernel avg %.2f us -> %.1f GB/s" % (
+        name, wall / args.steps * 1e6, avg_us, step_bytes / avg_us / 1e3))
+    out = {"metric": "GLA decode step: achieved HBM GB/s and us/call", "value": round(value, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAMES[dtype],
+           "data": "synthetic",
+           "config": {"workload": name, "bh": bh, "dk": dk, "dv": dv, "in_place": True,
+                      "rotating_buffers": nbuf},
+           "us_per_call": round(wall / args.steps * 1e6, 3), "kernel_us_avg": round(avg_us, 3),
+           "roofline": {"bound": "hbm", "achieved": round(step_bytes / avg_us / 1e3, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(step_bytes / avg_us / 1e3 / HBM_PEAK_GBS, 4),
+                        "traffic": None}}
+    g.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +213,8 @@ def main():
                     help="force the k-groups of a cross-workgroup variant (0 = auto)")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=("gemv", "gla"), default="gemv",
+                    help="gemv (default, the headline) or gla: one GLA decode step")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the streaming-read probe (the practical read ceiling)")
     args = ap.parse_args()
@@ -160,6 +226,11 @@ def main():
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: one process, one GPU; WORLD_SIZE > 1 is not supported", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "gla":
+        if args.workload == "gemv_18432x7168_f16":
+            args.workload = "gla_decode_b1h32_128x128_bf16"
+        return gla_bench(args)
 
     import numpy as np
     import torch

@@ -34,10 +34,10 @@ GEMV_FLAG_XCD_CONTIGUOUS = 1
 GEMV_MAX_N = 1073741824
 GEMV_MAX_K = 134217728
 
-# every symbol include/gemv.h declares
+# every symbol include/gemv.h and include/gla_decode.h declare
 EXPORTS = ("gemv_create", "gemv_run", "gemv_run_ex", "gemv_destroy", "gemv_status_string",
            "gemv_check_args", "gemv_check_args_ex", "gemv_num_variants", "gemv_variant_info",
-           "gemv_force_config", "gemv_query_config")
+           "gemv_force_config", "gemv_query_config", "gla_decode_step", "gla_check_args")
 
 
 class GemvError(RuntimeError):
@@ -100,6 +100,11 @@ def load():
     lib.gemv_force_config.restype = st
     lib.gemv_query_config.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.POINTER(gemv_config_t)]
     lib.gemv_query_config.restype = st
+    lib.gla_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
+                                    ctypes.c_int, vp]
+    lib.gla_decode_step.restype = st
+    lib.gla_check_args.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int]
+    lib.gla_check_args.restype = st
     _lib = lib
     return lib
 
@@ -164,6 +169,15 @@ def gemv_query_config(h, n, k, dtype):
     cfg = gemv_config_t()
     s = load().gemv_query_config(h, n, k, dtype, ctypes.byref(cfg))
     return s, cfg
+
+
+def gla_decode_step(h, q, k, v, gk, S_in, S_out, o, bh, dk, dv, scale, dtype, stream=None):
+    """One GLA decode step (include/gla_decode.h); all pointers are addresses."""
+    return load().gla_decode_step(h, q, k, v, gk, S_in, S_out, o, bh, dk, dv, scale, dtype, stream)
+
+
+def gla_check_args(q, k, v, gk, S_in, S_out, o, bh, dk, dv, dtype):
+    return load().gla_check_args(q, k, v, gk, S_in, S_out, o, bh, dk, dv, dtype)
 
 
 # ---- torch-tensor convenience ------------------------------------------------
@@ -240,3 +254,34 @@ class Gemv:
         if s != GEMV_OK:
             raise GemvError(s, "gemv_run")
         return c
+
+
+class GlaDecode:
+    """One GLA decode step on torch tensors, through a Gemv handle:
+    S_out = diag(exp(gk)) S_in + outer(k, v); o = scale * q^T S_out, per head.
+    q, k, gk: (bh, dk); v: (bh, dv); S_in, S_out: float32 (bh, dk, dv), S_out may
+    be S_in; o: (bh, dv) of q's dtype."""
+
+    def __init__(self, gemv=None):
+        self.g = gemv if gemv is not None else Gemv()
+
+    def __call__(self, q, k, v, gk, S_in, S_out, o, scale, stream=None):
+        import torch
+        bh, dk = q.shape
+        dv = v.shape[1]
+        for t, shape in ((k, (bh, dk)), (gk, (bh, dk)), (v, (bh, dv)), (o, (bh, dv)),
+                         (S_in, (bh, dk, dv)), (S_out, (bh, dk, dv))):
+            if tuple(t.shape) != shape or not t.is_contiguous():
+                raise GemvError(GEMV_ERR_INVALID_ARG, "shape/contiguity of a GLA argument")
+        dt = _dtype_code(q)
+        if any(t.dtype != q.dtype for t in (k, v, gk, o)) or S_in.dtype != torch.float32 or \
+                S_out.dtype != torch.float32:
+            raise GemvError(GEMV_ERR_UNSUPPORTED_DTYPE, "q, k, v, gk, o share a 16-bit dtype; S is float32")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        s = gla_decode_step(self.g.h, q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(),
+                            S_in.data_ptr(), S_out.data_ptr(), o.data_ptr(), bh, dk, dv,
+                            float(scale), dt, stream)
+        if s != GEMV_OK:
+            raise GemvError(s, "gla_decode_step")
+        return o

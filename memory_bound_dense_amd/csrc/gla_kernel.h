@@ -1,0 +1,112 @@
+// One decode step of gated linear attention for gfx950 (TileLang Case
+// Studies, Case D "Background"), per (batch, head):
+//
+//     S_new = diag(exp(gk)) S + outer(k, v)        S: DK x DV, float32
+//     o     = scale * q^T S_new                    o: DV, 16-bit dtype
+//
+// Like the GEMV this is bound by HBM: the state is read once and written once
+// (8 bytes per element) and everything else is a few KiB.  The pages' kernel
+// (Case D) streams state tiles through shared memory with TMA pipelines in
+// two passes; here one pass does both: every lane owns 4 consecutive state
+// columns of a column block and walks the rows of the head, so each state
+// element is loaded once (16-byte buffer load), updated in registers, stored
+// once (16-byte buffer store) and folded into its column's partial of o in
+// the same step.  There is no second pass over the state and no shared tile
+// to race on.  The row groups' partials of o are summed through LDS in a
+// fixed order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemv_kernel.h"
+
+namespace mbd {
+
+constexpr int kGlaThreads = 256;
+
+// LPR lanes per row, 4 columns each: a column block of 4*LPR columns and
+// kGlaThreads/LPR row groups.  Workgroup b handles head b / nblk and column
+// block b % nblk.  S_out may equal S_in (each 16 bytes are read, then written,
+// by one lane).
+template <int DT, int LPR>
+__global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ gk, const float* S_in,
+    float* S_out, uint16_t* __restrict__ o, int dk, int dv, float scale, int nblk) {
+  constexpr int CW = 4 * LPR;                 // columns per block
+  constexpr int RG = kGlaThreads / LPR;       // row groups
+  __shared__ float part[RG][CW];
+
+  const int t = threadIdx.x;
+  const int c4 = t % LPR;
+  const int rg = t / LPR;
+  const int64_t head = blockIdx.x / nblk;
+  const int blk = blockIdx.x - (int)(head * nblk);
+  const int j0 = blk * CW + c4 * 4;           // first column of this lane
+  const bool active = j0 < dv;                // dv % 4 == 0: a lane's 4 columns are all in or all out
+
+  const int64_t rowbase = head * dk;          // row index of the head's first state row
+  const __amdgpu_buffer_rsrc_t sin_r =
+      make_rsrc(S_in + rowbase * dv, (uint32_t)dk * (uint32_t)dv * 4u);
+  const __amdgpu_buffer_rsrc_t sout_r =
+      make_rsrc(S_out + rowbase * dv, (uint32_t)dk * (uint32_t)dv * 4u);
+
+  float vj[4] = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vj[c] = widen<DT>(v[head * dv + j0 + c]);
+  }
+  float oacc[4] = {0.f, 0.f, 0.f, 0.f};
+
+  // Four rows per trip: their loads are issued together (a lane only ever
+  // rewrites the 16 bytes it has just read, so this is safe in place too).
+  constexpr int kRows = 4;
+  if (active) {
+    for (int i0 = rg; i0 < dk; i0 += kRows * RG) {
+      u32x4 sv[kRows];
+      float e[kRows], ki[kRows], qi[kRows];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const int i = i0 + r * RG;
+        if (i < dk) {
+          sv[r] = __builtin_amdgcn_raw_buffer_load_b128(
+              sin_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, 0);
+          e[r] = expf(widen<DT>(gk[rowbase + i]));
+          ki[r] = widen<DT>(k[rowbase + i]);
+          qi[r] = widen<DT>(q[rowbase + i]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const int i = i0 + r * RG;
+        if (i < dk) {
+          u32x4 nv;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t w = sv[r][c];
+            const float sn = __builtin_fmaf(ki[r], vj[c], e[r] * __builtin_bit_cast(float, w));
+            nv[c] = __builtin_bit_cast(uint32_t, sn);
+            oacc[c] = __builtin_fmaf(qi[r], sn, oacc[c]);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(
+              nv, sout_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, 0);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < 4; ++c) part[rg][c4 * 4 + c] = oacc[c];
+  __syncthreads();
+  if (t < CW) {
+    const int j = blk * CW + t;
+    if (j < dv) {
+      float s = 0.0f;
+      for (int r = 0; r < RG; ++r) s += part[r][t];
+      o[head * dv + j] = to_bits<DT>(scale * s);
+    }
+  }
+}
+
+}  // namespace mbd

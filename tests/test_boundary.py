@@ -11,13 +11,17 @@ import memory_bound_dense_amd as mbd
 from memory_bound_dense_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gemv.h")
+HEADERS = [os.path.join(ROOT, "include", "gemv.h"), os.path.join(ROOT, "include", "gla_decode.h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemv_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for hdr in HEADERS:
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**((?:gemv|gla)_\w+)\s*\(", text,
+                                flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_exports():
@@ -133,3 +137,35 @@ def test_check_args_epilogue(bias, expect):
     # the plain checks still come first
     assert mbd.gemv_check_args_ex(B0 + 1, A0, C0, 4, 8, 0, 0.5, bias) == _lib.GEMV_ERR_MISALIGNED
     assert mbd.gemv_check_args_ex(B0, A0, C0, 4, 8, 0) == _lib.GEMV_OK
+
+
+
+# GLA decode step: fake, well-separated addresses (16-byte aligned state)
+Q0, K0, V0, G0, S0, S1, O0 = (1 << 40) + 0, (1 << 40) + (1 << 30), (1 << 40) + (2 << 30), \
+    (1 << 40) + (3 << 30), 1 << 41, (1 << 41) + (1 << 34), 1 << 42
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((Q0, K0, V0, G0, S0, S1, O0, 32, 128, 128, 1), _lib.GEMV_OK),
+    ((Q0, K0, V0, G0, S0, S0, O0, 32, 128, 128, 1), _lib.GEMV_OK),         # in place
+    ((Q0, K0, V0, G0, S0, S0 + 16, O0, 32, 128, 128, 1), _lib.GEMV_ERR_ALIASING),
+    ((Q0, K0, V0, G0, S0, S1, S1 + 64, 32, 128, 128, 1), _lib.GEMV_ERR_ALIASING),   # o in the state
+    ((Q0, K0, V0, G0, S0, S1, Q0 + 2, 32, 128, 128, 1), _lib.GEMV_ERR_ALIASING),    # o over q
+    ((Q0, K0, V0, G0, S0, S1, O0, 32, 128, 126, 1), _lib.GEMV_ERR_INVALID_ARG),    # dv % 4
+    ((Q0, K0, V0, G0, S0 + 8, S1, O0, 32, 128, 128, 1), _lib.GEMV_ERR_MISALIGNED),
+    ((Q0 + 1, K0, V0, G0, S0, S1, O0, 32, 128, 128, 1), _lib.GEMV_ERR_MISALIGNED),
+    ((Q0, K0, V0, G0, S0, S1, O0, 32, 128, 128, 2), _lib.GEMV_ERR_UNSUPPORTED_DTYPE),
+    ((Q0, K0, V0, G0, S0, S1, O0, -1, 128, 128, 1), _lib.GEMV_ERR_INVALID_ARG),
+    ((0, 0, 0, 0, 0, 0, 0, 0, 128, 128, 1), _lib.GEMV_OK),                  # bh == 0: no-op
+    ((0, 0, 0, 0, 0, 0, O0, 32, 0, 128, 1), _lib.GEMV_OK),                  # dk == 0: only o
+    ((0, K0, V0, G0, S0, S1, O0, 32, 128, 128, 1), _lib.GEMV_ERR_INVALID_ARG),
+    ((Q0, K0, V0, G0, S0, S1, O0, 32, 65537, 4, 1), _lib.GEMV_ERR_TOO_LARGE),
+    ((Q0, K0, V0, G0, S0, S1, O0, 32, 32768, 16384, 1), _lib.GEMV_ERR_TOO_LARGE),
+])
+def test_gla_check_args(args, expect):
+    assert mbd.gla_check_args(*args) == expect
+
+
+def test_gla_null_handle():
+    assert mbd.gla_decode_step(None, Q0, K0, V0, G0, S0, S1, O0, 1, 4, 4, 1.0, 0) == \
+        _lib.GEMV_ERR_NULL_HANDLE
