@@ -183,6 +183,32 @@ def gla_bench(args):
     value = step_bytes / (wall / args.steps) / 1e9
     log("[bench] %s: wall %.2f us/step, kernel avg %.2f us -> %.1f GB/s" % (
         name, wall / args.steps * 1e6, avg_us, step_bytes / avg_us / 1e3))
+    # the practical ceiling for this traffic mix: a plain copy of the state
+    ceiling = None
+    if not args.no_probe:
+        from memory_bound_dense_amd import probe
+        nbytes = state_bytes // probe.CHUNK * probe.CHUNK
+        if nbytes:
+            dst = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+            best = None
+            for grid in (0, 512, 2048):
+                for i in range(5):
+                    probe.stream_copy(Ss[i % nbuf].data_ptr(), dst[i % nbuf].data_ptr(), nbytes, grid,
+                                      True, sp)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for i in range(args.steps):
+                    probe.stream_copy(Ss[i % nbuf].data_ptr(), dst[i % nbuf].data_ptr(), nbytes, grid,
+                                      True, sp)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / args.steps
+                best = us if best is None else min(best, us)
+            ceiling = {"bytes_moved": 2 * nbytes, "us": round(best, 3),
+                       "gbs": round(2 * nbytes / best / 1e3, 1)}
+            log("[bench] streaming copy of the state: %.2f us -> %.1f GB/s" % (best, ceiling["gbs"]))
+            del dst
     out = {"metric": "GLA decode step: achieved HBM GB/s and us/call", "value": round(value, 2),
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
@@ -195,6 +221,8 @@ def gla_bench(args):
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(step_bytes / avg_us / 1e3 / HBM_PEAK_GBS, 4),
                         "traffic": None}}
+    if ceiling:
+        out["stream_copy_probe"] = ceiling
     g.close()
     print(json.dumps(out), flush=True)
 

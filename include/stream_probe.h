@@ -32,6 +32,14 @@ extern "C" {
 int mbd_stream_read(const void* src, size_t bytes, uint32_t* out, int out_len, int grid,
                     int nontemporal, int xcd_contiguous, hipStream_t stream, int* launched);
 
+/* Copy `bytes` bytes from src to dst (both 16-byte aligned, not
+ * overlapping; bytes a non-zero multiple of 16 KiB) with 16-byte loads and
+ * stores: the read + write counterpart of mbd_stream_read.  `grid` as there
+ * (0 = one trip per workgroup).  Returns 0, -1 on a bad argument, -2 if the
+ * launch failed. */
+int mbd_stream_copy(const void* src, void* dst, size_t bytes, int grid, int nontemporal,
+                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -520,14 +520,19 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return report(h, GEMV_ERR_HIP, "hipGetDevice");
   if (dev != h->device) return report(h, GEMV_ERR_WRONG_DEVICE, "gla_decode_step");
-  // widest column block (32 lanes x 4 columns) that still gives >= 2 workgroups per CU
+  // The widest column block (8, 16 or 32 lanes x 4 columns) that still gives
+  // >= 16 workgroups per CU; state loads and stores non-temporal (measured on
+  // MI355X: ~13% faster than the default policy; 2048 heads of 128 x 128 run
+  // at ~90% of a plain copy of the same bytes).
   static const GlaFn fns[2][3] = {
-      {&mbd::gla_decode_kernel<mbd::DT_F16, 8>, &mbd::gla_decode_kernel<mbd::DT_F16, 16>,
-       &mbd::gla_decode_kernel<mbd::DT_F16, 32>},
-      {&mbd::gla_decode_kernel<mbd::DT_BF16, 8>, &mbd::gla_decode_kernel<mbd::DT_BF16, 16>,
-       &mbd::gla_decode_kernel<mbd::DT_BF16, 32>}};
+      {&mbd::gla_decode_kernel<mbd::DT_F16, 8, 4, kPolNT, kPolNT>,
+       &mbd::gla_decode_kernel<mbd::DT_F16, 16, 4, kPolNT, kPolNT>,
+       &mbd::gla_decode_kernel<mbd::DT_F16, 32, 4, kPolNT, kPolNT>},
+      {&mbd::gla_decode_kernel<mbd::DT_BF16, 8, 4, kPolNT, kPolNT>,
+       &mbd::gla_decode_kernel<mbd::DT_BF16, 16, 4, kPolNT, kPolNT>,
+       &mbd::gla_decode_kernel<mbd::DT_BF16, 32, 4, kPolNT, kPolNT>}};
   int sel = 0;
-  const int64_t want = 2 * (int64_t)h->num_cus;
+  const int64_t want = 16 * (int64_t)h->num_cus;
   for (int c = 2; c >= 0; --c) {
     const int64_t cw = 4 * (8 << c);
     if (bh * ((dv + cw - 1) / cw) >= want || c == 0) { sel = c; break; }

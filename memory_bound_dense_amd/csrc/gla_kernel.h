@@ -29,7 +29,7 @@ constexpr int kGlaThreads = 256;
 // kGlaThreads/LPR row groups.  Workgroup b handles head b / nblk and column
 // block b % nblk.  S_out may equal S_in (each 16 bytes are read, then written,
 // by one lane).
-template <int DT, int LPR>
+template <int DT, int LPR, int ROWS = 4, int LPOL = 0, int SPOL = 0>
 __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ gk, const float* S_in,
@@ -59,9 +59,10 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
   }
   float oacc[4] = {0.f, 0.f, 0.f, 0.f};
 
-  // Four rows per trip: their loads are issued together (a lane only ever
+  // ROWS rows per trip: their loads are issued together (a lane only ever
   // rewrites the 16 bytes it has just read, so this is safe in place too).
-  constexpr int kRows = 4;
+  // LPOL / SPOL: cache-policy bits of the state loads / stores.
+  constexpr int kRows = ROWS;
   if (active) {
     for (int i0 = rg; i0 < dk; i0 += kRows * RG) {
       u32x4 sv[kRows];
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
         const int i = i0 + r * RG;
         if (i < dk) {
           sv[r] = __builtin_amdgcn_raw_buffer_load_b128(
-              sin_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, 0);
+              sin_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, LPOL);
           e[r] = expf(widen<DT>(gk[rowbase + i]));
           ki[r] = widen<DT>(k[rowbase + i]);
           qi[r] = widen<DT>(q[rowbase + i]);
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
             oacc[c] = __builtin_fmaf(qi[r], sn, oacc[c]);
           }
           __builtin_amdgcn_raw_buffer_store_b128(
-              nv, sout_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, 0);
+              nv, sout_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, SPOL);
         }
       }
     }

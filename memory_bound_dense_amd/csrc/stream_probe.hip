@@ -59,7 +59,50 @@ __global__ __launch_bounds__(kThreads) void stream_read(const uint8_t* __restric
   }
 }
 
+// Streaming copy: the same chunk walk, each 16-byte vector read and written
+// once (read + write traffic, the mix of a state update).
+template <int POL>
+__global__ __launch_bounds__(kThreads) void stream_copy(const uint8_t* __restrict__ src,
+                                                        uint8_t* __restrict__ dst, uint64_t nvec) {
+  const uint64_t per = (uint64_t)kThreads * kUnroll;
+  const uint64_t nchunks = nvec / per;
+  for (uint64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+    const uint64_t base = ch * per;
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(src + base * 16u), (short)0, kThreads * kUnroll * 16, kRsrcWord3);
+    __amdgpu_buffer_rsrc_t w = __builtin_amdgcn_make_buffer_rsrc(
+        dst + base * 16u, (short)0, kThreads * kUnroll * 16, kRsrcWord3);
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, ((uint32_t)u * kThreads + threadIdx.x) * 16u, 0u, POL);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(v[u], w, ((uint32_t)u * kThreads + threadIdx.x) * 16u, 0u, POL);
+  }
+}
+
 }  // namespace
+
+extern "C" int mbd_stream_copy(const void* src, void* dst, size_t bytes, int grid, int nontemporal,
+                               hipStream_t stream) {
+  if (!src || !dst || bytes == 0 || (bytes % (kThreads * kUnroll * 16)) != 0 ||
+      (((uintptr_t)src | (uintptr_t)dst) % 16) != 0 || grid < 0)
+    return -1;
+  const uint8_t* s8 = (const uint8_t*)src;
+  uint8_t* d8 = (uint8_t*)dst;
+  if (s8 < d8 + bytes && d8 < s8 + bytes) return -1;
+  const uint64_t nvec = bytes / 16;
+  const uint64_t per_wg = (uint64_t)kThreads * kUnroll;
+  uint64_t g = grid > 0 ? (uint64_t)grid : nvec / per_wg;
+  if (g > (1u << 20)) g = 1u << 20;
+  if (g < 1) g = 1;
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_copy<2>, dim3((unsigned)g), dim3(kThreads), 0, stream, s8, d8, nvec);
+  else
+    hipLaunchKernelGGL(stream_copy<0>, dim3((unsigned)g), dim3(kThreads), 0, stream, s8, d8, nvec);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
 
 extern "C" int mbd_stream_read(const void* src, size_t bytes, uint32_t* out, int out_len, int grid,
                                int nontemporal, int xcd, hipStream_t stream, int* launched) {

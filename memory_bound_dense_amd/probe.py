@@ -22,6 +22,9 @@ def load():
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
         lib.mbd_stream_read.restype = ctypes.c_int
+        lib.mbd_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.mbd_stream_copy.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -35,3 +38,10 @@ def stream_read(src_ptr, nbytes, out_ptr, out_len, grid=0, nontemporal=True, str
     if rc != 0:
         raise RuntimeError("mbd_stream_read failed (%d)" % rc)
     return launched.value
+
+
+def stream_copy(src_ptr, dst_ptr, nbytes, grid=0, nontemporal=True, stream=None):
+    """Enqueue one streaming copy of nbytes (a multiple of CHUNK)."""
+    rc = load().mbd_stream_copy(src_ptr, dst_ptr, nbytes, grid, int(bool(nontemporal)), stream)
+    if rc != 0:
+        raise RuntimeError("mbd_stream_copy failed (%d)" % rc)
