@@ -369,7 +369,9 @@ def main():
                    "variant": variant, "grid": grid, "kgroups": kgroups,
                    "rows_per_wave": vinfo.rows,
                    "unroll": vinfo.unroll, "waves_per_wg": vinfo.waves, "splits": vinfo.splits,
-                   "a_mode": ["lds", "cached"][vinfo.a_mode], "rotating_buffers": nbuf},
+                   "a_mode": {0: "lds", 1: "cached", 2: "lds_shifted"}[vinfo.a_mode],
+                   "layout": ["lanes_along_k", "row_per_lane"][vinfo.layout],
+                   "rotating_buffers": nbuf},
         "us_per_call": round(ms_per_step * 1e3, 3),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernel_us_avg": round(avg_us, 3),

@@ -14,8 +14,7 @@
 
 namespace {
 
-using KernelFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, int, int, float*,
-                          unsigned*, int, float, const uint16_t*);
+using KernelFn = void (*)(mbd::GemvArgs);
 
 struct Variant {
   gemv_variant_info_t info;
@@ -451,17 +450,30 @@ extern "C" gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void*
   s = resolve(h, n, k, ((uintptr_t)B & 15u) == 0, &L);
   if (s != GEMV_OK) return report(h, s, "no variant fits (LDS or workspace)");
   const Variant& var = kVariants[L.variant];
-  const uint16_t* Bp = (const uint16_t*)B;
-  const uint16_t* ap = (const uint16_t*)a;
-  uint16_t* cp = (uint16_t*)c;
-  int ni = (int)n, ki = (int)k;
-  float* ws = h->ws;
-  unsigned* cnt = h->cnt;
-  int flags = L.flags | (ep ? mbd::kFlagEpilogue : 0);
-  float alpha = ep ? ep->alpha : 1.0f;
-  const uint16_t* bias = ep ? (const uint16_t*)ep->bias : nullptr;
-  void* args[] = {(void*)&Bp, (void*)&ap, (void*)&cp,    (void*)&ni,    (void*)&ki,
-                  (void*)&ws, (void*)&cnt, (void*)&flags, (void*)&alpha, (void*)&bias};
+  const gemv_variant_info_t& vi = var.info;
+  mbd::GemvArgs p;
+  p.B = (const uint16_t*)B;
+  p.a = (const uint16_t*)a;
+  p.c = (uint16_t*)c;
+  p.bias = ep ? (const uint16_t*)ep->bias : nullptr;
+  p.ws = h->ws;
+  p.cnt = h->cnt;
+  p.n = (int)n;
+  p.k = (int)k;
+  p.flags = L.flags | (ep ? mbd::kFlagEpilogue : 0);
+  p.alpha = ep ? ep->alpha : 1.0f;
+  // balanced shares: rows over the row units, full k-steps over the k-slices
+  int64_t units;
+  if (vi.a_mode == mbd::A_LDS_SHIFTED) units = (int64_t)L.grid * vi.waves;      // a wave per unit
+  else if (vi.splits == 1 && !vi.cross_wg) units = (int64_t)L.grid * (vi.waves / vi.splits);
+  else units = L.grid;                                                          // a workgroup per unit
+  p.rows_q = (int)(n / units);
+  p.rows_r = (int)(n % units);
+  const int64_t nfull = k / mbd::kStep;
+  const int64_t nsl = (int64_t)vi.splits * L.kgroups;
+  p.slice_q = (int)(nfull / nsl);
+  p.slice_r = (int)(nfull % nsl);
+  void* args[] = {(void*)&p};
   hipError_t e = hipLaunchKernel((const void*)var.fn[dtype], dim3((unsigned)L.grid, (unsigned)L.kgroups),
                                  dim3((unsigned)(var.info.waves * mbd::kLanes)), args, L.lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));

@@ -166,11 +166,39 @@ __device__ __forceinline__ float finish(float s, int flags, float alpha,
   return bias ? __builtin_fmaf(alpha, s, widen<DT>(bias[row])) : alpha * s;
 }
 
+// Everything a GEMV kernel needs, passed by value (the kernel-argument
+// segment is read with scalar loads).  Rows and k-steps are dealt in balanced
+// shares worked out on the host, so a wave finds its range with a multiply
+// and a min instead of a 64-bit division: share u of U starts at
+// u*q + min(u, r) and holds q + (u < r) items, where q = N / U, r = N % U.
+struct GemvArgs {
+  const uint16_t* B;
+  const uint16_t* a;
+  uint16_t* c;
+  const uint16_t* bias;   // fused epilogue (flags & kFlagEpilogue), may be null
+  float* ws;              // cross-workgroup partials
+  unsigned* cnt;          // cross-workgroup arrival counters
+  int n, k, flags;
+  float alpha;
+  int rows_q, rows_r;     // rows per row unit (per wave, or per workgroup)
+  int slice_q, slice_r;   // full 512-element steps per k-slice
+};
+
+__device__ __forceinline__ int share_start(int64_t u, int q, int r) {
+  return (int)(u * q + (u < r ? u : (int64_t)r));
+}
+
 template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL, bool XWG>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
-    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* c,
-    int n, int k, float* __restrict__ ws, unsigned* __restrict__ cnt, int flags, float alpha,
-    const uint16_t* bias) {
+    const GemvArgs p) {
+  const uint16_t* __restrict__ B = p.B;
+  const uint16_t* __restrict__ a = p.a;
+  uint16_t* c = p.c;
+  const int n = p.n, k = p.k, flags = p.flags;
+  const float alpha = p.alpha;
+  const uint16_t* bias = p.bias;
+  float* __restrict__ ws = p.ws;
+  unsigned* __restrict__ cnt = p.cnt;
   static_assert(WAVES % S == 0, "splits must divide the waves of a workgroup");
   static_assert(!XWG || AMODE == A_CACHED, "a k-chunk per workgroup does not stage all of a");
   constexpr int G = WAVES / S;   // row groups per workgroup
@@ -204,8 +232,9 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
   const int q = XWG ? (int)blockIdx.y : 0;
   const int gsl = q * S + sl;
   const int nsl = Q * S;
-  const int t0 = (int)(((int64_t)nfull * gsl) / nsl);
-  const int t1 = (int)(((int64_t)nfull * (gsl + 1)) / nsl);
+  const int t0 = share_start(gsl, p.slice_q, p.slice_r);
+  const int t1 = t0 + p.slice_q + (gsl < p.slice_r ? 1 : 0);
+  (void)nsl;
   const bool tail = (rem != 0) && (gsl == nsl - 1);
   const int lane_off = lane * 16;
 
@@ -217,10 +246,9 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
   // combine works on a workgroup's whole range).
   constexpr bool kWaveRanges = S == 1 && !XWG;
   const int64_t wg = (flags & kFlagXcdContiguous) ? xcd_unit(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int64_t units = kWaveRanges ? (int64_t)gridDim.x * G : (int64_t)gridDim.x;
   const int64_t unit = kWaveRanges ? wg * G + rg : wg;
-  const int lo = (int)((unit * n) / units);
-  const int hi = (int)(((unit + 1) * n) / units);
+  const int lo = share_start(unit, p.rows_q, p.rows_r);
+  const int hi = lo + p.rows_q + (unit < p.rows_r ? 1 : 0);
   constexpr int kTrip = kWaveRanges ? R : RB;
   const int goff = kWaveRanges ? 0 : rg * R;
 
@@ -378,9 +406,13 @@ __device__ __forceinline__ uint32_t keep_mask(int j0, int k) {
 
 template <int DT, int U, int WAVES, int BPOL>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
-    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* c,
-    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/, int flags,
-    float alpha, const uint16_t* bias) {
+    const GemvArgs p) {
+  const uint16_t* __restrict__ B = p.B;
+  const uint16_t* __restrict__ a = p.a;
+  uint16_t* c = p.c;
+  const int k = p.k, flags = p.flags;
+  const float alpha = p.alpha;
+  const uint16_t* bias = p.bias;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & (kLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -423,10 +455,9 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
   }
 
   const int64_t wg = (flags & kFlagXcdContiguous) ? xcd_unit(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int64_t units = (int64_t)gridDim.x * WAVES;
   const int64_t unit = wg * WAVES + wave;
-  const int lo = (int)((unit * n) / units);
-  const int hi = (int)(((unit + 1) * n) / units);
+  const int lo = share_start(unit, p.rows_q, p.rows_r);
+  const int hi = lo + p.rows_q + (unit < p.rows_r ? 1 : 0);
 
   for (int row = lo; row < hi; ++row) {
     const uint16_t* rowp = B + (int64_t)row * k;
@@ -492,9 +523,13 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
 // automatic plan.
 template <int DT, int WAVES>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_rowlane_kernel(
-    const uint16_t* __restrict__ B, const uint16_t* __restrict__ a, uint16_t* c,
-    int n, int k, float* __restrict__ /*ws*/, unsigned* __restrict__ /*cnt*/, int flags,
-    float alpha, const uint16_t* bias) {
+    const GemvArgs p) {
+  const uint16_t* __restrict__ B = p.B;
+  const uint16_t* __restrict__ a = p.a;
+  uint16_t* c = p.c;
+  const int n = p.n, k = p.k, flags = p.flags;
+  const float alpha = p.alpha;
+  const uint16_t* bias = p.bias;
   const int lane = threadIdx.x & (kLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a, (uint32_t)k * 2u);
