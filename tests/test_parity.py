@@ -470,3 +470,38 @@ def test_epilogue_integer_exact_and_in_place(g, dtype):
             c = to_device(bias_bits, dtype)
             got = run_ex(g, Bd, ad, alpha, c, v, c=c)
             assert np.array_equal(got, ref), ("in place", alpha, v)
+
+
+def test_random_shapes(g):
+    """Seeded random (n, k, dtype), base pointers shifted by 0..7 elements,
+    the automatic plan and three random variants (random grid) per shape,
+    one with the epilogue: against the full oracle."""
+    rng = np.random.default_rng(123)
+    for case in range(40):
+        n = int(np.exp(rng.uniform(0, np.log(4000))))
+        k = int(np.exp(rng.uniform(0, np.log(30000))))
+        if n * k > 12_000_000:
+            k = max(1, 12_000_000 // n)
+        dtype = F16 if rng.random() < 0.5 else BF16
+        shift = int(rng.integers(0, 8))
+        B, a = random_inputs(n, k, dtype, seed=1000 + case)
+        ref, _, ab = oracle.gemv(dtype, B, a)
+        Bbig = to_device(np.concatenate([np.zeros(shift, np.uint16), B.ravel()]), dtype)
+        Bd = Bbig[shift:].view(n, k)
+        ad = to_device(a, dtype)
+        picks = [-1] + [int(x) for x in rng.choice(VARIANTS, size=3, replace=False)]
+        for v in picks:
+            grid = 0 if v < 0 else int(rng.choice([0, 1, 7, 300]))
+            got = run(g, Bd, ad, v, grid)
+            if got is None:
+                continue
+            _check(dtype, got, ref, ab, k, v, "random case %d (%d x %d, shift %d, grid %d)"
+                   % (case, n, k, shift, grid))
+        alpha = float(rng.choice([0.5, -1.0, 3.0]))
+        bias = values_to_bits(rng.normal(size=n).astype(np.float32), dtype)
+        ref_e, y, ab_e = oracle.gemv_epilogue(dtype, B, a, alpha, bias)
+        got = run_ex(g, Bd, ad, alpha, to_device(bias, dtype))
+        gv, rv = oracle.decode(dtype, got), oracle.decode(dtype, ref_e)
+        from parity import ulp
+        bound = 4e-3 * abs(alpha) * ab_e + ulp(dtype, rv)
+        assert np.all(np.abs(gv - rv) <= bound), ("epilogue", case, n, k)
