@@ -99,3 +99,46 @@ def test_two_streams_two_handles_repeatable():
             assert np.array_equal(to_bits(outs2[i]), ref[i]), (it, SHAPES[i])
     g1.close()
     g2.close()
+
+
+def test_stress_split_and_lds_variants_repeatable():
+    """Variants with synchronisation inside (LDS staging, in-workgroup splits,
+    cross-workgroup splits, realigned rows): 150 back-to-back runs each with
+    random host delays and eager work between them must all give the bits
+    of the first run."""
+    g = mbd.Gemv()
+    rng = random.Random(7)
+    picks = []
+    for v in range(mbd.gemv_num_variants()):
+        info = mbd.gemv_variant_info(v)[1]
+        if info.layout == 0 and (info.a_mode != 1 or info.splits > 1 or info.cross_wg):
+            picks.append(v)
+    shapes = [(64, 65536, BF16), (1000, 7001, F16), (300, 4096, BF16)]
+    for i, (n, k, dtype) in enumerate(shapes):
+        B, a = random_inputs(n, k, dtype, seed=200 + i)
+        Bd, ad = to_device(B, dtype), to_device(a, dtype)
+        for v in rng.sample(picks, 6):
+            g.force_config(v)
+            try:
+                g.query_config(n, k, dtype)
+            except mbd.GemvError:
+                g.force_config(-1)
+                continue
+            c = torch.empty(n, dtype=Bd.dtype, device="cuda")
+            g(Bd, ad, c)
+            torch.cuda.synchronize()
+            first = to_bits(c)
+            for it in range(150):
+                if rng.random() < 0.2:
+                    time.sleep(rng.random() * 2e-4)
+                if rng.random() < 0.2:
+                    torch.randn(1 << 16, device="cuda").sum()
+                c.fill_(float("nan"))
+                g(Bd, ad, c)
+                if rng.random() < 0.5:
+                    torch.cuda.synchronize()
+                    assert np.array_equal(to_bits(c), first), (n, k, v, it)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(c), first), (n, k, v)
+            g.force_config(-1)
+    g.close()
