@@ -96,8 +96,8 @@ size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
   return b;
 }
 
+// Rows a workgroup covers per trip (layout 1: rows == 64, one per lane).
 int64_t rows_per_block(const gemv_variant_info_t& v) { return (int64_t)(v.waves / v.splits) * v.rows; }
-// (for layout 1, rows == 64: one row per lane)
 
 // Device workspace of a handle: fp32 partial sums (kgroups x n) and one
 // arrival counter per row range, for the cross-workgroup variants.
@@ -134,29 +134,30 @@ int find_variant(const Plan& p) {
   return -1;
 }
 
-// The general rule, for shapes without a measured entry:
-//  * rows whose start is not 16-byte aligned (k % 8 != 0): one row per wave
-//    and a staged in LDS, which keeps the texture path free for the
-//    unaligned B loads;
-//  * otherwise a through the caches and non-temporal B loads; two rows per
-//    wave when both n and k are large;
-//  * k is split inside a workgroup while every wave still streams at least
-//    8 KiB of B, and further (down to two 512-element steps per slice) while
-//    the grid has fewer than 4096 waves.
+// The general rule, for shapes without a measured entry, in this order:
+//  1. rows that do not start on 16-byte boundaries (k % 8 != 0, or B itself
+//     misaligned): the realigning kernel -- aligned granules of B, a staged
+//     twice in LDS -- on a persistent grid, when its LDS fits;
+//  2. too few rows to give the GPU 4096 waves even with 16 waves per row:
+//     k split across workgroups as well (cross-workgroup variants);
+//  3. misaligned rows whose realigning LDS does not fit: unaligned 16-byte
+//     loads with a staged in LDS (or through the caches if that does not fit
+//     either);
+//  4. otherwise a through the caches and non-temporal B loads, two rows per
+//     wave when both n and k are large, and k split inside a workgroup while
+//     every wave still streams at least 8 KiB of B, further (down to two
+//     512-element steps per slice) while the grid has fewer than 4096 waves.
 Plan rule_plan(int64_t n, int64_t k, size_t max_lds, bool b_aligned) {
   const int64_t nfull0 = k / mbd::kStep;
-  // Rows that do not start on 16-byte boundaries: aligned granules of B and a
-  // realigned through LDS (persistent grid: a is staged once per workgroup).
-  // As fast as unaligned 16-byte loads on MI355X and needs no unaligned
-  // access at all.
+  // 1. (persistent grid: a is staged once per workgroup; as fast as unaligned
+  // 16-byte loads on MI355X and needs no unaligned access at all)
   if (k > 0 && (k % 8 != 0 || !b_aligned)) {
     Plan p = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
     if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
   }
-  // Too few rows to give the GPU 4096 waves even with 16 waves per row:
-  // split k across workgroups too (8 waves per row per workgroup, Q groups,
-  // about 2048 waves in all -- more k-groups cost more than they bring on
-  // MI355X), keeping at least two 512-element steps per wave.
+  // 2. 8 waves per row per workgroup, Q groups, about 2048 waves in all (more
+  // k-groups cost more than they bring on MI355X), keeping at least two
+  // 512-element steps per wave.
   if (n * 16 < 4096 && nfull0 >= 2 * 8 * 2) {
     int64_t Q = (2048 + n * 8 - 1) / (n * 8);
     const int64_t qmax = nfull0 / (2 * 8);
@@ -164,11 +165,13 @@ Plan rule_plan(int64_t n, int64_t k, size_t max_lds, bool b_aligned) {
     if (Q > 64) Q = 64;
     if (Q * n <= (int64_t)kWsFloats && Q > 1) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
-  if (k % 8 != 0) {
+  // 3.
+  if (k % 8 != 0 || !b_aligned) {
     Plan p = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 0, 1};
     if (lds_bytes(kVariants[find_variant(p)].info, k) > max_lds) p.a_mode = mbd::A_CACHED;
     return p;
   }
+  // 4.
   const int64_t nfull = k / mbd::kStep;
   const int R = (n >= 4096 && k >= 6144) ? 2 : 1;
   const int64_t row_bytes = 2 * k * R;

@@ -5,13 +5,14 @@
 // enough 16-byte loads of B in flight on every CU and to do nothing else
 // expensive.  No matrix cores: this is not a contraction worth tiling.
 //
-// Mapping (the lanes-along-k layout that TileLang Case Studies, Case B, shows
-// is the one that coalesces; here sized for 64-lane wavefronts):
+// gemv_kernel -- the lanes-along-k layout that TileLang Case Studies, Case B,
+// shows is the one that coalesces, sized for 64-lane wavefronts:
 //   * a workgroup has WAVES wavefronts, arranged as G = WAVES/S row groups
 //     times S k-slices;
-//   * a row group owns R consecutive rows; the wave streams those R rows, and
-//     lane l of the wave reads elements [8*(64*t + l), +8) of each row at step
-//     t -- one 16-byte load per lane, 1 KiB contiguous per row per wave;
+//   * rows are dealt in balanced contiguous ranges (per wave, or per
+//     workgroup when S > 1 or XWG); a wave walks its range R rows at a time,
+//     and lane l reads elements [8*(64*t + l), +8) of each of those rows at
+//     step t -- one 16-byte load per lane, 1 KiB contiguous per row per wave;
 //   * U steps are unrolled, so a wave keeps R*U KiB of B in flight;
 //   * a is either staged once per workgroup in LDS (A_LDS; Case B.2 is the
 //     shared-memory variant of this choice) or read with the same 16-byte
@@ -23,14 +24,20 @@
 //   * with XWG, Q = gridDim.y workgroups also share a row range along k:
 //     each writes its fp32 row partials to a workspace, and the workgroup
 //     that arrives last (a device-scope counter per row range) sums the Q
-//     partials in a fixed order and writes c.
+//     partials in a fixed order and writes c;
+//   * an optional fused epilogue (alpha, bias) is one FMA before the store.
+// gemv_realign_kernel -- rows that do not start on 16-byte boundaries: B in
+// aligned granules, a realigned through two shifted LDS copies.
+// gemv_rowlane_kernel -- the uncoalesced layout (one row per lane), for
+// measurement only.
 //
 // Loads go through buffer resources: the row base is a wave-uniform 64-bit
-// address in SGPRs, the per-row offset is an SGPR soffset and the lane offset
-// a single VGPR shared by all rows, and the range check of the descriptor
-// bounds every access to the rows the wave owns.  Rows are only 2-byte
-// aligned when k is not a multiple of 8; the 16-byte loads then rely on the
-// unaligned buffer access that ROCm enables for compute queues.
+// address in SGPRs, the per-row offset an SGPR soffset and the lane offset a
+// single VGPR shared by all rows.  Every offset is in bounds by construction;
+// the descriptor's range (the wave's rows) is a second fence.  In
+// gemv_kernel, rows are only 2-byte aligned when k is not a multiple of 8;
+// its 16-byte loads then rely on the unaligned buffer access that ROCm
+// enables for compute queues (the realigning kernel needs none).
 #pragma once
 
 #include <hip/hip_runtime.h>
