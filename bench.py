@@ -23,7 +23,6 @@ Algorithmic bytes per step = 2 * (n*k + k + n): B, a and c once each.
 Prints ONE JSON line on stdout; human-readable detail goes to stderr.
 """
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -36,8 +35,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "achieved HBM GB/s (% of MI355X peak) and µs/call, n=18432 k=7168 fp16"
-KERNEL_SOURCES = [os.path.join(ROOT, "memory_bound_dense_amd", "csrc", "gemv_kernel.h"),
-                  os.path.join(ROOT, "memory_bound_dense_amd", "csrc", "gemv.hip")]
 
 
 def log(*a):
@@ -45,11 +42,8 @@ def log(*a):
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from memory_bound_dense_amd.profile_counters import kernel_source_hash as ksh
+    return ksh()
 
 
 def read_traffic(workload, n_launch_bytes):

@@ -36,11 +36,21 @@ GEMV_KERNEL = "gemv_kernel"
 COPY_KERNEL = "copyBuffer"
 
 
+def _strip_comments(text):
+    """C/C++ source without comments and with whitespace collapsed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
+    """Hash of the GEMV sources (kernels, variant table, plan rule), blind to
+    comments and whitespace: a summary taken on other code is not reused."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 
