@@ -142,8 +142,9 @@ const char* gemv_status_string(gemv_status_t s);
  * with 16-byte loads along k, `unroll` 512-element steps per loop trip.
  * a_mode 0: a is staged once per workgroup in LDS; 1: a is read through the
  * cache hierarchy with the same 16-byte loads; 2: for rows that do not start
- * on a 16-byte boundary, B is read in aligned 16-byte granules and a is
- * staged in LDS twice (shifted by 0 and 1 element) to line up with them.
+ * on a 16-byte boundary, B is read in aligned 16-byte granules starting at
+ * the 128-byte line that holds each row's first element, and a is staged in
+ * LDS twice (shifted by 0 and 1 element) to line up with them.
  * splits > 1 sums the k-slices of a row group in a fixed order through LDS
  * (deterministic). */
 typedef struct {

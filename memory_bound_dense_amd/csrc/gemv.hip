@@ -31,10 +31,11 @@ constexpr int kLanesPerWave = 64;
    {&mbd::gemv_kernel<mbd::DT_F16, R, U, W, S, AM, POL, X>,                         \
     &mbd::gemv_kernel<mbd::DT_BF16, R, U, W, S, AM, POL, X>}}
 #define MBD_VARIANT(R, U, W, S, AM, POL) MBD_VARIANT_X(R, U, W, S, AM, POL, false)
-#define MBD_REALIGN(U, W, POL)                                                      \
-  {{1, U, W, 1, mbd::A_LDS_SHIFTED, POL, 0, 0},                                     \
-   {&mbd::gemv_realign_kernel<mbd::DT_F16, U, W, POL>,                              \
-    &mbd::gemv_realign_kernel<mbd::DT_BF16, U, W, POL>}}
+#define MBD_REALIGN_R(R, U, W, POL)                                                 \
+  {{R, U, W, 1, mbd::A_LDS_SHIFTED, POL, 0, 0},                                     \
+   {&mbd::gemv_realign_kernel<mbd::DT_F16, R, U, W, POL>,                           \
+    &mbd::gemv_realign_kernel<mbd::DT_BF16, R, U, W, POL>}}
+#define MBD_REALIGN(U, W, POL) MBD_REALIGN_R(1, U, W, POL)
 
 // The compiled variants: (rows R, unroll U, waves W, splits S, a mode, B
 // cache policy).  Row variants (S == 1) give each wave R whole rows; split
@@ -73,11 +74,15 @@ const Variant kVariants[] = {
     MBD_VARIANT_X(1, 4, 8, 8, CCH, NT, true), MBD_VARIANT_X(1, 2, 8, 8, CCH, NT, true),
     MBD_VARIANT_X(1, 4, 4, 4, CCH, NT, true), MBD_VARIANT_X(1, 2, 4, 4, CCH, NT, true),
     MBD_VARIANT_X(2, 4, 8, 4, CCH, NT, true), MBD_VARIANT_X(1, 4, 4, 1, CCH, NT, true),
-    // 48..51: rows not 16-byte aligned: aligned B granules, a realigned in LDS
+    // 48..51: rows not 16-byte aligned: line-aligned B granules, a realigned in LDS
     MBD_REALIGN(4, 4, NT), MBD_REALIGN(2, 4, NT), MBD_REALIGN(4, 8, NT), MBD_REALIGN(8, 4, NT),
     // 52: one row per lane, one element per step (the uncoalesced layout; study only)
     {{kLanesPerWave, 1, 4, 1, mbd::A_CACHED, 0, 0, 1},
      {&mbd::gemv_rowlane_kernel<mbd::DT_F16, 4>, &mbd::gemv_rowlane_kernel<mbd::DT_BF16, 4>}},
+    // 53..57: more realigning shapes (two rows per trip in 54..56)
+    MBD_REALIGN(8, 8, NT), MBD_REALIGN_R(2, 4, 4, NT), MBD_REALIGN_R(2, 4, 8, NT),
+    MBD_REALIGN_R(2, 2, 8, NT),
+    MBD_REALIGN(2, 8, NT),
 };
 #undef NT
 #undef LDS
@@ -87,7 +92,9 @@ constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
   const int64_t nsteps = (k + mbd::kStep - 1) / mbd::kStep;
   if (v.a_mode == mbd::A_LDS_SHIFTED) {   // two shifted, zero-padded copies of a
-    const int64_t len = mbd::kPadA + (k + 7 + mbd::kStep - 1) / mbd::kStep * mbd::kStep + 8;
+    const int64_t steps =
+        ((k + mbd::kLine - 1 + mbd::kStep - 1) / mbd::kStep + v.unroll - 1) / v.unroll * v.unroll;
+    const int64_t len = mbd::kPadA + steps * mbd::kStep + 8;
     return (size_t)(4 * len);
   }
   size_t b = 0;

@@ -394,24 +394,29 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
 // ---------------------------------------------------------------------------
 // Rows that do not start on a 16-byte boundary (k % 8 != 0, or B itself not
 // 16-byte aligned).  Instead of unaligned 16-byte loads, B is read in aligned
-// 16-byte granules and a is shifted to match: vector v of row i covers row
-// elements [8v - o, 8v - o + 8), o = the row's offset in elements from the
-// granule boundary (0..7), so it needs a[8v - o .. 8v - o + 7].  LDS holds a
-// twice, shifted by 0 and by 1 element behind kPadA zero elements, which makes
-// that window start on a 4-byte boundary for either parity of o (two
-// ds_read2_b32).  The first and last vectors of a row are masked element by
-// element, so nothing from a neighbouring row (a NaN or inf included) enters
-// the sum.  A granule that holds at least one byte of B never crosses a page
-// boundary, so the aligned reads past a row's ends stay in mapped memory.
-// One row per wave, rows dealt to waves in balanced contiguous ranges.
-constexpr int kPadA = 8;
+// 16-byte granules from the 128-byte cache line that holds the row's first
+// element, and a is shifted to match: vector v of row i covers row elements
+// [8v - o, 8v - o + 8), o = the row's offset in elements from that line
+// (0..63), so it needs a[8v - o .. 8v - o + 7].  With line-aligned windows a
+// wave's 1 KiB load covers exactly 8 lines, so no line is fetched by two
+// loads (16-byte windows straddle 9 lines and refetch the shared one).  LDS
+// holds a twice, shifted by 0 and by 1 element behind kPadA zero elements,
+// which makes that window start on a 4-byte boundary for either parity of o
+// (two ds_read2_b32).  The first and last vectors of a row are masked element
+// by element, so nothing from a neighbouring row (a NaN or inf included)
+// enters the sum.  A 128-byte line that holds at least one byte of B never
+// crosses a page boundary, so the aligned reads past a row's ends stay in
+// mapped memory.  Rows are dealt to waves in balanced contiguous ranges, R
+// rows per trip.
+constexpr int kLine = 64;               // elements per 128-byte line
+constexpr int kPadA = kLine;
 
 __device__ __forceinline__ uint32_t keep_mask(int j0, int k) {
   // element j0 in the low half, j0 + 1 in the high half; keep those in [0, k)
   return ((j0 >= 0 && j0 < k) ? 0x0000ffffu : 0u) | ((j0 + 1 >= 0 && j0 + 1 < k) ? 0xffff0000u : 0u);
 }
 
-template <int DT, int U, int WAVES, int BPOL>
+template <int DT, int R, int U, int WAVES, int BPOL>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
     const GemvArgs p) {
   const uint16_t* __restrict__ B = p.B;
@@ -425,7 +430,9 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // copy 0: a_0[kPadA + x] = a[x]; copy 1: a_1[kPadA + x] = a[x - 1]; zeros elsewhere
-  const int nsteps_max = (k + 7 + kStep - 1) / kStep;
+  // whole groups of U steps are read (masked beyond the row), so the copies
+  // cover ceil(steps / U) * U steps
+  const int nsteps_max = ((k + kLine - 1 + kStep - 1) / kStep + U - 1) / U * U;
   const int len = kPadA + nsteps_max * kStep + 8;        // elements per copy, a multiple of 8
   uint32_t* a0w = reinterpret_cast<uint32_t*>(smem);      // len / 2 dwords each
   uint32_t* a1w = a0w + len / 2;
@@ -466,58 +473,85 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
   const int lo = share_start(unit, p.rows_q, p.rows_r);
   const int hi = lo + p.rows_q + (unit < p.rows_r ? 1 : 0);
 
-  for (int row = lo; row < hi; ++row) {
-    const uint16_t* rowp = B + (int64_t)row * k;
-    const int o = (int)(((uintptr_t)rowp >> 1) & 7u);   // wave-uniform
-    const int nv = (o + k + kVec - 1) / kVec;            // granules touching the row
-    const __amdgpu_buffer_rsrc_t brsrc = make_rsrc(rowp - o, (uint32_t)nv * 16u);
-    const uint32_t* aw = (o & 1) ? a1w : a0w;
-    // dword of the a copy that lines up with element 0 of granule v: (8v - o + (o & 1) + kPadA) / 2
-    const int abase = (kPadA - o + (o & 1)) >> 1;
-    const int nsteps = (nv + kLanes - 1) / kLanes;
-    const int tmid = ((k + o) / kVec) / kLanes;          // steps [1, tmid) need no masks
-    float acc0 = 0.0f, acc1 = 0.0f;
-
-    auto masked_step = [&](int t) {
-      const int v = t * kLanes + lane;
-      u32x4 bv = {0u, 0u, 0u, 0u};
-      if (v < nv) bv = __builtin_amdgcn_raw_buffer_load_b128(brsrc, v * 16, 0u, BPOL);
-      const int j0 = v * kVec - o;                       // row element of the granule's first half-word
+  // R rows per trip (their loads issued together); a second row past the
+  // range end repeats the first and is not stored.
+  for (int row0 = lo; row0 < hi; row0 += R) {
+    const uint16_t* basep[R];       // 16-byte aligned start of each row's granules
+    const uint32_t* aw[R];          // the a copy that matches the row's offset
+    int o[R], nv[R], abase[R], tmid[R];
+    int nsteps = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = bv[i];
-        bv[i] = w & keep_mask(j0 + 2 * i, k);
-      }
-      const int d = abase + v * 4;
-      u32x4 av = {aw[d], aw[d + 1], aw[d + 2], aw[d + 3]};
-      fma8<DT>(bv, av, acc0, acc1);
-    };
-
-    masked_step(0);
-    int t = 1;
-    for (; t + U <= tmid; t += U) {
-      u32x4 bv[U], av[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        bv[u] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, ((t + u) * kLanes + lane) * 16, 0u, BPOL);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int d = abase + ((t + u) * kLanes + lane) * 4;
-        av[u][0] = aw[d]; av[u][1] = aw[d + 1]; av[u][2] = aw[d + 2]; av[u][3] = aw[d + 3];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) fma8<DT>(bv[u], av[u], acc0, acc1);
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + r < hi ? row0 + r : row0;
+      const uint16_t* rowp = B + (int64_t)row * k;
+      o[r] = (int)(((uintptr_t)rowp >> 1) & (kLine - 1));  // wave-uniform
+      nv[r] = (o[r] + k + kVec - 1) / kVec;                // granules touching the row
+      basep[r] = rowp - o[r];                              // 128-byte aligned
+      aw[r] = (o[r] & 1) ? a1w : a0w;
+      // dword of the a copy lined up with element 0 of granule v: (8v - o + (o & 1) + kPadA) / 2
+      abase[r] = (kPadA - o[r] + (o[r] & 1)) >> 1;
+      tmid[r] = ((k + o[r]) / kVec) / kLanes;              // steps [1, tmid) need no masks
+      const int ns = (nv[r] + kLanes - 1) / kLanes;
+      nsteps = ns > nsteps ? ns : nsteps;
     }
-    for (; t < tmid; ++t) {
-      const u32x4 bv = __builtin_amdgcn_raw_buffer_load_b128(brsrc, (t * kLanes + lane) * 16, 0u, BPOL);
-      const int d = abase + (t * kLanes + lane) * 4;
-      u32x4 av = {aw[d], aw[d + 1], aw[d + 2], aw[d + 3]};
-      fma8<DT>(bv, av, acc0, acc1);
-    }
-    for (; t < nsteps; ++t) masked_step(t);
+    float acc[R][2];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.0f;
 
-    const float tot = wave_sum(acc0 + acc1);
-    if (lane == 0) c[row] = to_bits<DT>(finish<DT>(tot, flags, alpha, bias, row));
+    // The steps in groups of U, all loads of a group issued together.  A row's
+    // group is "clean" when every granule in it lies inside the row; the
+    // others (the row's first granules when o != 0, its last full granules
+    // and beyond) are masked after the load.  Granules at or past nv lie
+    // outside the descriptor's range: the hardware returns them without a
+    // memory access, and the mask clears them whatever they hold.
+    for (int t = 0; t < nsteps; t += U) {
+      u32x4 bv[R][U], av[R][U];
+      bool clean[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        clean[r] = (t > 0 || o[r] == 0) && (t + U <= tmid[r]);
+        const __amdgpu_buffer_rsrc_t brsrc = make_rsrc(basep[r], (uint32_t)nv[r] * 16u);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          bv[r][u] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, ((t + u) * kLanes + lane) * 16, 0u,
+                                                           BPOL);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int d = abase[r] + ((t + u) * kLanes + lane) * 4;
+          av[r][u][0] = aw[r][d]; av[r][u][1] = aw[r][d + 1];
+          av[r][u][2] = aw[r][d + 2]; av[r][u][3] = aw[r][d + 3];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (!clean[r]) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int j0 = ((t + u) * kLanes + lane) * kVec - o[r];   // row element of the granule start
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t w = bv[r][u][i];
+              bv[r][u][i] = w & keep_mask(j0 + 2 * i, k);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) fma8<DT>(bv[r][u], av[r][u], acc[r][0], acc[r][1]);
+      }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float tot = wave_sum(acc[r][0] + acc[r][1]);
+      const int row = row0 + r;
+      if (lane == 0 && row < hi) c[row] = to_bits<DT>(finish<DT>(tot, flags, alpha, bias, row));
+    }
   }
 }
 

@@ -4,8 +4,9 @@ rocprofv3's CSV output into the short text summaries kept under profiles/.
 Programs (run as the profiled program, after ``rocprofv3 ... --``):
 
   python3 -m memory_bound_dense_amd.profile_counters gemv --workload NAME --launches N
-      N launches of the GEMV in its automatic configuration, rotating over
-      copies of the inputs that exceed 1 GiB (as bench.py does).
+      N launches of the GEMV in its automatic configuration (or the one given
+      by --variant/--grid), rotating over copies of the inputs that exceed
+      1 GiB (as bench.py does).
   python3 -m memory_bound_dense_amd.profile_counters copy --bytes X --launches N
       N device-to-device copies of X bytes (a plain copy kernel of known
       traffic: X bytes read and X bytes written), to calibrate the counters.
@@ -32,7 +33,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", "gemv_kernel.h"), os.path.join(PKG, "csrc", "gemv.hip")]
-GEMV_KERNEL = "gemv_kernel"
+GEMV_KERNEL = "gemv_"              # every GEMV kernel (row, realigning, row-per-lane)
 COPY_KERNEL = "copyBuffer"
 
 
@@ -56,7 +57,7 @@ def kernel_source_hash():
 
 # ---- programs ----------------------------------------------------------------
 
-def run_gemv(workload, launches):
+def run_gemv(workload, launches, variant=-1, grid=0):
     sys.path.insert(0, ROOT)
     import numpy as np
     import torch
@@ -74,6 +75,8 @@ def run_gemv(workload, launches):
     Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]
     torch.cuda.synchronize()
     g = mbd.Gemv()
+    if variant >= 0:
+        g.force_config(variant, grid)
     v, grid, kgroups = g.query_config(n, k, dtype)
     for i in range(launches):
         g(Bs[i % nbuf], As[i % nbuf], Cs[i % nbuf])
@@ -185,6 +188,8 @@ def main():
     p = sub.add_parser("gemv")
     p.add_argument("--workload", default="gemv_18432x7168_f16")
     p.add_argument("--launches", type=int, default=20)
+    p.add_argument("--variant", type=int, default=-1, help="force this variant (-1: automatic)")
+    p.add_argument("--grid", type=int, default=0, help="grid of a forced variant (0: full)")
     p = sub.add_parser("copy")
     p.add_argument("--bytes", type=int, default=256 << 20)
     p.add_argument("--launches", type=int, default=10)
@@ -204,7 +209,7 @@ def main():
     p.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd == "gemv":
-        run_gemv(a.workload, a.launches)
+        run_gemv(a.workload, a.launches, a.variant, a.grid)
     elif a.cmd == "copy":
         run_copy(a.bytes, a.launches)
     elif a.cmd == "summarize-trace":
