@@ -160,6 +160,17 @@ typedef struct {
                          one element per step -- the uncoalesced layout of
                          TileLang Case Studies, Case B, kept for measurement
                          and never chosen automatically */
+  int32_t stages;     /* 0: the plain loop (a wave issues a group of loads,
+                         then waits for it); 1..3: the pipelined-B form of
+                         TileLang Case Studies, Case B.1, kept for measurement
+                         and never chosen automatically -- each wave keeps
+                         `stages` - 1 items of `unroll` steps x `rows` rows in
+                         flight while it consumes one (1 = sequential,
+                         2 = double, 3 = triple buffering); it needs 16-byte
+                         aligned rows (k % 8 == 0, B 16-byte aligned) and
+                         returns GEMV_ERR_UNSUPPORTED otherwise */
+  int32_t b_lds;      /* stages > 0: 1 = the slots are in LDS, filled by
+                         buffer loads that write LDS directly; 0 = registers */
 } gemv_variant_info_t;
 
 typedef struct {

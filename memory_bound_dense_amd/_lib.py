@@ -50,7 +50,8 @@ class gemv_variant_info_t(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("unroll", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("splits", ctypes.c_int32), ("a_mode", ctypes.c_int32),
                 ("b_policy", ctypes.c_int32), ("cross_wg", ctypes.c_int32),
-                ("layout", ctypes.c_int32)]
+                ("layout", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("b_lds", ctypes.c_int32)]
 
 
 class gemv_epilogue_t(ctypes.Structure):

@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemv.so")
 SOURCES = [os.path.join(CSRC, "gemv.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, "gemv_kernel.h"), os.path.join(CSRC, "gla_kernel.h"),
-                  os.path.join(INCLUDE, "gemv.h"), os.path.join(INCLUDE, "gla_decode.h")]
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("gemv_kernel.h", "gemv_staged.h", "gla_kernel.h")] + \
+    [os.path.join(INCLUDE, "gemv.h"), os.path.join(INCLUDE, "gla_decode.h")]
 # measurement aid: a plain streaming read (the practical HBM read ceiling)
 PROBE_LIB = os.path.join(PKG, "libmbd_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]

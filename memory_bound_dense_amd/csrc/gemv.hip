@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "gemv_kernel.h"
+#include "gemv_staged.h"
 #include "gla_kernel.h"
 
 namespace {
@@ -36,6 +37,10 @@ constexpr int kLanesPerWave = 64;
    {&mbd::gemv_realign_kernel<mbd::DT_F16, R, U, W, POL>,                           \
     &mbd::gemv_realign_kernel<mbd::DT_BF16, R, U, W, POL>}}
 #define MBD_REALIGN(U, W, POL) MBD_REALIGN_R(1, U, W, POL)
+#define MBD_STAGED(R, U, W, P, LDS)                                                 \
+  {{R, U, W, 1, mbd::A_CACHED, kPolNT, 0, 0, P, LDS},                               \
+   {&mbd::gemv_staged_kernel<mbd::DT_F16, R, U, W, P, LDS, kPolNT>,                 \
+    &mbd::gemv_staged_kernel<mbd::DT_BF16, R, U, W, P, LDS, kPolNT>}}
 
 // The compiled variants: (rows R, unroll U, waves W, splits S, a mode, B
 // cache policy).  Row variants (S == 1) give each wave R whole rows; split
@@ -83,6 +88,12 @@ const Variant kVariants[] = {
     MBD_REALIGN(8, 8, NT), MBD_REALIGN_R(2, 4, 4, NT), MBD_REALIGN_R(2, 4, 8, NT),
     MBD_REALIGN_R(2, 2, 8, NT),
     MBD_REALIGN(2, 8, NT),
+    // 58..62: B prefetched P items ahead through register slots (P = 1: none)
+    MBD_STAGED(2, 2, 8, 1, false), MBD_STAGED(2, 2, 8, 2, false), MBD_STAGED(2, 2, 8, 3, false),
+    MBD_STAGED(2, 4, 8, 2, false), MBD_STAGED(1, 4, 8, 2, false),
+    // 63..66: the same through LDS slots filled by buffer loads into LDS
+    MBD_STAGED(2, 2, 8, 1, true), MBD_STAGED(2, 2, 8, 2, true), MBD_STAGED(2, 2, 8, 3, true),
+    MBD_STAGED(1, 4, 4, 2, true),
 };
 #undef NT
 #undef LDS
@@ -97,6 +108,8 @@ size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
     const int64_t len = mbd::kPadA + steps * mbd::kStep + 8;
     return (size_t)(4 * len);
   }
+  if (v.stages > 0)   // pipelined B: LDS slots of every wave, or none
+    return v.b_lds ? (size_t)v.waves * v.stages * v.unroll * v.rows * mbd::kStepBytes : 0;
   size_t b = 0;
   if (v.a_mode == mbd::A_LDS) b += (size_t)nsteps * mbd::kStepBytes;
   if (v.splits > 1) b += (size_t)v.waves * v.rows * sizeof(float);
@@ -135,7 +148,8 @@ int find_variant(const Plan& p) {
   for (int v = 0; v < kNumVariants; ++v) {
     const gemv_variant_info_t& i = kVariants[v].info;
     if (i.rows == p.rows && i.unroll == p.unroll && i.waves == p.waves && i.splits == p.splits &&
-        i.a_mode == p.a_mode && i.b_policy == p.policy && i.cross_wg == x && i.layout == 0)
+        i.a_mode == p.a_mode && i.b_policy == p.policy && i.cross_wg == x && i.layout == 0 &&
+        i.stages == 0)
       return v;
   }
   return -1;
@@ -303,6 +317,8 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, bool 
     q = p.kgroups;
   }
   const gemv_variant_info_t& info = kVariants[v].info;
+  // the pipelined variants load whole 16-byte granules of aligned rows only
+  if (info.stages > 0 && k > 0 && (k % 8 != 0 || !b_aligned)) return GEMV_ERR_UNSUPPORTED;
   const int64_t rb = rows_per_block(info);
   const int64_t nrb = (n + rb - 1) / rb;       // one row range per wave (or workgroup)
   if (g <= 0 || g > nrb) g = nrb;
@@ -474,7 +490,8 @@ extern "C" gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void*
   p.alpha = ep ? ep->alpha : 1.0f;
   // balanced shares: rows over the row units, full k-steps over the k-slices
   int64_t units;
-  if (vi.a_mode == mbd::A_LDS_SHIFTED) units = (int64_t)L.grid * vi.waves;      // a wave per unit
+  if (vi.a_mode == mbd::A_LDS_SHIFTED || vi.stages > 0)
+    units = (int64_t)L.grid * vi.waves;                                         // a wave per unit
   else if (vi.splits == 1 && !vi.cross_wg) units = (int64_t)L.grid * (vi.waves / vi.splits);
   else units = L.grid;                                                          // a workgroup per unit
   p.rows_q = (int)(n / units);

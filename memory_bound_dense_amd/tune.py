@@ -116,17 +116,20 @@ def main():
                      "kgroups": cfg[2], "rows": info.rows, "unroll": info.unroll,
                      "waves": info.waves, "splits": info.splits, "a_mode": info.a_mode,
                      "b_policy": info.b_policy, "cross_wg": info.cross_wg, "layout": info.layout,
+                     "stages": info.stages, "b_lds": info.b_lds,
                      "us_median": round(med, 3), "us_min": round(min(times[i]), 3),
                      "gbs": round(nbytes / med / 1e3, 1), "auto": cfg == auto})
     rows.sort(key=lambda r: r["us_median"])
     best = rows[0]["us_median"]
-    print("%4s %4s %6s %3s | %2s %2s %2s %2s %2s %2s %2s | %9s %8s %7s" % (
-        "rank", "var", "grid", "kg", "R", "U", "W", "S", "am", "pl", "x", "us", "GB/s", "vs best"))
+    print("%4s %4s %6s %3s | %2s %2s %2s %2s %2s %2s %2s %2s %2s | %9s %8s %7s" % (
+        "rank", "var", "grid", "kg", "R", "U", "W", "S", "am", "pl", "x", "P", "L", "us", "GB/s",
+        "vs best"))
     for r_i, r in enumerate(rows):
         if r_i < args.top or r["auto"]:
-            print("%4d %4d %6d %3d | %2d %2d %2d %2d %2d %2d %2d | %9.3f %8.1f %6.1f%%%s" % (
+            print("%4d %4d %6d %3d | %2d %2d %2d %2d %2d %2d %2d %2d %2d | %9.3f %8.1f %6.1f%%%s" % (
                 r_i + 1, r["variant"], r["grid"], r["kgroups"], r["rows"], r["unroll"], r["waves"],
-                r["splits"], r["a_mode"], r["b_policy"], r["cross_wg"], r["us_median"], r["gbs"],
+                r["splits"], r["a_mode"], r["b_policy"], r["cross_wg"], r["stages"], r["b_lds"],
+                r["us_median"], r["gbs"],
                 100 * (r["us_median"] / best - 1), "  <- automatic plan" if r["auto"] else ""))
     if args.out:
         with open(args.out, "a") as f:

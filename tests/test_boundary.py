@@ -60,6 +60,13 @@ def test_variant_table():
         assert info.layout in (0, 1)
         if info.layout == 1:
             assert info.rows == 64 and info.splits == 1 and not info.cross_wg
+        assert 0 <= info.stages <= 3 and info.b_lds in (0, 1)
+        if info.stages:
+            # pipelined B: cached a, one wave per row range, no split
+            assert info.a_mode == 1 and info.splits == 1 and not info.cross_wg
+            assert info.layout == 0
+        else:
+            assert info.b_lds == 0
     assert mbd.gemv_variant_info(nv)[0] == _lib.GEMV_ERR_INVALID_ARG
     assert mbd.gemv_variant_info(-1)[0] == _lib.GEMV_ERR_INVALID_ARG
 

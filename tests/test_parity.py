@@ -60,6 +60,14 @@ def fits(g, v, n, k, dtype):
         g.force_config(-1)
 
 
+def staged_rejects(v, Bd):
+    """The pipelined-B variants take 16-byte aligned rows only (and say so
+    with GEMV_ERR_UNSUPPORTED)."""
+    k = Bd.shape[1]
+    return v >= 0 and mbd.gemv_variant_info(v)[1].stages > 0 and k > 0 and \
+        (k % 8 != 0 or Bd.data_ptr() % 16 != 0)
+
+
 def run(g, Bd, ad, variant=-1, grid=0, kgroups=0):
     """c = B @ a with a forced configuration; None if the variant cannot run
     this shape."""
@@ -72,6 +80,13 @@ def run(g, Bd, ad, variant=-1, grid=0, kgroups=0):
     try:
         if n > 0:
             LAST_EXTRA[0] = _extra_adds(g, n, k, dtype)
+        if staged_rejects(variant, Bd):
+            with pytest.raises(mbd.GemvError) as ei:
+                g(Bd, ad, c)
+            assert ei.value.status == mbd._lib.GEMV_ERR_UNSUPPORTED
+            torch.cuda.synchronize()
+            assert torch.all(torch.isnan(c))     # nothing was launched
+            return None
         g(Bd, ad, c)
     finally:
         g.force_config(-1)
@@ -200,6 +215,9 @@ def test_misaligned_base_pointers(g, dtype):
     assert Bd.data_ptr() % 16 != 0 and ad.data_ptr() % 16 != 0
     for v in [-1] + VARIANTS:
         if not fits(g, v, n, k, dtype):
+            continue
+        if staged_rejects(v, Bd):
+            assert run(g, Bd, ad, v) is None
             continue
         cbig = torch.full((n + 5,), 7.0, dtype=torch_dtype(dtype), device="cuda")
         c = cbig[5:]
@@ -402,6 +420,9 @@ def run_ex(g, Bd, ad, alpha, bias, variant=-1, c=None):
     dtype = mbd.GEMV_F16 if Bd.dtype == torch.float16 else mbd.GEMV_BF16
     if not fits(g, variant, n, k, dtype):
         return None
+    if staged_rejects(variant, Bd):
+        assert run(g, Bd, ad, variant) is None
+        return None
     if c is None:
         c = torch.full((n,), float("nan"), dtype=Bd.dtype, device=Bd.device)
     g.force_config(variant)
@@ -505,3 +526,35 @@ def test_random_shapes(g):
         from parity import ulp
         bound = 4e-3 * abs(alpha) * ab_e + ulp(dtype, rv)
         assert np.all(np.abs(gv - rv) <= bound), ("epilogue", case, n, k)
+
+
+STAGED = [v for v in VARIANTS if mbd.gemv_variant_info(v)[1].stages > 0]
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
+def test_staged_pipeline(g, dtype):
+    """The pipelined-B variants: many row trips per wave (small grids), item
+    counts that are not multiples of the depth, groups past the last full
+    step, k below one step, partial last steps, and the 64-row store
+    batches; integer inputs make every order exact, so the result must equal
+    the oracle bit for bit, and c's neighbours stay untouched."""
+    assert STAGED
+    for n, k in [(1000, 7168), (300, 512), (129, 1536), (77, 4104), (65, 256), (333, 2560),
+                 (5, 8)]:
+        B, a = integer_inputs(n, k, dtype, seed=n + k)
+        ref = oracle.gemv(dtype, B, a)[0]
+        Bd, ad = to_device(B, dtype), to_device(a, dtype)
+        for v in STAGED:
+            for grid in (0, 1, 3, 17):
+                cbig = torch.full((n + 130,), 5.0, dtype=torch_dtype(dtype), device="cuda")
+                c = cbig[65:65 + n]
+                g.force_config(v, grid)
+                try:
+                    g(Bd, ad, c)
+                finally:
+                    g.force_config(-1)
+                torch.cuda.synchronize()
+                got = to_bits(c)
+                bad = np.nonzero(got != ref)[0]
+                assert bad.size == 0, (n, k, v, grid, bad[:5])
+                assert torch.all(cbig[:65] == 5.0) and torch.all(cbig[65 + n:] == 5.0), (n, k, v)

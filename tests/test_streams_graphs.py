@@ -103,7 +103,8 @@ def test_two_streams_two_handles_repeatable():
 
 def test_stress_split_and_lds_variants_repeatable():
     """Variants with synchronisation inside (LDS staging, in-workgroup splits,
-    cross-workgroup splits, realigned rows): 150 back-to-back runs each with
+    cross-workgroup splits, realigned rows, B pipelined through LDS with
+    explicit waits): 150 back-to-back runs each with
     random host delays and eager work between them must all give the bits
     of the first run."""
     g = mbd.Gemv()
@@ -111,7 +112,7 @@ def test_stress_split_and_lds_variants_repeatable():
     picks = []
     for v in range(mbd.gemv_num_variants()):
         info = mbd.gemv_variant_info(v)[1]
-        if info.layout == 0 and (info.a_mode != 1 or info.splits > 1 or info.cross_wg):
+        if info.layout == 0 and (info.a_mode != 1 or info.splits > 1 or info.cross_wg or info.b_lds):
             picks.append(v)
     shapes = [(64, 65536, BF16), (1000, 7001, F16), (300, 4096, BF16)]
     for i, (n, k, dtype) in enumerate(shapes):
