@@ -157,8 +157,9 @@ int find_variant(const Plan& p) {
 
 // The general rule, for shapes without a measured entry, in this order:
 //  1. rows that do not start on 16-byte boundaries (k % 8 != 0, or B itself
-//     misaligned): the realigning kernel -- aligned granules of B, a staged
-//     twice in LDS -- on a persistent grid, when its LDS fits;
+//     misaligned): the realigning kernel -- aligned granules of B from each
+//     row's 128-byte line, a staged twice in LDS -- on a persistent grid,
+//     when its LDS fits;
 //  2. too few rows to give the GPU 4096 waves even with 16 waves per row:
 //     k split across workgroups as well (cross-workgroup variants);
 //  3. misaligned rows whose realigning LDS does not fit: unaligned 16-byte
@@ -170,8 +171,8 @@ int find_variant(const Plan& p) {
 //     512-element steps per slice) while the grid has fewer than 4096 waves.
 Plan rule_plan(int64_t n, int64_t k, size_t max_lds, bool b_aligned) {
   const int64_t nfull0 = k / mbd::kStep;
-  // 1. (persistent grid: a is staged once per workgroup; as fast as unaligned
-  // 16-byte loads on MI355X and needs no unaligned access at all)
+  // 1. (persistent grid: a is staged once per workgroup; measured faster than
+  // unaligned 16-byte loads on MI355X, and needs no unaligned access at all)
   if (k > 0 && (k % 8 != 0 || !b_aligned)) {
     Plan p = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
     if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
