@@ -139,7 +139,6 @@ struct TunedShape {
   Plan plan;
 };
 const TunedShape kTuned[] = {
-    {4096, 11008, {1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0, 1}},
     {4096, 14336, {1, 4, 4, 1, mbd::A_CACHED, kPolNT, 512, 1}},
 };
 
@@ -166,10 +165,12 @@ int find_variant(const Plan& p) {
 //     loads with a staged in LDS (or through the caches if that does not fit
 //     either);
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
-//     wave when both n and k are large, and k split inside a workgroup while
-//     every wave still streams at least 8 KiB of B, further (down to two
-//     512-element steps per slice) while the grid has fewer than 4096 waves.
-Plan rule_plan(int64_t n, int64_t k, size_t max_lds, bool b_aligned) {
+//     wave when both n and k are large; a row of at most 8 steps goes to one
+//     wave; longer rows are split along k inside a
+//     workgroup until every wave has at most 4 steps (one batch of loads:
+//     measured best on MI355X), further (down to two steps per slice) while
+//     the grid has fewer than 4096 waves.
+Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned) {
   const int64_t nfull0 = k / mbd::kStep;
   // 1. (persistent grid: a is staged once per workgroup; measured faster than
   // unaligned 16-byte loads on MI355X, and needs no unaligned access at all)
@@ -196,20 +197,24 @@ Plan rule_plan(int64_t n, int64_t k, size_t max_lds, bool b_aligned) {
   // 4.
   const int64_t nfull = k / mbd::kStep;
   const int R = (n >= 4096 && k >= 6144) ? 2 : 1;
-  const int64_t row_bytes = 2 * k * R;
+  // a row of at most 8 steps: one wave takes all of it, in one batch for
+  // fp16; bf16's widening costs twice the vector work of fp16's mixed FMA,
+  // and two batches of 4 steps measure ~2% faster there
+  if (R == 1 && nfull <= 8)
+    return Plan{1, dtype == GEMV_F16 ? 8 : 4, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
   const int smax = R == 1 ? 16 : 8;
   int S = 1;
-  while (S < smax && row_bytes / (2 * S) >= 8192 && nfull >= 2 * (2 * S)) S *= 2;
+  while (S < smax && (nfull + S - 1) / S > 4) S *= 2;   // at most 4 steps per wave: one batch
   while (S < smax && ((n + R - 1) / R) * S < 4096 && nfull >= 2 * (2 * S)) S *= 2;
   const int W = S == 1 ? 4 : (S <= 8 ? 8 : 16);
   return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0, 1};
 }
 
-Plan auto_plan(int64_t n, int64_t k, size_t max_lds, bool b_aligned) {
+Plan auto_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned) {
   if (b_aligned)
     for (const TunedShape& t : kTuned)
       if (t.n == n && t.k == k) return t.plan;
-  return rule_plan(n, k, max_lds, b_aligned);
+  return rule_plan(n, k, dtype, max_lds, b_aligned);
 }
 
 constexpr uint32_t kMagic = 0x47454d56u;   // "GEMV"
@@ -300,8 +305,8 @@ struct Launch {
 };
 static_assert(GEMV_FLAG_XCD_CONTIGUOUS == mbd::kFlagXcdContiguous, "flag values agree");
 
-static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, bool b_aligned,
-                             Launch* L) {
+static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_dtype_t dtype,
+                             bool b_aligned, Launch* L) {
   int v;
   int64_t g, q;
   int flags = 0;
@@ -311,7 +316,7 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, bool 
     q = h->forced.kgroups;
     flags = h->forced.flags;
   } else {
-    const Plan p = auto_plan(n, k, h->max_lds, b_aligned);
+    const Plan p = auto_plan(n, k, dtype, h->max_lds, b_aligned);
     v = find_variant(p);
     if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
     g = p.grid;
@@ -449,7 +454,7 @@ extern "C" gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k
   if (dtype != GEMV_F16 && dtype != GEMV_BF16) return GEMV_ERR_UNSUPPORTED_DTYPE;
   if (n <= 0 || k < 0 || n > GEMV_MAX_N || k > GEMV_MAX_K) return GEMV_ERR_INVALID_ARG;
   Launch L;
-  gemv_status_t s = resolve(h, n, k, true, &L);
+  gemv_status_t s = resolve(h, n, k, dtype, true, &L);
   if (s != GEMV_OK) return s;
   out->variant = L.variant;
   out->grid = L.grid;
@@ -474,7 +479,7 @@ extern "C" gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void*
   if (hipGetDevice(&dev) != hipSuccess) return report(h, GEMV_ERR_HIP, "hipGetDevice");
   if (dev != h->device) return report(h, GEMV_ERR_WRONG_DEVICE, "gemv_run");
   Launch L;
-  s = resolve(h, n, k, ((uintptr_t)B & 15u) == 0, &L);
+  s = resolve(h, n, k, dtype, ((uintptr_t)B & 15u) == 0, &L);
   if (s != GEMV_OK) return report(h, s, "no variant fits (LDS or workspace)");
   const Variant& var = kVariants[L.variant];
   const gemv_variant_info_t& vi = var.info;

@@ -56,6 +56,9 @@ constexpr int kVec = 8;                 // 16-bit elements per 16-byte load
 constexpr int kStep = kLanes * kVec;    // elements per row per wave-load
 constexpr int kStepBytes = kStep * 2;   // 1 KiB
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+// A buffer offset beyond every descriptor's range (ranges here are < 2^31
+// bytes): a load from it returns zeros without a memory access.
+constexpr uint32_t kOffsetOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -299,33 +302,49 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
         for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
       }
     }
-    for (; t < t1; ++t) {
-      u32x4 bv[R];
+    // The last, partial group: the remaining full steps (fewer than U) and,
+    // on the last slice, the partial step, loaded in one batch -- one round
+    // trip, not one per step.  Every slot loads; a slot past them loads from
+    // an offset outside the descriptor's range, which returns zeros without
+    // touching memory, so the group has no branches (and no registers of its
+    // own beyond the main loop's).  a is zeroed there too, so 0 x inf cannot
+    // turn into a NaN.
+    const int nrem = t1 - t;                           // 0 .. U-1
+    if (nrem > 0 || tail) {
+      const int e0 = (nfull * kLanes + lane) * kVec;   // this lane's first element of the partial step
+      const bool tail_full = tail && e0 + kVec <= k;   // a whole 16-byte vector inside the row
+      u32x4 bv[U][R];
+      u32x4 av[U];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        bv[r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, t * kStepBytes + lane_off, soff[r], BPOL);
-      }
-      u32x4 av;
-      if constexpr (AMODE == A_LDS) {
-        av = a_lds[t * kLanes + lane];
-      } else {
-        av = __builtin_amdgcn_raw_buffer_load_b128(arsrc, t * kStepBytes + lane_off, 0u, 0);
+      for (int u = 0; u < U; ++u) {
+        const int st = t + u;
+        const bool ok = u < nrem || (u == nrem && tail_full);
+        const uint32_t off = ok ? (uint32_t)(st * kStepBytes + lane_off) : kOffsetOutOfRange;
+#pragma unroll
+        for (int r = 0; r < R; ++r) bv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, off, soff[r], BPOL);
+        if constexpr (AMODE == A_LDS) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 x = a_lds[ok ? st * kLanes + lane : 0];
+          av[u] = ok ? x : z;
+        } else {
+          av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0u, 0);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) fma8<DT>(bv[r], av, acc[r][0], acc[r][1]);
-    }
-    if (tail) {
-      const int e0 = (nfull * kLanes + lane) * kVec;
-      u32x4 av;
-      if constexpr (AMODE == A_LDS) {
-        av = a_lds[nfull * kLanes + lane];
-      } else {
-        av = load_vec_tail(arsrc, e0, k, 0u);
-      }
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        u32x4 bv = load_vec_tail(brsrc, e0, k, soff[r]);
-        fma8<DT>(bv, av, acc[r][0], acc[r][1]);
+        for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
+      }
+      // the one vector that straddles k (rows not 16-byte aligned only)
+      if (tail && (k & (kVec - 1)) != 0 && e0 < k && e0 + kVec > k) {
+        u32x4 ap;
+        if constexpr (AMODE == A_LDS) {
+          ap = a_lds[nfull * kLanes + lane];
+        } else {
+          ap = load_vec_tail(arsrc, e0, k, 0u);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) fma8<DT>(load_vec_tail(brsrc, e0, k, soff[r]), ap, acc[r][0], acc[r][1]);
       }
     }
 
