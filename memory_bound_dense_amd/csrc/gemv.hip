@@ -551,6 +551,9 @@ extern "C" gemv_status_t gla_check_args(const void* q, const void* k, const void
   return GEMV_OK;
 }
 
+// Heads of at most this many rows stage exp(gk), k and q in LDS (6 KiB).
+constexpr int64_t kGlaStageRows = 512;
+
 using GlaFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
                        const float*, float*, uint16_t*, int, int, float, int);
 
@@ -567,21 +570,29 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
   if (dev != h->device) return report(h, GEMV_ERR_WRONG_DEVICE, "gla_decode_step");
   // The widest column block (8, 16 or 32 lanes x 4 columns) that still gives
   // >= 16 workgroups per CU; state loads and stores non-temporal (measured on
-  // MI355X: ~13% faster than the default policy; 2048 heads of 128 x 128 run
-  // at ~90% of a plain copy of the same bytes).
-  static const GlaFn fns[2][3] = {
-      {&mbd::gla_decode_kernel<mbd::DT_F16, 8, 4, kPolNT, kPolNT>,
-       &mbd::gla_decode_kernel<mbd::DT_F16, 16, 4, kPolNT, kPolNT>,
-       &mbd::gla_decode_kernel<mbd::DT_F16, 32, 4, kPolNT, kPolNT>},
-      {&mbd::gla_decode_kernel<mbd::DT_BF16, 8, 4, kPolNT, kPolNT>,
-       &mbd::gla_decode_kernel<mbd::DT_BF16, 16, 4, kPolNT, kPolNT>,
-       &mbd::gla_decode_kernel<mbd::DT_BF16, 32, 4, kPolNT, kPolNT>}};
+  // MI355X: ~13% faster than the default policy).  Heads of at most
+  // kGlaStageRows rows get exp(gk), k and q staged once per workgroup in LDS.
+  static const GlaFn fns[2][2][3] = {
+      {{&mbd::gla_decode_kernel<mbd::DT_F16, 8, 4, kPolNT, kPolNT, false>,
+        &mbd::gla_decode_kernel<mbd::DT_F16, 16, 4, kPolNT, kPolNT, false>,
+        &mbd::gla_decode_kernel<mbd::DT_F16, 32, 4, kPolNT, kPolNT, false>},
+       {&mbd::gla_decode_kernel<mbd::DT_F16, 8, 4, kPolNT, kPolNT, true>,
+        &mbd::gla_decode_kernel<mbd::DT_F16, 16, 4, kPolNT, kPolNT, true>,
+        &mbd::gla_decode_kernel<mbd::DT_F16, 32, 4, kPolNT, kPolNT, true>}},
+      {{&mbd::gla_decode_kernel<mbd::DT_BF16, 8, 4, kPolNT, kPolNT, false>,
+        &mbd::gla_decode_kernel<mbd::DT_BF16, 16, 4, kPolNT, kPolNT, false>,
+        &mbd::gla_decode_kernel<mbd::DT_BF16, 32, 4, kPolNT, kPolNT, false>},
+       {&mbd::gla_decode_kernel<mbd::DT_BF16, 8, 4, kPolNT, kPolNT, true>,
+        &mbd::gla_decode_kernel<mbd::DT_BF16, 16, 4, kPolNT, kPolNT, true>,
+        &mbd::gla_decode_kernel<mbd::DT_BF16, 32, 4, kPolNT, kPolNT, true>}}};
   int sel = 0;
   const int64_t want = 16 * (int64_t)h->num_cus;
   for (int c = 2; c >= 0; --c) {
     const int64_t cw = 4 * (8 << c);
     if (bh * ((dv + cw - 1) / cw) >= want || c == 0) { sel = c; break; }
   }
+  const int stage = dk <= kGlaStageRows ? 1 : 0;
+  const size_t lds = stage ? (size_t)(3 * dk) * sizeof(float) : 0;
   const int64_t cw = 4 * (8 << sel);
   int nblk = (int)((dv + cw - 1) / cw);
   const int64_t grid = bh * nblk;
@@ -592,8 +603,8 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
   int dki = (int)dk, dvi = (int)dv;
   void* args[] = {(void*)&qp, (void*)&kp,  (void*)&vp,  (void*)&gp,    (void*)&S_in, (void*)&S_out,
                   (void*)&op, (void*)&dki, (void*)&dvi, (void*)&scale, (void*)&nblk};
-  hipError_t e = hipLaunchKernel((const void*)fns[dtype][sel], dim3((unsigned)grid),
-                                 dim3(mbd::kGlaThreads), args, 0, stream);
+  hipError_t e = hipLaunchKernel((const void*)fns[dtype][stage][sel], dim3((unsigned)grid),
+                                 dim3(mbd::kGlaThreads), args, lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));
   return GEMV_OK;
 }

@@ -29,7 +29,11 @@ constexpr int kGlaThreads = 256;
 // kGlaThreads/LPR row groups.  Workgroup b handles head b / nblk and column
 // block b % nblk.  S_out may equal S_in (each 16 bytes are read, then written,
 // by one lane).
-template <int DT, int LPR, int ROWS = 4, int LPOL = 0, int SPOL = 0>
+// STAGE: exp(gk), k and q of the head are computed once per workgroup into
+// LDS (3 * dk floats of dynamic LDS) instead of being loaded -- and exp taken
+// -- by every lane of a row group for every row; the host picks it when the
+// head is short enough for that LDS to stay small.
+template <int DT, int LPR, int ROWS = 4, int LPOL = 0, int SPOL = 0, bool STAGE = false>
 __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ gk, const float* S_in,
@@ -52,6 +56,16 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
   const __amdgpu_buffer_rsrc_t sout_r =
       make_rsrc(S_out + rowbase * dv, (uint32_t)dk * (uint32_t)dv * 4u);
 
+  extern __shared__ float gla_rows[];        // STAGE: e[0..dk), k[dk..2dk), q[2dk..3dk)
+  if constexpr (STAGE) {
+    for (int i = t; i < dk; i += kGlaThreads) {
+      gla_rows[i] = expf(widen<DT>(gk[rowbase + i]));
+      gla_rows[dk + i] = widen<DT>(k[rowbase + i]);
+      gla_rows[2 * dk + i] = widen<DT>(q[rowbase + i]);
+    }
+    __syncthreads();
+  }
+
   float vj[4] = {0.f, 0.f, 0.f, 0.f};
   if (active) {
 #pragma unroll
@@ -73,9 +87,15 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
         if (i < dk) {
           sv[r] = __builtin_amdgcn_raw_buffer_load_b128(
               sin_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, LPOL);
-          e[r] = expf(widen<DT>(gk[rowbase + i]));
-          ki[r] = widen<DT>(k[rowbase + i]);
-          qi[r] = widen<DT>(q[rowbase + i]);
+          if constexpr (STAGE) {
+            e[r] = gla_rows[i];
+            ki[r] = gla_rows[dk + i];
+            qi[r] = gla_rows[2 * dk + i];
+          } else {
+            e[r] = expf(widen<DT>(gk[rowbase + i]));
+            ki[r] = widen<DT>(k[rowbase + i]);
+            qi[r] = widen<DT>(q[rowbase + i]);
+          }
         }
       }
 #pragma unroll
