@@ -32,7 +32,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemv_kernel.h", "gemv_staged.h", "gemv.hip")]
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemv_kernel.h", "gemv_staged.h", "gemv.hip", "handle.h")]
 GEMV_KERNEL = "gemv_"              # every GEMV kernel (row, realigning, row-per-lane)
 COPY_KERNEL = "copyBuffer"
 
