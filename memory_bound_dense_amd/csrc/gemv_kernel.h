@@ -276,66 +276,46 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.0f;
 
-    int t = t0;
-    for (; t + U <= t1; t += U) {
-      u32x4 bv[U][R];
-      u32x4 av[U];
+    if constexpr (R == 1) {
+      // One row per wave: every group in the form of the last group below
+      // (slots past the wave's steps load zeros from outside the
+      // descriptor's range; the partial step is the slot after step t1 - 1).
+      // Measured on MI355X 1-2.5% faster than the two-part loop for these
+      // variants; for two rows and more the two-part loop, whose full groups
+      // need fewer registers, is faster.
+      const int e0 = (nfull * kLanes + lane) * kVec;
+      const bool tail_full = tail && e0 + kVec <= k;
+      const int tend = t1 + (tail ? 1 : 0);
+      for (int t = t0; t < tend; t += U) {
+        u32x4 bv[U][R];
+        u32x4 av[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < U; ++u) {
+          const int st = t + u;
+          const bool ok = st < t1 || (st == t1 && tail_full);
+          const uint32_t off = ok ? (uint32_t)(st * kStepBytes + lane_off) : kOffsetOutOfRange;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          bv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, (t + u) * kStepBytes + lane_off,
-                                                           soff[r], BPOL);
+          for (int r = 0; r < R; ++r) bv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, off, soff[r], BPOL);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int st = t + u;
+          const bool ok = st < t1 || (st == t1 && tail_full);
+          if constexpr (AMODE == A_LDS) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 x = a_lds[ok ? st * kLanes + lane : 0];
+            av[u] = ok ? x : z;
+          } else {
+            const uint32_t off = ok ? (uint32_t)(st * kStepBytes + lane_off) : kOffsetOutOfRange;
+            av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0u, 0);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if constexpr (AMODE == A_LDS) {
-          av[u] = a_lds[(t + u) * kLanes + lane];
-        } else {
-          av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, (t + u) * kStepBytes + lane_off, 0u, 0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
-      }
-    }
-    // The last, partial group: the remaining full steps (fewer than U) and,
-    // on the last slice, the partial step, loaded in one batch -- one round
-    // trip, not one per step.  Every slot loads; a slot past them loads from
-    // an offset outside the descriptor's range, which returns zeros without
-    // touching memory, so the group has no branches (and no registers of its
-    // own beyond the main loop's).  a is zeroed there too, so 0 x inf cannot
-    // turn into a NaN.
-    const int nrem = t1 - t;                           // 0 .. U-1
-    if (nrem > 0 || tail) {
-      const int e0 = (nfull * kLanes + lane) * kVec;   // this lane's first element of the partial step
-      const bool tail_full = tail && e0 + kVec <= k;   // a whole 16-byte vector inside the row
-      u32x4 bv[U][R];
-      u32x4 av[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int st = t + u;
-        const bool ok = u < nrem || (u == nrem && tail_full);
-        const uint32_t off = ok ? (uint32_t)(st * kStepBytes + lane_off) : kOffsetOutOfRange;
-#pragma unroll
-        for (int r = 0; r < R; ++r) bv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, off, soff[r], BPOL);
-        if constexpr (AMODE == A_LDS) {
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 x = a_lds[ok ? st * kLanes + lane : 0];
-          av[u] = ok ? x : z;
-        } else {
-          av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0u, 0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
-      }
-      // the one vector that straddles k (rows not 16-byte aligned only)
       if (tail && (k & (kVec - 1)) != 0 && e0 < k && e0 + kVec > k) {
         u32x4 ap;
         if constexpr (AMODE == A_LDS) {
@@ -345,6 +325,78 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) fma8<DT>(load_vec_tail(brsrc, e0, k, soff[r]), ap, acc[r][0], acc[r][1]);
+      }
+    } else {
+      int t = t0;
+      for (; t + U <= t1; t += U) {
+        u32x4 bv[U][R];
+        u32x4 av[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            bv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, (t + u) * kStepBytes + lane_off,
+                                                             soff[r], BPOL);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if constexpr (AMODE == A_LDS) {
+            av[u] = a_lds[(t + u) * kLanes + lane];
+          } else {
+            av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, (t + u) * kStepBytes + lane_off, 0u, 0);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
+        }
+      }
+      // The last, partial group: the remaining full steps (fewer than U) and,
+      // on the last slice, the partial step, loaded in one batch -- one round
+      // trip, not one per step.  Every slot loads; a slot past them loads from
+      // an offset outside the descriptor's range, which returns zeros without
+      // touching memory, so the group has no branches (and no registers of its
+      // own beyond the main loop's).  a is zeroed there too, so 0 x inf cannot
+      // turn into a NaN.
+      const int nrem = t1 - t;                           // 0 .. U-1
+      if (nrem > 0 || tail) {
+        const int e0 = (nfull * kLanes + lane) * kVec;   // this lane's first element of the partial step
+        const bool tail_full = tail && e0 + kVec <= k;   // a whole 16-byte vector inside the row
+        u32x4 bv[U][R];
+        u32x4 av[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int st = t + u;
+          const bool ok = u < nrem || (u == nrem && tail_full);
+          const uint32_t off = ok ? (uint32_t)(st * kStepBytes + lane_off) : kOffsetOutOfRange;
+#pragma unroll
+          for (int r = 0; r < R; ++r) bv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(brsrc, off, soff[r], BPOL);
+          if constexpr (AMODE == A_LDS) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 x = a_lds[ok ? st * kLanes + lane : 0];
+            av[u] = ok ? x : z;
+          } else {
+            av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0u, 0);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
+        }
+        // the one vector that straddles k (rows not 16-byte aligned only)
+        if (tail && (k & (kVec - 1)) != 0 && e0 < k && e0 + kVec > k) {
+          u32x4 ap;
+          if constexpr (AMODE == A_LDS) {
+            ap = a_lds[nfull * kLanes + lane];
+          } else {
+            ap = load_vec_tail(arsrc, e0, k, 0u);
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) fma8<DT>(load_vec_tail(brsrc, e0, k, soff[r]), ap, acc[r][0], acc[r][1]);
+        }
       }
     }
 
