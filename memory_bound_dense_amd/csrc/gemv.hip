@@ -95,6 +95,8 @@ const Variant kVariants[] = {
     // 63..66: the same through LDS slots filled by buffer loads into LDS
     MBD_STAGED(2, 2, 8, 1, true), MBD_STAGED(2, 2, 8, 2, true), MBD_STAGED(2, 2, 8, 3, true),
     MBD_STAGED(1, 4, 4, 2, true),
+    // 67..68: realigning, 16 waves per workgroup (half the staging of a per wave)
+    MBD_REALIGN(4, 16, NT), MBD_REALIGN(2, 16, NT),
 };
 #undef NT
 #undef LDS
@@ -157,27 +159,37 @@ int find_variant(const Plan& p) {
 
 // The general rule, for shapes without a measured entry, in this order:
 //  1. rows that do not start on 16-byte boundaries (k % 8 != 0, or B itself
-//     misaligned): the realigning kernel -- aligned granules of B from each
-//     row's 128-byte line, a staged twice in LDS -- on a persistent grid,
-//     when its LDS fits;
+//     misaligned), as long as the realigning kernel's two copies of a leave
+//     room for 32 waves per CU: that kernel -- aligned granules of B from
+//     each row's 128-byte line, a staged twice in LDS -- with 8 waves per
+//     workgroup on a persistent grid while its LDS is <= 40 KiB (4
+//     workgroups per CU), and, for n >= 4096, with 16 waves per workgroup
+//     (one row each, 2 workgroups per CU) while it is <= 70 KiB (k ~ 15.8K;
+//     measured: ahead by 9% at k = 14337, behind by 7% at k = 16383);
 //  2. too few rows to give the GPU 4096 waves even with 16 waves per row:
 //     k split across workgroups as well (cross-workgroup variants);
-//  3. misaligned rows whose realigning LDS does not fit: unaligned 16-byte
-//     loads with a staged in LDS (or through the caches if that does not fit
-//     either);
+//  3. misaligned rows longer than that: unaligned 16-byte loads, two rows
+//     per one-wave workgroup when n >= 2048, otherwise the plan of 4.
+//     (Measured on MI355X over misaligned shapes with k from 4097 to 65537:
+//     the realigning kernel leads up to k ~ 14K and then falls behind, 13-40%
+//     at k >= 16K, as its LDS cuts the waves per CU.)
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
-//     wave when both n and k are large; a row of at most 8 steps goes to one
-//     wave; longer rows are split along k inside a
+//     wave (a read once for both) when n >= 1024 and k >= 6144; a row of at
+//     most 8 steps goes to one wave; longer rows are split along k inside a
 //     workgroup until every wave has at most 4 steps (one batch of loads:
 //     measured best on MI355X), further (down to two steps per slice) while
-//     the grid has fewer than 4096 waves.
+//     the grid has fewer than 4096 waves.  (Two rows per wave measured 2-12%
+//     faster than one for n = 1024..3072 and k = 8K..64K.)
 Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned) {
   const int64_t nfull0 = k / mbd::kStep;
-  // 1. (persistent grid: a is staged once per workgroup; measured faster than
-  // unaligned 16-byte loads on MI355X, and needs no unaligned access at all)
-  if (k > 0 && (k % 8 != 0 || !b_aligned)) {
-    Plan p = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
-    if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
+  const bool misaligned = k > 0 && (k % 8 != 0 || !b_aligned);
+  // 1. (a is staged once per workgroup; no unaligned access at all)
+  if (misaligned) {
+    const Plan p8 = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
+    const size_t l = lds_bytes(kVariants[find_variant(p8)].info, k);
+    if (l <= (size_t)40 * 1024 && l <= max_lds) return p8;
+    const Plan p16 = {1, 4, 16, 1, mbd::A_LDS_SHIFTED, kPolNT, 0, 1};
+    if (n >= 4096 && l <= (size_t)70 * 1024 && l <= max_lds) return p16;
   }
   // 2. 8 waves per row per workgroup, Q groups, about 2048 waves in all (more
   // k-groups cost more than they bring on MI355X), keeping at least two
@@ -190,14 +202,10 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     if (Q * n <= (int64_t)kWsFloats && Q > 1) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
   // 3.
-  if (k % 8 != 0 || !b_aligned) {
-    Plan p = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 0, 1};
-    if (lds_bytes(kVariants[find_variant(p)].info, k) > max_lds) p.a_mode = mbd::A_CACHED;
-    return p;
-  }
+  if (misaligned && n >= 2048) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.
   const int64_t nfull = k / mbd::kStep;
-  const int R = (n >= 4096 && k >= 6144) ? 2 : 1;
+  const int R = (n >= 1024 && k >= 6144) ? 2 : 1;
   // a row of at most 8 steps: one wave takes all of it, in one batch for
   // fp16; bf16's widening costs twice the vector work of fp16's mixed FMA,
   // and two batches of 4 steps measure ~2% faster there

@@ -409,10 +409,32 @@ def test_realigned_rows_do_not_leak(g, dtype):
 
 
 def test_auto_plan_realigns_misaligned_rows(g):
-    for n, k in [(18433, 7169), (100, 1000)]:
+    """Misaligned rows: the realigning kernel while its LDS leaves 32 waves
+    per CU (8 waves per workgroup up to 40 KiB, 16 up to 64 KiB), then
+    unaligned loads (two rows per one-wave workgroup for n >= 4096)."""
+    for n, k, want in [(18433, 7169, (2, 8)), (8192, 12289, (2, 16)), (8192, 16383, (1, 1)),
+                       (100, 1000, (1, None))]:
         v, grid, q = g.query_config(n, k, BF16)
         info = mbd.gemv_variant_info(v)[1]
-        assert info.a_mode == (2 if k % 8 else 1), (n, k, v)
+        assert info.a_mode == want[0], (n, k, v)
+        if want[1] is not None:
+            assert info.waves == want[1], (n, k, v)
+        if k == 16383:
+            assert info.rows == 2 and info.splits == 1, (n, k, v)
+
+
+@pytest.mark.parametrize("n,k,dtype,shift", [(4096, 12289, BF16, 3), (4096, 16001, F16, 1),
+                                             (1000, 16383, BF16, 5)],
+                         ids=["4096x12289_bf16", "4096x16001_f16", "1000x16383_bf16"])
+def test_auto_plan_long_misaligned_rows(g, n, k, dtype, shift):
+    """Each tier of the automatic plan for misaligned rows against the full
+    oracle, with B's base pointer off 16-byte alignment as well."""
+    B, a = random_inputs(n, k, dtype, seed=n + k)
+    ref, _, ab = oracle.gemv(dtype, B, a)
+    Bbig = to_device(np.concatenate([np.zeros(shift, np.uint16), B.ravel()]), dtype)
+    Bd = Bbig[shift:].view(n, k)
+    got = run(g, Bd, to_device(a, dtype))
+    _check(dtype, got, ref, ab, k, -1, "auto %dx%d shift %d" % (n, k, shift))
 
 
 def run_ex(g, Bd, ad, alpha, bias, variant=-1, c=None):
