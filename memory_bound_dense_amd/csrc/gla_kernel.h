@@ -56,6 +56,31 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
   const __amdgpu_buffer_rsrc_t sout_r =
       make_rsrc(S_out + rowbase * dv, (uint32_t)dk * (uint32_t)dv * 4u);
 
+  // ROWS rows per trip, their loads issued together, and the next trip's
+  // loads issued before this trip's update (a lane only ever rewrites the 16
+  // bytes it has itself read, so this is safe in place too).  The first
+  // trip's loads, and v, are issued before the staging below, so their
+  // latency overlaps it.  Rows past dk load from outside the descriptor's
+  // range (zeros, no memory access) and are not stored.  LPOL / SPOL:
+  // cache-policy bits of the state loads / stores.
+  constexpr int kRows = ROWS;
+  constexpr int kTrip = kRows * RG;
+  auto load_trip = [&](int i0, u32x4 (&sv)[kRows]) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int i = i0 + r * RG;
+      const uint32_t off = i < dk ? ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u : kOffsetOutOfRange;
+      sv[r] = __builtin_amdgcn_raw_buffer_load_b128(sin_r, off, 0u, LPOL);
+    }
+  };
+  u32x4 cur[kRows];
+  float vj[4] = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    load_trip(rg, cur);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vj[c] = widen<DT>(v[head * dv + j0 + c]);
+  }
+
   extern __shared__ float gla_rows[];        // STAGE: e[0..dk), k[dk..2dk), q[2dk..3dk)
   if constexpr (STAGE) {
     for (int i = t; i < dk; i += kGlaThreads) {
@@ -66,27 +91,17 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
     __syncthreads();
   }
 
-  float vj[4] = {0.f, 0.f, 0.f, 0.f};
-  if (active) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) vj[c] = widen<DT>(v[head * dv + j0 + c]);
-  }
   float oacc[4] = {0.f, 0.f, 0.f, 0.f};
-
-  // ROWS rows per trip: their loads are issued together (a lane only ever
-  // rewrites the 16 bytes it has just read, so this is safe in place too).
-  // LPOL / SPOL: cache-policy bits of the state loads / stores.
-  constexpr int kRows = ROWS;
   if (active) {
-    for (int i0 = rg; i0 < dk; i0 += kRows * RG) {
-      u32x4 sv[kRows];
+    for (int i0 = rg; i0 < dk; i0 += kTrip) {
+      u32x4 nxt[kRows];
+      const bool more = i0 + kTrip < dk;
+      if (more) load_trip(i0 + kTrip, nxt);
       float e[kRows], ki[kRows], qi[kRows];
 #pragma unroll
       for (int r = 0; r < kRows; ++r) {
         const int i = i0 + r * RG;
         if (i < dk) {
-          sv[r] = __builtin_amdgcn_raw_buffer_load_b128(
-              sin_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, LPOL);
           if constexpr (STAGE) {
             e[r] = gla_rows[i];
             ki[r] = gla_rows[dk + i];
@@ -105,7 +120,7 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
           u32x4 nv;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const uint32_t w = sv[r][c];
+            const uint32_t w = cur[r][c];
             const float sn = __builtin_fmaf(ki[r], vj[c], e[r] * __builtin_bit_cast(float, w));
             nv[c] = __builtin_bit_cast(uint32_t, sn);
             oacc[c] = __builtin_fmaf(qi[r], sn, oacc[c]);
@@ -113,6 +128,10 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
           __builtin_amdgcn_raw_buffer_store_b128(
               nv, sout_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, SPOL);
         }
+      }
+      if (more) {
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) cur[r] = nxt[r];
       }
     }
   }
