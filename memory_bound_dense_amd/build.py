@@ -32,6 +32,8 @@ def _hipcc_shared(sources, out, verbose):
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # the first 16 dwords of kernel arguments arrive in SGPRs at wave launch
+           "-mllvm", "-amdgpu-kernarg-preload-count=16",
            "-I", INCLUDE, "-I", CSRC] + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -19,7 +19,8 @@ using mbd_host::kPolNT;
 
 namespace {
 
-using KernelFn = void (*)(mbd::GemvArgs);
+using KernelFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, int, int, int, int, int, int,
+                          int, float, const uint16_t*, float*, unsigned*);
 
 struct Variant {
   gemv_variant_info_t info;
@@ -496,7 +497,11 @@ extern "C" gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void*
   const int64_t nsl = (int64_t)vi.splits * L.kgroups;
   p.slice_q = (int)(nfull / nsl);
   p.slice_r = (int)(nfull % nsl);
-  void* args[] = {(void*)&p};
+  // in the order of the kernels' parameters (MBD_GEMV_PARAMS)
+  void* args[] = {(void*)&p.B,       (void*)&p.a,       (void*)&p.c,       (void*)&p.n,
+                  (void*)&p.k,       (void*)&p.flags,   (void*)&p.rows_q,  (void*)&p.rows_r,
+                  (void*)&p.slice_q, (void*)&p.slice_r, (void*)&p.alpha,   (void*)&p.bias,
+                  (void*)&p.ws,      (void*)&p.cnt};
   hipError_t e = hipLaunchKernel((const void*)var.fn[dtype], dim3((unsigned)L.grid, (unsigned)L.kgroups),
                                  dim3((unsigned)(var.info.waves * mbd::kLanes)), args, L.lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));

@@ -79,7 +79,8 @@ __device__ __forceinline__ void staged_issue(StagedRegs<R, U, P>& regs, uint8_t*
 }
 
 template <int DT, int R, int U, int WAVES, int P, bool VIA_LDS, int BPOL>
-__global__ __launch_bounds__(WAVES * kLanes) void gemv_staged_kernel(const GemvArgs p) {
+__global__ __launch_bounds__(WAVES * kLanes) void gemv_staged_kernel(MBD_GEMV_PARAMS) {
+  MBD_GEMV_ARGS;
   static_assert(P >= 1 && P <= 3, "pipeline depth 1..3");
   static_assert((P - 1) * U * R <= 63, "the slot wait must fit vmcnt");
   const uint16_t* __restrict__ B = p.B;

@@ -53,8 +53,8 @@ namespace {
 // Heads of at most this many rows stage exp(gk), k and q in LDS (6 KiB).
 constexpr int64_t kGlaStageRows = 512;
 
-using GlaFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
-                       const float*, float*, uint16_t*, int, int, float, int);
+using GlaFn = void (*)(const float*, float*, int, int, int, const uint16_t*, const uint16_t*,
+                       const uint16_t*, const uint16_t*, uint16_t*, float);
 
 }  // namespace
 
@@ -102,8 +102,8 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
                  *gp = (const uint16_t*)gk;
   uint16_t* op = (uint16_t*)o;
   int dki = (int)dk, dvi = (int)dv;
-  void* args[] = {(void*)&qp, (void*)&kp,  (void*)&vp,  (void*)&gp,    (void*)&S_in, (void*)&S_out,
-                  (void*)&op, (void*)&dki, (void*)&dvi, (void*)&scale, (void*)&nblk};
+  void* args[] = {(void*)&S_in, (void*)&S_out, (void*)&dki, (void*)&dvi, (void*)&nblk, (void*)&vp,
+                  (void*)&gp,   (void*)&kp,    (void*)&qp,  (void*)&op,  (void*)&scale};
   hipError_t e = hipLaunchKernel((const void*)fns[dtype][stage][sel], dim3((unsigned)grid),
                                  dim3(mbd::kGlaThreads), args, lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));

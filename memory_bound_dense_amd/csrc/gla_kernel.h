@@ -34,10 +34,12 @@ constexpr int kGlaThreads = 256;
 // -- by every lane of a row group for every row; the host picks it when the
 // head is short enough for that LDS to stay small.
 template <int DT, int LPR, int ROWS = 4, int LPOL = 0, int SPOL = 0, bool STAGE = false>
+// Parameters in the order a workgroup needs them (the first 14 dwords are
+// preloaded into SGPRs at wave launch).
 __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ gk, const float* S_in,
-    float* S_out, uint16_t* __restrict__ o, int dk, int dv, float scale, int nblk) {
+    const float* S_in, float* S_out, int dk, int dv, int nblk, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ gk, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, float scale) {
   constexpr int CW = 4 * LPR;                 // columns per block
   constexpr int RG = kGlaThreads / LPR;       // row groups
   __shared__ float part[RG][CW];
