@@ -167,8 +167,10 @@ int find_variant(const Plan& p) {
 //     workgroups per CU), and, for n >= 4096, with 16 waves per workgroup
 //     (one row each, 2 workgroups per CU) while it is <= 70 KiB (k ~ 15.8K;
 //     measured: ahead by 9% at k = 14337, behind by 7% at k = 16383);
-//  2. too few rows to give the GPU 4096 waves even with 16 waves per row:
-//     k split across workgroups as well (cross-workgroup variants);
+//  2. too few rows to give the GPU 2048 waves even with 16 waves per row
+//     (n < 128): k split across workgroups as well (cross-workgroup
+//     variants; measured best for n = 32 and 64, 22-43% behind the
+//     in-workgroup split for n = 128 and 200);
 //  3. misaligned rows longer than that: unaligned 16-byte loads, two rows
 //     per one-wave workgroup when n >= 2048, otherwise the plan of 4.
 //     (Measured on MI355X over misaligned shapes with k from 4097 to 65537:
@@ -195,7 +197,7 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // 2. 8 waves per row per workgroup, Q groups, about 2048 waves in all (more
   // k-groups cost more than they bring on MI355X), keeping at least two
   // 512-element steps per wave.
-  if (n * 16 < 4096 && nfull0 >= 2 * 8 * 2) {
+  if (n * 16 < 2048 && nfull0 >= 2 * 8 * 2) {
     int64_t Q = (2048 + n * 8 - 1) / (n * 8);
     const int64_t qmax = nfull0 / (2 * 8);
     if (Q > qmax) Q = qmax;
