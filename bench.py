@@ -46,9 +46,9 @@ def kernel_source_hash():
     return ksh()
 
 
-def read_traffic(workload, n_launch_bytes):
+def read_traffic(workload, n_launch_bytes, plan):
     """HBM traffic per launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and the same plan; else None."""
     path = os.path.join(ROOT, "profiles", "%s.counters.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -57,7 +57,7 @@ def read_traffic(workload, n_launch_bytes):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash() or kv.get("plan") != plan:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -345,7 +345,8 @@ def main():
     if ceiling:
         log("[bench] streaming-read probe over the same bytes: %.2f us -> %.1f GB/s" % (
             ceiling["us"], ceiling["gbs"]))
-    traffic = read_traffic(name, step_bytes)
+    from memory_bound_dense_amd.profile_counters import plan_signature
+    traffic = read_traffic(name, step_bytes, plan_signature(variant, grid, kgroups))
     out = {
         "metric": METRIC,
         "value": round(value, 2),

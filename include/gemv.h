@@ -205,6 +205,20 @@ gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t* cfg);
 gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k, gemv_dtype_t dtype,
                                 gemv_config_t* out);
 
+/* The configuration the automatic plan picks for (n, k, dtype), worked out on
+ * the host alone -- no handle, no device, no HIP call -- for a device whose
+ * per-workgroup LDS limit is `max_lds` bytes (163840 on MI355X) and a B that
+ * is (b_aligned != 0) or is not 16-byte aligned.  It is the rule gemv_run
+ * applies (TileLang Case Studies, Case B.4: the choice is fixed host logic,
+ * not per-call tuning), so tools and CPU tests can inspect it; on a real
+ * handle gemv_query_config gives the same answer (it also checks the LDS the
+ * kernels declare statically).  grid is the number of workgroups launched.
+ * Errors: GEMV_ERR_INVALID_ARG (out NULL, n <= 0, k < 0, sizes above the
+ * limits, max_lds <= 0), GEMV_ERR_UNSUPPORTED_DTYPE, GEMV_ERR_UNSUPPORTED (no
+ * compiled variant fits). */
+gemv_status_t gemv_plan_config(int64_t n, int64_t k, gemv_dtype_t dtype, int32_t b_aligned,
+                               int64_t max_lds, gemv_config_t* out);
+
 #ifdef __cplusplus
 }
 #endif

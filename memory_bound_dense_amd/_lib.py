@@ -37,7 +37,8 @@ GEMV_MAX_K = 134217728
 # every symbol include/gemv.h and include/gla_decode.h declare
 EXPORTS = ("gemv_create", "gemv_run", "gemv_run_ex", "gemv_destroy", "gemv_status_string",
            "gemv_check_args", "gemv_check_args_ex", "gemv_num_variants", "gemv_variant_info",
-           "gemv_force_config", "gemv_query_config", "gla_decode_step", "gla_check_args")
+           "gemv_force_config", "gemv_query_config", "gemv_plan_config", "gla_decode_step",
+           "gla_check_args")
 
 
 class GemvError(RuntimeError):
@@ -101,6 +102,8 @@ def load():
     lib.gemv_force_config.restype = st
     lib.gemv_query_config.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.POINTER(gemv_config_t)]
     lib.gemv_query_config.restype = st
+    lib.gemv_plan_config.argtypes = [i64, i64, ctypes.c_int, i32, i64, ctypes.POINTER(gemv_config_t)]
+    lib.gemv_plan_config.restype = st
     lib.gla_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
                                     ctypes.c_int, vp]
     lib.gla_decode_step.restype = st
@@ -169,6 +172,13 @@ def gemv_force_config(h, variant=-1, grid=0, kgroups=0, flags=0):
 def gemv_query_config(h, n, k, dtype):
     cfg = gemv_config_t()
     s = load().gemv_query_config(h, n, k, dtype, ctypes.byref(cfg))
+    return s, cfg
+
+
+def gemv_plan_config(n, k, dtype, b_aligned=1, max_lds=160 * 1024):
+    """The automatic plan for a shape, on the host alone (no device)."""
+    cfg = gemv_config_t()
+    s = load().gemv_plan_config(n, k, dtype, int(b_aligned), max_lds, ctypes.byref(cfg))
     return s, cfg
 
 

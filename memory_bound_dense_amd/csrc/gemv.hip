@@ -298,23 +298,11 @@ struct Launch {
 };
 static_assert(GEMV_FLAG_XCD_CONTIGUOUS == mbd::kFlagXcdContiguous, "flag values agree");
 
-static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_dtype_t dtype,
-                             bool b_aligned, Launch* L) {
-  int v;
-  int64_t g, q;
-  int flags = 0;
-  if (h->forced.variant >= 0) {
-    v = h->forced.variant;
-    g = h->forced.grid;
-    q = h->forced.kgroups;
-    flags = h->forced.flags;
-  } else {
-    const Plan p = auto_plan(n, k, dtype, h->max_lds, b_aligned);
-    v = find_variant(p);
-    if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
-    g = p.grid;
-    q = p.kgroups;
-  }
+// The shape-dependent part of a launch: validate a variant, grid and
+// k-group count against (n, k) and fill in the grid actually launched and
+// the dynamic LDS.  Needs no device.
+static gemv_status_t shape_launch(int v, int64_t g, int64_t q, int flags, int64_t n, int64_t k,
+                                  bool b_aligned, Launch* L) {
   const gemv_variant_info_t& info = kVariants[v].info;
   // the pipelined variants load whole 16-byte granules of aligned rows only
   if (info.stages > 0 && k > 0 && (k % 8 != 0 || !b_aligned)) return GEMV_ERR_UNSUPPORTED;
@@ -336,14 +324,54 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_
     if (q > 1) return GEMV_ERR_INVALID_ARG;
     q = 1;
   }
-  const size_t l = lds_bytes(info, k);
-  const size_t st = h->static_lds[v][0] > h->static_lds[v][1] ? h->static_lds[v][0] : h->static_lds[v][1];
-  if (l + st > h->max_lds) return GEMV_ERR_UNSUPPORTED;
   L->variant = v;
   L->grid = (int)g;
   L->kgroups = (int)q;
   L->flags = flags;
-  L->lds = l;
+  L->lds = lds_bytes(info, k);
+  return GEMV_OK;
+}
+
+static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_dtype_t dtype,
+                             bool b_aligned, Launch* L) {
+  int v;
+  int64_t g, q;
+  int flags = 0;
+  if (h->forced.variant >= 0) {
+    v = h->forced.variant;
+    g = h->forced.grid;
+    q = h->forced.kgroups;
+    flags = h->forced.flags;
+  } else {
+    const Plan p = auto_plan(n, k, dtype, h->max_lds, b_aligned);
+    v = find_variant(p);
+    if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
+    g = p.grid;
+    q = p.kgroups;
+  }
+  gemv_status_t s = shape_launch(v, g, q, flags, n, k, b_aligned, L);
+  if (s != GEMV_OK) return s;
+  const size_t st = h->static_lds[v][0] > h->static_lds[v][1] ? h->static_lds[v][0] : h->static_lds[v][1];
+  if (L->lds + st > h->max_lds) return GEMV_ERR_UNSUPPORTED;
+  return GEMV_OK;
+}
+
+extern "C" gemv_status_t gemv_plan_config(int64_t n, int64_t k, gemv_dtype_t dtype, int32_t b_aligned,
+                                          int64_t max_lds, gemv_config_t* out) {
+  if (!out) return GEMV_ERR_INVALID_ARG;
+  if (dtype != GEMV_F16 && dtype != GEMV_BF16) return GEMV_ERR_UNSUPPORTED_DTYPE;
+  if (n <= 0 || k < 0 || n > GEMV_MAX_N || k > GEMV_MAX_K || max_lds <= 0) return GEMV_ERR_INVALID_ARG;
+  const Plan p = auto_plan(n, k, dtype, (size_t)max_lds, b_aligned != 0);
+  const int v = find_variant(p);
+  if (v < 0) return GEMV_ERR_UNSUPPORTED;
+  Launch L;
+  gemv_status_t s = shape_launch(v, p.grid, p.kgroups, 0, n, k, b_aligned != 0, &L);
+  if (s != GEMV_OK) return s;
+  if (L.lds > (size_t)max_lds) return GEMV_ERR_UNSUPPORTED;
+  out->variant = L.variant;
+  out->grid = L.grid;
+  out->kgroups = L.kgroups;
+  out->flags = L.flags;
   return GEMV_OK;
 }
 

@@ -32,7 +32,10 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemv_kernel.h", "gemv_staged.h", "gemv.hip", "handle.h")]
+# the GEMV device code and the flags it is compiled with; which kernel a
+# workload runs (the plan) is recorded and checked separately
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemv_kernel.h", "gemv_staged.h")] + \
+    [os.path.join(PKG, "build.py")]
 GEMV_KERNEL = "gemv_"              # every GEMV kernel (row, realigning, row-per-lane)
 COPY_KERNEL = "copyBuffer"
 
@@ -46,13 +49,33 @@ def _strip_comments(text):
 
 
 def kernel_source_hash():
-    """Hash of the GEMV sources (kernels, variant table, plan rule), blind to
-    comments and whitespace: a summary taken on other code is not reused."""
+    """Hash of the GEMV device code and its build flags, blind to comments and
+    whitespace: a summary taken on other code is not reused."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(p) as f:
             h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def plan_signature(variant, grid, kgroups):
+    """The kernel a launch runs, by shape rather than by table index."""
+    sys.path.insert(0, ROOT)
+    import memory_bound_dense_amd as mbd
+    i = mbd.gemv_variant_info(variant)[1]
+    return "R%d U%d W%d S%d a%d p%d x%d l%d st%d lds%d grid %d kgroups %d" % (
+        i.rows, i.unroll, i.waves, i.splits, i.a_mode, i.b_policy, i.cross_wg, i.layout, i.stages,
+        i.b_lds, grid, kgroups)
+
+
+def workload_plan_signature(n, k, dtype):
+    """The automatic plan of a workload (host rule, 16-byte aligned B)."""
+    sys.path.insert(0, ROOT)
+    import memory_bound_dense_amd as mbd
+    s, cfg = mbd.gemv_plan_config(n, k, dtype, 1, 160 * 1024)
+    if s != mbd.GEMV_OK:
+        raise RuntimeError(mbd.gemv_status_string(s))
+    return plan_signature(cfg.variant, cfg.grid, cfg.kgroups)
 
 
 # ---- programs ----------------------------------------------------------------
@@ -166,6 +189,7 @@ def summarize_counters(workload, fetch, write, copy_fetch, copy_write, copy_byte
         "commands:",
     ] + ["  " + c for c in commands] + [
         "kernel_source_sha256_16: %s" % kernel_source_hash(),
+        "plan: %s" % workload_plan_signature(n, k, dtype),
         "copy_kernel_bytes: %d" % copy_bytes,
         "copy_fetch_counted_bytes: %.0f" % f_c,
         "copy_write_counted_bytes: %.0f" % w_c,

@@ -376,6 +376,18 @@ def test_query_config_many_shapes(g):
                 assert 0 <= v < NV and grid >= 1 and q >= 1, (n, k, dtype)
 
 
+def test_query_config_matches_the_host_plan(g):
+    """The handle's plan is the host-only rule of gemv_plan_config (the
+    device's per-workgroup LDS limit is 160 KiB)."""
+    for n in (1, 64, 127, 128, 1000, 2048, 4096, 18432, 18433):
+        for k in (1, 512, 7168, 7169, 12289, 16383, 65536):
+            for dtype in (F16, BF16):
+                v, grid, q = g.query_config(n, k, dtype)
+                s, cfg = mbd.gemv_plan_config(n, k, dtype, 1, 160 * 1024)
+                assert s == mbd.GEMV_OK
+                assert (v, grid, q) == (cfg.variant, cfg.grid, cfg.kgroups), (n, k, dtype)
+
+
 REALIGN = [v for v in VARIANTS if mbd.gemv_variant_info(v)[1].a_mode == 2]
 
 

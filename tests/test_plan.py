@@ -1,0 +1,154 @@
+"""The automatic plan without a GPU (gemv_plan_config: the rule gemv_run
+applies, worked out on the host).
+
+* the plan of every configured workload, as measured best on MI355X with the
+  tuner (a change to the rule shows up here first);
+* the tiers for rows off 16-byte boundaries and for few rows;
+* properties over a wide sweep of shapes: a valid, compiled, non-ablation
+  variant whose LDS fits, and bad arguments rejected with the documented
+  status.
+"""
+import itertools
+
+import pytest
+
+import memory_bound_dense_amd as mbd
+from memory_bound_dense_amd import _lib
+from gemv_inputs import ALL_WORKLOADS, BF16, EXTRA_WORKLOADS, F16
+
+MAX_LDS = 160 * 1024          # bytes of LDS per workgroup on MI355X
+
+
+def plan(n, k, dtype, aligned=True):
+    s, cfg = mbd.gemv_plan_config(n, k, dtype, 1 if aligned else 0, MAX_LDS)
+    assert s == mbd.GEMV_OK, (n, k, dtype, aligned, mbd.gemv_status_string(s))
+    info = mbd.gemv_variant_info(cfg.variant)[1]
+    return cfg, info
+
+
+def shape_of(info):
+    return (info.rows, info.unroll, info.waves, info.splits, info.a_mode, info.cross_wg)
+
+
+# (rows, unroll, waves, splits, a_mode, cross_wg) per configured workload;
+# a_mode 1 = a through the caches, 2 = the realigning kernel's shifted LDS copies
+WORKLOAD_PLANS = {
+    "tiny_256x512_f16": (1, 8, 4, 1, 1, 0),
+    "gemv_18432x7168_f16": (2, 4, 8, 4, 1, 0),
+    "gemv_7168x16384_bf16": (2, 4, 8, 8, 1, 0),
+    "sweep_4096x4096_f16": (1, 8, 4, 1, 1, 0),
+    "sweep_4096x4096_bf16": (1, 4, 4, 1, 1, 0),
+    "sweep_11008x4096_f16": (1, 8, 4, 1, 1, 0),
+    "sweep_11008x4096_bf16": (1, 4, 4, 1, 1, 0),
+    "sweep_4096x11008_f16": (2, 4, 8, 8, 1, 0),
+    "sweep_4096x11008_bf16": (2, 4, 8, 8, 1, 0),
+    "sweep_14336x4096_f16": (1, 8, 4, 1, 1, 0),
+    "sweep_14336x4096_bf16": (1, 4, 4, 1, 1, 0),
+    "sweep_4096x14336_f16": (1, 4, 4, 1, 1, 0),
+    "sweep_4096x14336_bf16": (1, 4, 4, 1, 1, 0),
+    "ragged_64x65536_bf16": (1, 4, 8, 8, 1, 1),
+    "ragged_1000x7000_bf16": (1, 4, 8, 4, 1, 0),
+    "ragged_18433x7169_bf16": (1, 4, 8, 1, 2, 0),
+    "large_28672x8192_f16": (2, 4, 8, 4, 1, 0),
+    "large_28672x8192_bf16": (2, 4, 8, 4, 1, 0),
+    "large_57344x7168_f16": (2, 4, 8, 4, 1, 0),
+    "large_57344x7168_bf16": (2, 4, 8, 4, 1, 0),
+    "square_1024x1024_f16": (1, 8, 4, 1, 1, 0),
+}
+
+
+@pytest.mark.parametrize("wl", ALL_WORKLOADS + EXTRA_WORKLOADS, ids=lambda w: w[0])
+def test_plan_of_every_workload(wl):
+    name, n, k, dtype, _ = wl
+    cfg, info = plan(n, k, dtype)
+    assert shape_of(info) == WORKLOAD_PLANS[name], (name, shape_of(info))
+    assert cfg.grid >= 1 and cfg.kgroups >= 1
+
+
+def test_plan_grids_of_the_production_shapes():
+    # one trip per workgroup: 4 rows (2 row groups x 2 rows) per workgroup for
+    # the headline, 2 rows for (7168, 16384)
+    assert plan(18432, 7168, F16)[0].grid == 4608
+    assert plan(7168, 16384, BF16)[0].grid == 3584
+    # the measured entry for (4096, 14336): 512 workgroups, 2 rows per wave
+    assert plan(4096, 14336, F16)[0].grid == 512
+    # the realigning kernel's persistent grid
+    assert plan(18433, 7169, BF16)[0].grid == 1536
+    # 64 rows: k shared by 4 workgroups per row range
+    assert plan(64, 65536, BF16)[0].kgroups == 4
+
+
+@pytest.mark.parametrize("n,k,want", [
+    # realigning kernel, 8 waves per workgroup while its LDS <= 40 KiB
+    (18433, 7169, (1, 4, 8, 1, 2, 0)),
+    (14336, 4097, (1, 4, 8, 1, 2, 0)),
+    (3072, 7169, (1, 4, 8, 1, 2, 0)),
+    # 16 waves per workgroup (n >= 4096) while it is <= 70 KiB
+    (8192, 9217, (1, 4, 16, 1, 2, 0)),
+    (8192, 12289, (1, 4, 16, 1, 2, 0)),
+    (7169, 14337, (1, 4, 16, 1, 2, 0)),
+    # beyond: unaligned loads, two rows per one-wave workgroup (n >= 2048)
+    (8192, 16383, (2, 4, 1, 1, 1, 0)),
+    (7169, 16383, (2, 4, 1, 1, 1, 0)),
+    (3072, 12289, (2, 4, 1, 1, 1, 0)),
+    (2048, 32769, (2, 4, 1, 1, 1, 0)),
+    (2048, 65537, (2, 4, 1, 1, 1, 0)),
+    # fewer rows: the split plan of aligned rows (two rows per wave from 1024)
+    (1024, 16385, (2, 4, 8, 8, 1, 0)),
+    (1000, 16385, (1, 4, 8, 8, 1, 0)),
+])
+def test_plan_misaligned_tiers(n, k, want):
+    for dtype in (F16, BF16):
+        assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
+    # a B pointer off 16-byte alignment makes every row misaligned, whatever k
+    if k % 8 == 1:
+        assert shape_of(plan(n, k - 1, F16, aligned=False)[1])[4] in (1, 2)
+
+
+@pytest.mark.parametrize("n,k,xwg", [
+    (32, 131072, True), (64, 65536, True), (127, 65536, True),
+    (128, 32768, False), (200, 16384, False),
+    (64, 511, False), (64, 16383, False),       # too few full steps to share
+])
+def test_plan_cross_workgroup_only_for_few_rows(n, k, xwg):
+    cfg, info = plan(n, k, BF16)
+    assert bool(info.cross_wg) == xwg, (n, k, shape_of(info))
+    assert (cfg.kgroups > 1) == xwg
+
+
+def test_plan_properties_over_a_sweep():
+    ns = [1, 7, 63, 64, 127, 128, 255, 256, 1000, 1023, 1024, 2047, 2048, 4095, 4096, 7168, 18433,
+          100000]
+    ks = [0, 1, 7, 8, 9, 511, 512, 513, 4096, 6143, 6144, 7169, 9217, 12289, 16383, 16384, 65536,
+          65537, 200000]
+    for n, k, dtype, aligned in itertools.product(ns, ks, (F16, BF16), (True, False)):
+        cfg, info = plan(n, k, dtype, aligned)
+        assert 0 <= cfg.variant < mbd.gemv_num_variants()
+        assert cfg.grid >= 1 and cfg.kgroups >= 1
+        assert info.layout == 0 and info.stages == 0, "an ablation variant was chosen"
+        misaligned = k > 0 and (k % 8 != 0 or not aligned)
+        if info.a_mode == 2:
+            assert misaligned
+        if info.cross_wg:
+            assert n < 128
+        rows_per_block = info.rows * info.waves // info.splits
+        assert cfg.grid <= (n + rows_per_block - 1) // rows_per_block
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 8, 0, 1, MAX_LDS), _lib.GEMV_ERR_INVALID_ARG),
+    ((-1, 8, 0, 1, MAX_LDS), _lib.GEMV_ERR_INVALID_ARG),
+    ((4, -1, 0, 1, MAX_LDS), _lib.GEMV_ERR_INVALID_ARG),
+    ((4, 8, 2, 1, MAX_LDS), _lib.GEMV_ERR_UNSUPPORTED_DTYPE),
+    ((4, 8, 0, 1, 0), _lib.GEMV_ERR_INVALID_ARG),
+    ((2 ** 30 + 1, 8, 0, 1, MAX_LDS), _lib.GEMV_ERR_INVALID_ARG),
+    ((4, 2 ** 27 + 1, 0, 1, MAX_LDS), _lib.GEMV_ERR_INVALID_ARG),
+    ((4, 0, 0, 1, MAX_LDS), _lib.GEMV_OK),
+])
+def test_plan_rejects_bad_arguments(args, expect):
+    assert mbd.gemv_plan_config(*args)[0] == expect
+
+
+def test_plan_null_output():
+    lib = _lib.load()
+    assert lib.gemv_plan_config(4, 8, 0, 1, MAX_LDS, None) == _lib.GEMV_ERR_INVALID_ARG
