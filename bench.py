@@ -242,7 +242,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the kernel on one GPU's share); "
+        print("bench.py: measures one GPU (the kernel on one GPU's share of the rows); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
