@@ -200,6 +200,8 @@ def summarize_counters(workload, fetch, write, copy_fetch, copy_write, copy_byte
         "algorithmic_bytes_per_launch: %d" % alg,
         "hbm_bytes_per_launch: %.0f" % traffic,
         "traffic_over_algorithmic: %.4f" % (traffic / alg),
+        "hbm_bytes_per_output: %.1f" % (traffic / n),
+        "algorithmic_bytes_per_output: %.1f" % (alg / n),
     ]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
