@@ -181,8 +181,12 @@ int find_variant(const Plan& p) {
 //     most 8 steps goes to one wave; longer rows are split along k inside a
 //     workgroup until every wave has at most 4 steps (one batch of loads:
 //     measured best on MI355X), further (down to two steps per slice) while
-//     the grid has fewer than 4096 waves.  (Two rows per wave measured 2-12%
-//     faster than one for n = 1024..3072 and k = 8K..64K.)
+//     the grid has fewer than 4096 waves.  Two exceptions: rows of >= 96
+//     steps with n >= 1536 are not split (two rows per one-wave workgroup),
+//     and up to 768 rows of 9..16 steps take four slices in four-wave
+//     workgroups.  (A tuner sweep over n = 256..3072, k = 4096..65536 on
+//     MI355X: this rule is within 1.7% of the best compiled plan on average,
+//     12% at worst; without the two exceptions 2.8% and 12.6%.)
 Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned) {
   const int64_t nfull0 = k / mbd::kStep;
   const bool misaligned = k > 0 && (k % 8 != 0 || !b_aligned);
@@ -208,12 +212,17 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   if (misaligned && n >= 2048) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.
   const int64_t nfull = k / mbd::kStep;
+  // very long rows (k >= 48K) and enough of them: no split, two rows per
+  // one-wave workgroup (the split's per-slice combine no longer pays)
+  if (nfull >= 96 && n >= 1536) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   const int R = (n >= 1024 && k >= 6144) ? 2 : 1;
   // a row of at most 8 steps: one wave takes all of it, in one batch for
   // fp16; bf16's widening costs twice the vector work of fp16's mixed FMA,
   // and two batches of 4 steps measure ~2% faster there
   if (R == 1 && nfull <= 8)
     return Plan{1, dtype == GEMV_F16 ? 8 : 4, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
+  // up to 16 steps and at most 768 rows: four slices in four-wave workgroups
+  if (R == 1 && nfull <= 16 && n <= 768) return Plan{1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
   const int smax = R == 1 ? 16 : 8;
   int S = 1;
   while (S < smax && (nfull + S - 1) / S > 4) S *= 2;   // at most 4 steps per wave: one batch

@@ -105,6 +105,20 @@ def test_plan_misaligned_tiers(n, k, want):
         assert shape_of(plan(n, k - 1, F16, aligned=False)[1])[4] in (1, 2)
 
 
+@pytest.mark.parametrize("n,k,want", [
+    (18432, 7168, (2, 4, 8, 4, 1, 0)),     # the headline: two rows, four slices
+    (3072, 65536, (2, 4, 1, 1, 1, 0)),     # >= 96 steps, n >= 1536: no split
+    (1536, 49152, (2, 4, 1, 1, 1, 0)),
+    (1024, 65536, (2, 4, 8, 8, 1, 0)),     # fewer rows: still split
+    (768, 8192, (1, 4, 4, 4, 1, 0)),       # <= 768 rows of 9..16 steps: 4 slices, 4 waves
+    (256, 5120, (1, 4, 4, 4, 1, 0)),
+    (1000, 8192, (1, 4, 8, 8, 1, 0)),      # more rows: the general split
+    (768, 4096, (1, 8, 4, 1, 1, 0)),       # <= 8 steps: one wave per row
+])
+def test_plan_aligned_rules(n, k, want):
+    assert shape_of(plan(n, k, F16)[1]) == want, (n, k)
+
+
 @pytest.mark.parametrize("n,k,xwg", [
     (32, 131072, True), (64, 65536, True), (127, 65536, True),
     (128, 32768, False), (200, 16384, False),
