@@ -34,7 +34,7 @@ def shape_of(info):
 # a_mode 1 = a through the caches, 2 = the realigning kernel's shifted LDS copies
 WORKLOAD_PLANS = {
     "tiny_256x512_f16": (1, 8, 4, 1, 1, 0),
-    "gemv_18432x7168_f16": (2, 4, 8, 4, 1, 0),
+    "gemv_18432x7168_f16": (2, 4, 4, 4, 1, 0),
     "gemv_7168x16384_bf16": (2, 4, 8, 8, 1, 0),
     "sweep_4096x4096_f16": (1, 8, 4, 1, 1, 0),
     "sweep_4096x4096_bf16": (1, 4, 4, 1, 1, 0),
@@ -49,10 +49,10 @@ WORKLOAD_PLANS = {
     "ragged_64x65536_bf16": (1, 4, 8, 8, 1, 1),
     "ragged_1000x7000_bf16": (1, 4, 8, 4, 1, 0),
     "ragged_18433x7169_bf16": (1, 4, 8, 1, 2, 0),
-    "large_28672x8192_f16": (2, 4, 8, 4, 1, 0),
-    "large_28672x8192_bf16": (2, 4, 8, 4, 1, 0),
-    "large_57344x7168_f16": (2, 4, 8, 4, 1, 0),
-    "large_57344x7168_bf16": (2, 4, 8, 4, 1, 0),
+    "large_28672x8192_f16": (2, 4, 4, 4, 1, 0),
+    "large_28672x8192_bf16": (2, 4, 4, 4, 1, 0),
+    "large_57344x7168_f16": (2, 4, 4, 4, 1, 0),
+    "large_57344x7168_bf16": (2, 4, 4, 4, 1, 0),
     "square_1024x1024_f16": (1, 8, 4, 1, 1, 0),
 }
 
@@ -66,9 +66,9 @@ def test_plan_of_every_workload(wl):
 
 
 def test_plan_grids_of_the_production_shapes():
-    # one trip per workgroup: 4 rows (2 row groups x 2 rows) per workgroup for
-    # the headline, 2 rows for (7168, 16384)
-    assert plan(18432, 7168, F16)[0].grid == 4608
+    # one trip per workgroup: 2 rows (one row group of 4 k-slices) per
+    # workgroup for the headline, 2 rows (8 k-slices) for (7168, 16384)
+    assert plan(18432, 7168, F16)[0].grid == 9216
     assert plan(7168, 16384, BF16)[0].grid == 3584
     # the measured entry for (4096, 14336): 512 workgroups, 2 rows per wave
     assert plan(4096, 14336, F16)[0].grid == 512
@@ -106,7 +106,7 @@ def test_plan_misaligned_tiers(n, k, want):
 
 
 @pytest.mark.parametrize("n,k,want", [
-    (18432, 7168, (2, 4, 8, 4, 1, 0)),     # the headline: two rows, four slices
+    (18432, 7168, (2, 4, 4, 4, 1, 0)),     # the headline: two rows, four slices, 4 waves
     (3072, 65536, (2, 4, 1, 1, 1, 0)),     # >= 96 steps, n >= 1536: no split
     (1536, 49152, (2, 4, 1, 1, 1, 0)),
     (1024, 65536, (2, 4, 8, 8, 1, 0)),     # fewer rows: still split
