@@ -218,11 +218,12 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // one-wave workgroup (the split's per-slice combine no longer pays)
   if (nfull >= 96 && n >= 1536) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   const int R = (n >= 1024 && k >= 6144) ? 2 : 1;
-  // a row of at most 8 steps: one wave takes all of it, in one batch for
-  // fp16; bf16's widening costs twice the vector work of fp16's mixed FMA,
-  // and two batches of 4 steps measure ~2% faster there
+  // a row of at most 8 steps: one wave takes all of it, in one batch; for
+  // bf16 below 4096 rows two batches of 4 steps (bf16's widening costs twice
+  // the vector work of fp16's mixed FMA; measured on MI355X: one batch is
+  // 2-3.4% faster from 4096 rows up, two are up to 2% faster below)
   if (R == 1 && nfull <= 8)
-    return Plan{1, dtype == GEMV_F16 ? 8 : 4, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
+    return Plan{1, (dtype == GEMV_F16 || n >= 4096) ? 8 : 4, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // up to 16 steps and at most 768 rows: four slices in four-wave workgroups
   if (R == 1 && nfull <= 16 && n <= 768) return Plan{1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
   const int smax = R == 1 ? 16 : 8;

@@ -37,13 +37,13 @@ WORKLOAD_PLANS = {
     "gemv_18432x7168_f16": (2, 4, 4, 4, 1, 0),
     "gemv_7168x16384_bf16": (2, 4, 8, 8, 1, 0),
     "sweep_4096x4096_f16": (1, 8, 4, 1, 1, 0),
-    "sweep_4096x4096_bf16": (1, 4, 4, 1, 1, 0),
+    "sweep_4096x4096_bf16": (1, 8, 4, 1, 1, 0),
     "sweep_11008x4096_f16": (1, 8, 4, 1, 1, 0),
-    "sweep_11008x4096_bf16": (1, 4, 4, 1, 1, 0),
+    "sweep_11008x4096_bf16": (1, 8, 4, 1, 1, 0),
     "sweep_4096x11008_f16": (2, 4, 8, 8, 1, 0),
     "sweep_4096x11008_bf16": (2, 4, 8, 8, 1, 0),
     "sweep_14336x4096_f16": (1, 8, 4, 1, 1, 0),
-    "sweep_14336x4096_bf16": (1, 4, 4, 1, 1, 0),
+    "sweep_14336x4096_bf16": (1, 8, 4, 1, 1, 0),
     "sweep_4096x14336_f16": (1, 4, 4, 1, 1, 0),
     "sweep_4096x14336_bf16": (1, 4, 4, 1, 1, 0),
     "ragged_64x65536_bf16": (1, 4, 8, 8, 1, 1),
@@ -117,6 +117,14 @@ def test_plan_misaligned_tiers(n, k, want):
 ])
 def test_plan_aligned_rules(n, k, want):
     assert shape_of(plan(n, k, F16)[1]) == want, (n, k)
+
+
+@pytest.mark.parametrize("n,k,want", [
+    (4096, 4096, (1, 8, 4, 1, 1, 0)),      # bf16, <= 8 steps, n >= 4096: one batch of 8
+    (2048, 4096, (1, 4, 4, 1, 1, 0)),      # below 4096 rows: two batches of 4
+])
+def test_plan_bf16_short_rows(n, k, want):
+    assert shape_of(plan(n, k, BF16)[1]) == want, (n, k)
 
 
 @pytest.mark.parametrize("n,k,xwg", [
