@@ -162,22 +162,34 @@ int find_variant(const Plan& p) {
 
 // The general rule, for shapes without a measured entry, in this order:
 //  1. rows that do not start on 16-byte boundaries (k % 8 != 0, or B itself
-//     misaligned), as long as the realigning kernel's two copies of a leave
-//     room for 32 waves per CU: that kernel -- aligned granules of B from
-//     each row's 128-byte line, a staged twice in LDS -- with 8 waves per
-//     workgroup on a persistent grid while its LDS is <= 40 KiB (4
-//     workgroups per CU), and, for n >= 4096, with 16 waves per workgroup
-//     (one row each, 2 workgroups per CU) while it is <= 70 KiB (k ~ 15.8K;
-//     measured: ahead by 9% at k = 14337, behind by 7% at k = 16383);
+//     misaligned) and at least 3072 of them.  Up to k = 8192: for up to 6144
+//     rows (or rows of at most 3 steps) one row per wave, a staged in LDS
+//     and B read with unaligned 16-byte loads, on at most 1536 four-wave
+//     workgroups; beyond that the realigning kernel (aligned granules of B
+//     from each row's 128-byte line, a staged twice in LDS) in eight-wave
+//     workgroups: two steps per batch on a persistent grid of 1024 (8192
+//     waves: 32 per CU, one full occupancy), and for rows of more than 12
+//     steps four per batch on a grid of 1536 while its LDS is <= 40 KiB.
+//     (A tuner sweep over 70 misaligned bf16 shapes with n = 512..65536,
+//     k = 1025..8001 on MI355X: within 3.5% of the best compiled plan on
+//     average; the realigning kernel alone, with four steps per batch on a
+//     grid of 1536, 14.8%, up to 61% for few rows.)  Longer rows: the
+//     realigning kernel with 16 waves per
+//     workgroup (one row each, 2 workgroups per CU) for n >= 4096 while its
+//     LDS is <= 70 KiB (k ~ 15.8K; measured: ahead by 9% at k = 14337,
+//     behind by 7% at k = 16383);
 //  2. too few rows to give the GPU 2048 waves even with 16 waves per row
 //     (n < 128): k split across workgroups as well (cross-workgroup
 //     variants; measured best for n = 32 and 64, 22-43% behind the
 //     in-workgroup split for n = 128 and 200);
-//  3. misaligned rows longer than that: unaligned 16-byte loads, two rows
-//     per one-wave workgroup when n >= 2048, otherwise the plan of 4.
-//     (Measured on MI355X over misaligned shapes with k from 4097 to 65537:
-//     the realigning kernel leads up to k ~ 14K and then falls behind, 13-40%
-//     at k >= 16K, as its LDS cuts the waves per CU.)
+//  3. misaligned rows longer than k = 8192 and not taken by 1: unaligned
+//     16-byte loads, two rows per one-wave workgroup when n >= 2048,
+//     otherwise the plan of 4.  (Measured on MI355X over misaligned shapes
+//     with k from 4097 to 65537: the realigning kernel leads up to k ~ 14K
+//     and then falls behind, 13-40% at k >= 16K, as its LDS cuts the waves
+//     per CU.)  Misaligned rows up to k = 8192 and fewer than 3072 of them
+//     take the plan of 4 as it stands, with unaligned loads (within 5% of
+//     the best in that sweep but for one shape, 19%).
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
 //     wave (a read once for both) when n >= 1024 and k >= 6144; a row of at
 //     most 8 steps goes to one wave; longer rows are split along k inside a
@@ -192,13 +204,21 @@ int find_variant(const Plan& p) {
 Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned) {
   const int64_t nfull0 = k / mbd::kStep;
   const bool misaligned = k > 0 && (k % 8 != 0 || !b_aligned);
-  // 1. (a is staged once per workgroup; no unaligned access at all)
-  if (misaligned) {
-    const Plan p8 = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
-    const size_t l = lds_bytes(kVariants[find_variant(p8)].info, k);
-    if (l <= (size_t)40 * 1024 && l <= max_lds) return p8;
+  constexpr int64_t kShortMisaligned = 8192;   // the k range of the measured tiers of 1
+  // 1.
+  if (misaligned && k <= kShortMisaligned && n >= 3072) {
+    const Plan pl = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 1536, 1};
+    const Plan pr = {1, 2, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1024, 1};
+    const Plan pr4 = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
+    const size_t l4 = lds_bytes(kVariants[find_variant(pr4)].info, k);
+    const Plan& p = (n <= 6144 || k <= 3 * mbd::kStep) ? pl
+                    : (k > 12 * mbd::kStep && l4 <= (size_t)40 * 1024) ? pr4 : pr;
+    if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
+  }
+  if (misaligned && k > kShortMisaligned && n >= 4096) {
     const Plan p16 = {1, 4, 16, 1, mbd::A_LDS_SHIFTED, kPolNT, 0, 1};
-    if (n >= 4096 && l <= (size_t)70 * 1024 && l <= max_lds) return p16;
+    const size_t l = lds_bytes(kVariants[find_variant(p16)].info, k);
+    if (l <= (size_t)70 * 1024 && l <= max_lds) return p16;
   }
   // 2. 8 waves per row per workgroup, Q groups, about 2048 waves in all (more
   // k-groups cost more than they bring on MI355X), keeping at least two
@@ -211,7 +231,7 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     if (Q * n <= (int64_t)kWsFloats && Q > 1) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
   // 3.
-  if (misaligned && n >= 2048) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
+  if (misaligned && k > kShortMisaligned && n >= 2048) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.
   const int64_t nfull = k / mbd::kStep;
   // very long rows (k >= 48K) and enough of them: no split, two rows per

@@ -31,7 +31,8 @@ def shape_of(info):
 
 
 # (rows, unroll, waves, splits, a_mode, cross_wg) per configured workload;
-# a_mode 1 = a through the caches, 2 = the realigning kernel's shifted LDS copies
+# a_mode 0 = a staged in LDS, 1 = a through the caches, 2 = the realigning
+# kernel's shifted LDS copies
 WORKLOAD_PLANS = {
     "tiny_256x512_f16": (1, 8, 4, 1, 1, 0),
     "gemv_18432x7168_f16": (2, 4, 4, 4, 1, 0),
@@ -72,18 +73,34 @@ def test_plan_grids_of_the_production_shapes():
     assert plan(7168, 16384, BF16)[0].grid == 3584
     # the measured entry for (4096, 14336): 512 workgroups, 2 rows per wave
     assert plan(4096, 14336, F16)[0].grid == 512
-    # the realigning kernel's persistent grid
+    # the realigning kernel's persistent grids: 1536 workgroups for rows of
+    # more than 12 steps, else 1024 (8192 waves)
     assert plan(18433, 7169, BF16)[0].grid == 1536
+    assert plan(18433, 4097, BF16)[0].grid == 1024
+    # one row per wave, a in LDS: at most 1536 workgroups
+    assert plan(3072, 7169, BF16)[0].grid == 768
+    assert plan(16384, 1025, BF16)[0].grid == 1536
     # 64 rows: k shared by 4 workgroups per row range
     assert plan(64, 65536, BF16)[0].kgroups == 4
 
 
 @pytest.mark.parametrize("n,k,want", [
-    # realigning kernel, 8 waves per workgroup while its LDS <= 40 KiB
+    # >= 3072 rows of k <= 8192: up to 6144 rows, or rows of <= 3 steps, one
+    # row per wave with a in LDS and unaligned B loads
+    (3072, 7169, (1, 4, 4, 1, 0, 0)),
+    (6144, 4097, (1, 4, 4, 1, 0, 0)),
+    (16384, 1025, (1, 4, 4, 1, 0, 0)),
+    (65536, 1535, (1, 4, 4, 1, 0, 0)),
+    # more rows of 4..12 steps: the realigning kernel, two steps per batch
+    (6145, 1545, (1, 2, 8, 1, 2, 0)),
+    (14336, 4097, (1, 2, 8, 1, 2, 0)),
+    (32768, 6143, (1, 2, 8, 1, 2, 0)),
+    # longer rows: four steps per batch while its LDS is <= 40 KiB
     (18433, 7169, (1, 4, 8, 1, 2, 0)),
-    (14336, 4097, (1, 4, 8, 1, 2, 0)),
-    (3072, 7169, (1, 4, 8, 1, 2, 0)),
-    # 16 waves per workgroup (n >= 4096) while it is <= 70 KiB
+    (32768, 8121, (1, 4, 8, 1, 2, 0)),
+    (32768, 8185, (1, 2, 8, 1, 2, 0)),
+    # k > 8192: the realigning kernel with 16 waves per workgroup (n >= 4096)
+    # while its LDS is <= 70 KiB
     (8192, 9217, (1, 4, 16, 1, 2, 0)),
     (8192, 12289, (1, 4, 16, 1, 2, 0)),
     (7169, 14337, (1, 4, 16, 1, 2, 0)),
@@ -96,13 +113,17 @@ def test_plan_grids_of_the_production_shapes():
     # fewer rows: the split plan of aligned rows (two rows per wave from 1024)
     (1024, 16385, (2, 4, 8, 8, 1, 0)),
     (1000, 16385, (1, 4, 8, 8, 1, 0)),
+    # fewer than 3072 rows of k <= 8192: the plan of aligned rows as well
+    (2048, 5121, (1, 4, 8, 4, 1, 0)),
+    (2048, 7169, (2, 4, 4, 4, 1, 0)),
+    (512, 5121, (1, 4, 4, 4, 1, 0)),
 ])
 def test_plan_misaligned_tiers(n, k, want):
     for dtype in (F16, BF16):
         assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
     # a B pointer off 16-byte alignment makes every row misaligned, whatever k
     if k % 8 == 1:
-        assert shape_of(plan(n, k - 1, F16, aligned=False)[1])[4] in (1, 2)
+        assert shape_of(plan(n, k - 1, F16, aligned=False)[1]) == want, (n, k)
 
 
 @pytest.mark.parametrize("n,k,want", [
