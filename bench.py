@@ -13,12 +13,19 @@ inside the measured region):
     synchronise, all on one stream; ms_per_step = wall time / K and
     value = algorithmic bytes per step / ms_per_step;
   * a HIP event pair on the launch stream brackets the same K launches; the
-    launches queue back to back with no idle gap between kernels (the host
-    enqueues far faster than a kernel runs), so the event time / K is the
-    kernel's average duration: roofline.achieved = algorithmic bytes per
-    launch / that average.  (An event pair around every single launch would
-    add the event packets' own cost to each duration.)
+    launches run back to back with no idle gap between kernels (a graph
+    replay, or host launches that enqueue far faster than a kernel runs),
+    so the event time / K is the kernel's average duration:
+    roofline.achieved = algorithmic bytes per launch / that average.  (An
+    event pair around every single launch would add the event packets' own
+    cost to each duration.)
 Algorithmic bytes per step = 2 * (n*k + k + n): B, a and c once each.
+
+The K timed steps are replayed from one HIP graph, captured once before the
+timed region (as a decode loop replays its graph); --stream launches each
+step from the host instead.  Either way every step is one full launch on the
+stream, in order.  --epilogue runs gemv_run_ex with c = 0.5 * (B @ a) + bias
+(bias counts 2n more bytes).
 
 Prints ONE JSON line on stdout; human-readable detail goes to stderr.
 """
@@ -129,6 +136,28 @@ def stream_probe(nbytes, steps, dev):
             "grid": best[1], "xcd_contiguous": best[2]}
 
 
+def capture_steps(step, steps, stream, dev):
+    """The K steps captured once into one HIP graph on a side stream (every
+    path of gemv_run and gla_decode_step is capture-safe: no allocation, no
+    memset, no synchronisation), then replayed once untimed on `stream`.
+    Returns the graph and the host cost of that replay per step (us)."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                step(i, side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    graph.replay()
+    host_us = (time.perf_counter() - t) / steps * 1e6
+    torch.cuda.synchronize()
+    return graph, host_us
+
+
 def gla_bench(args):
     """One GLA decode step per step (include/gla_decode.h), the state updated
     in place as a decode loop does; copies of the state rotate over > 1 GiB."""
@@ -155,7 +184,7 @@ def gla_bench(args):
     scale = 1.0 / math.sqrt(dk)
     P = [(Ss[i].data_ptr(), os_[i].data_ptr()) for i in range(nbuf)]
 
-    def step(i):
+    def step(i, sp=sp):
         s_, o_ = P[i % nbuf]
         rc = mbd.gla_decode_step(g.h, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), gd.data_ptr(),
                                  s_, s_, o_, bh, dk, dv, scale, dtype, sp)
@@ -164,12 +193,18 @@ def gla_bench(args):
 
     for i in range(args.warmup):
         step(i)
+    graph = None
+    if not args.stream:
+        graph, _ = capture_steps(step, args.steps, stream, dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -209,7 +244,7 @@ def gla_bench(args):
            "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAMES[dtype],
            "data": "synthetic",
            "config": {"workload": name, "bh": bh, "dk": dk, "dv": dv, "in_place": True,
-                      "rotating_buffers": nbuf},
+                      "rotating_buffers": nbuf, "launch": "stream" if args.stream else "graph"},
            "us_per_call": round(wall / args.steps * 1e6, 3), "kernel_us_avg": round(avg_us, 3),
            "roofline": {"bound": "hbm", "achieved": round(step_bytes / avg_us / 1e3, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -239,6 +274,11 @@ def main():
                     help="gemv (default, the headline) or gla: one GLA decode step")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the streaming-read probe (the practical read ceiling)")
+    ap.add_argument("--stream", action="store_true",
+                    help="launch each step from the host onto the stream instead of replaying "
+                         "one HIP graph that holds the K launches (the default)")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="run gemv_run_ex with c = 0.5 * (B @ a) + bias (bias: one more n-vector)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -299,9 +339,18 @@ def main():
             variant, vinfo.rows, vinfo.unroll, vinfo.waves, vinfo.splits, vinfo.a_mode,
             vinfo.b_policy, vinfo.cross_wg, grid, kgroups, nbuf, 2.0 * n * k / 1e6))
 
-    def step(i):
+    if args.epilogue:
+        # c = 0.5 * (B @ a) + bias, bias one more n-vector per rotation slot
+        biases = [torch.randn(n, device=dev).to(td) for _ in range(nbuf)]
+        bptr = [x.data_ptr() for x in biases]
+        step_bytes += 2 * n
+
+    def step(i, sp=sp):
         b, a, c = ptrs[i % nbuf]
-        s = run(h, b, a, c, n, k, dtype, sp)
+        if args.epilogue:
+            s = mbd.gemv_run_ex(h, b, a, c, n, k, dtype, 0.5, bptr[i % nbuf], sp)
+        else:
+            s = run(h, b, a, c, n, k, dtype, sp)
         if s != 0:
             raise mbd.GemvError(s, "gemv_run")
 
@@ -321,14 +370,22 @@ def main():
     torch.cuda.synchronize()
     host_us = host / args.steps * 1e6
 
+    graph, replay_host_us = None, None
+    if not args.stream:
+        graph, replay_host_us = capture_steps(step, args.steps, stream, dev)
+        log("[bench] captured %d launches into one HIP graph" % args.steps)
+
     # timed region: whole-job throughput, with one event pair on the stream
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -346,7 +403,9 @@ def main():
         log("[bench] streaming-read probe over the same bytes: %.2f us -> %.1f GB/s" % (
             ceiling["us"], ceiling["gbs"]))
     from memory_bound_dense_amd.profile_counters import plan_signature
-    traffic = read_traffic(name, step_bytes, plan_signature(variant, grid, kgroups))
+    # the counter summaries are taken on plain launches (no epilogue)
+    traffic = None if args.epilogue else read_traffic(name, step_bytes,
+                                                      plan_signature(variant, grid, kgroups))
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -366,11 +425,13 @@ def main():
                    "unroll": vinfo.unroll, "waves_per_wg": vinfo.waves, "splits": vinfo.splits,
                    "a_mode": {0: "lds", 1: "cached", 2: "lds_shifted"}[vinfo.a_mode],
                    "layout": ["lanes_along_k", "row_per_lane"][vinfo.layout],
-                   "rotating_buffers": nbuf},
+                   "rotating_buffers": nbuf, "launch": "stream" if args.stream else "graph",
+                   "epilogue": "alpha_bias" if args.epilogue else "none"},
         "us_per_call": round(ms_per_step * 1e3, 3),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernel_us_avg": round(avg_us, 3),
         "host_us_per_call": round(host_us, 3),
+        "graph_replay_host_us_per_step": None if replay_host_us is None else round(replay_host_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -146,7 +146,7 @@ def counter_per_dispatch(path, kernel_substr, counter):
     return vals
 
 
-def summarize_trace(stats_csv, trace_csv, command, out):
+def summarize_trace(stats_csv, trace_csv, command, out, last=0):
     lines = ["# rocprofv3 kernel trace summary", "command: %s" % command,
              "kernel_source_sha256_16: %s" % kernel_source_hash(), ""]
     stats = _rows(stats_csv)
@@ -157,7 +157,9 @@ def summarize_trace(stats_csv, trace_csv, command, out):
         lines.append("  " + " | ".join(r[k] for k in keys))
     if trace_csv:
         durs = {}
-        for r in _rows(trace_csv):
+        rows = sorted(_rows(trace_csv), key=lambda r: int(_col(r, "Start_Timestamp",
+                                                                "Start-Timestamp")))
+        for r in rows:
             nm = _col(r, "Kernel_Name", "Kernel-Name")
             d = (int(_col(r, "End_Timestamp", "End-Timestamp")) -
                  int(_col(r, "Start_Timestamp", "Start-Timestamp"))) / 1000.0
@@ -167,6 +169,16 @@ def summarize_trace(stats_csv, trace_csv, command, out):
         for nm, d in durs.items():
             lines.append("  %s: dispatches %d avg %.3f median %.3f min %.3f max %.3f" % (
                 nm, len(d), statistics.fmean(d), statistics.median(d), min(d), max(d)))
+        if last:
+            # the timed region: a kernel's last `last` dispatches, in start order
+            lines.append("")
+            lines.append("the last %d dispatches of each kernel with at least that many "
+                         "(the timed region), us:" % last)
+            for nm, d in durs.items():
+                if len(d) >= last:
+                    t = d[-last:]
+                    lines.append("  %s: avg %.3f median %.3f min %.3f max %.3f" % (
+                        nm, statistics.fmean(t), statistics.median(t), min(t), max(t)))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -224,6 +236,8 @@ def main():
     p.add_argument("--trace", default="")
     p.add_argument("--command", required=True)
     p.add_argument("--out", required=True)
+    p.add_argument("--last", type=int, default=0,
+                   help="also summarise each kernel's last N dispatches (the timed region)")
     p = sub.add_parser("summarize-counters")
     p.add_argument("--workload", required=True)
     p.add_argument("--fetch", required=True)
@@ -239,7 +253,7 @@ def main():
     elif a.cmd == "copy":
         run_copy(a.bytes, a.launches)
     elif a.cmd == "summarize-trace":
-        summarize_trace(a.stats, a.trace, a.command, a.out)
+        summarize_trace(a.stats, a.trace, a.command, a.out, a.last)
     else:
         summarize_counters(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes,
                            a.commands, a.out)
