@@ -104,9 +104,30 @@ def cpu_baseline(B_bits, a_bits, dtype, n, k, target_s=10.0):
             "us_per_call": round(dt / calls * 1e6 * n / rows, 1)}
 
 
-def stream_probe(nbytes, steps, dev):
+def time_launches(launch, steps, stream, dev, graph):
+    """Average device time (us) of `steps` calls of launch(i, stream_handle),
+    back to back on `stream`: from one HIP graph replay (captured first) or
+    from host launches, bracketed by one event pair."""
+    import torch
+    g = capture_steps(launch, steps, stream, dev)[0] if graph else None
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            launch(i, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def stream_probe(nbytes, steps, dev, graph=True):
     """A plain streaming read of the same number of bytes (rounded down to
-    whole 16 KiB chunks), timed like the GEMV: the practical read ceiling."""
+    whole 16 KiB chunks), timed like the GEMV (the same launch mode): the
+    practical read ceiling."""
     import torch
     from memory_bound_dense_amd import probe
     nbytes = nbytes // probe.CHUNK * probe.CHUNK
@@ -116,19 +137,12 @@ def stream_probe(nbytes, steps, dev):
     stream = torch.cuda.current_stream(dev)
     best = None
     for grid, xcd in ((0, False), (512, False), (512, True), (1024, False), (2048, False)):
+        def launch(i, sp, grid=grid, xcd=xcd):
+            probe.stream_read(bufs[i % nbuf].data_ptr(), nbytes, out.data_ptr(), out.numel(), grid,
+                              True, sp, xcd)
         for i in range(10):
-            probe.stream_read(bufs[i % nbuf].data_ptr(), nbytes, out.data_ptr(), out.numel(), grid,
-                              True, stream.cuda_stream, xcd)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(steps):
-            probe.stream_read(bufs[i % nbuf].data_ptr(), nbytes, out.data_ptr(), out.numel(), grid,
-                              True, stream.cuda_stream, xcd)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+            launch(i, stream.cuda_stream)
+        us = time_launches(launch, steps, stream, dev, graph)
         if best is None or us < best[0]:
             best = (us, grid, xcd)
     del bufs
@@ -221,18 +235,12 @@ def gla_bench(args):
             dst = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
             best = None
             for grid in (0, 512, 2048):
+                def launch(i, sp, grid=grid):
+                    probe.stream_copy(Ss[i % nbuf].data_ptr(), dst[i % nbuf].data_ptr(), nbytes, grid,
+                                      True, sp)
                 for i in range(5):
-                    probe.stream_copy(Ss[i % nbuf].data_ptr(), dst[i % nbuf].data_ptr(), nbytes, grid,
-                                      True, sp)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                e0.record(stream)
-                for i in range(args.steps):
-                    probe.stream_copy(Ss[i % nbuf].data_ptr(), dst[i % nbuf].data_ptr(), nbytes, grid,
-                                      True, sp)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / args.steps
+                    launch(i, sp)
+                us = time_launches(launch, args.steps, stream, dev, not args.stream)
                 best = us if best is None else min(best, us)
             ceiling = {"bytes_moved": 2 * nbytes, "us": round(best, 3),
                        "gbs": round(2 * nbytes / best / 1e3, 1)}
@@ -398,7 +406,7 @@ def main():
             ms_per_step * 1e3, value, avg_us, achieved, 100 * achieved / HBM_PEAK_GBS,
             HBM_PEAK_GBS))
 
-    ceiling = stream_probe(2 * n * k, args.steps, dev) if not args.no_probe else None
+    ceiling = stream_probe(2 * n * k, args.steps, dev, not args.stream) if not args.no_probe else None
     if ceiling:
         log("[bench] streaming-read probe over the same bytes: %.2f us -> %.1f GB/s" % (
             ceiling["us"], ceiling["gbs"]))
