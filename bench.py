@@ -21,6 +21,13 @@ inside the measured region):
     cost to each duration.)
 Algorithmic bytes per step = 2 * (n*k + k + n): B, a and c once each.
 
+K defaults to 2000: on MI355X the first ~20 ms of sustained load after an
+idle gap run 1-5% slower while the memory clocks come up (a kernel trace of
+the headline shows 38.5-39.6 us per launch there, then 37.5-37.6 us), so a
+timed region of a few ms (K = 200 is 7.7 ms for the headline) reads low.
+The K untimed host launches and the untimed graph replay before the timed
+region are that much sustained load already.
+
 The K timed steps are replayed from one HIP graph, captured once before the
 timed region (as a decode loop replays its graph); --stream launches each
 step from the host instead.  Either way every step is one full launch on the
@@ -267,7 +274,7 @@ def gla_bench(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="gemv_18432x7168_f16",
                     help="workload name (gemv_inputs.ALL_WORKLOADS / EXTRA_WORKLOADS)")
