@@ -75,10 +75,29 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
       sv[r] = __builtin_amdgcn_raw_buffer_load_b128(sin_r, off, 0u, LPOL);
     }
   };
+  // Without staging, the row scalars (gk, k, q) of a trip travel with its
+  // state rows: loaded a trip ahead at a clamped index (always in bounds),
+  // as raw 16-bit values, so no branch holds a load back and nothing waits
+  // on one memory round trip before issuing the next.  (With both behind
+  // conditions the compiler waited for the state before the loop and for
+  // each row's scalars in turn: several round trips where one suffices.)
+  auto load_scalars = [&](int i0, uint16_t (&sg)[kRows], uint16_t (&sk)[kRows],
+                          uint16_t (&sq)[kRows]) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int i = i0 + r * RG;
+      const int64_t ic = rowbase + (i < dk ? i : dk - 1);
+      sg[r] = gk[ic];
+      sk[r] = k[ic];
+      sq[r] = q[ic];
+    }
+  };
   u32x4 cur[kRows];
+  uint16_t cg[kRows], ck[kRows], cq[kRows];
   float vj[4] = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     load_trip(rg, cur);
+    if constexpr (!STAGE) load_scalars(rg, cg, ck, cq);
 #pragma unroll
     for (int c = 0; c < 4; ++c) vj[c] = widen<DT>(v[head * dv + j0 + c]);
   }
@@ -96,44 +115,87 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
   float oacc[4] = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     for (int i0 = rg; i0 < dk; i0 += kTrip) {
-      u32x4 nxt[kRows];
+      // The next trip's loads go out before this trip waits on anything.
+      // Without staging they are issued unconditionally (state rows past dk
+      // come from outside the descriptor's range: no memory access), and
+      // the update below is branch-free, so no branch holds a load back.
+      // With staging the loads are conditional and the update branches per
+      // row (measured on MI355X: 0.6-4.6% faster there than the
+      // unconditional form; without staging the unconditional form is 6%
+      // faster at 32 heads).
       const bool more = i0 + kTrip < dk;
-      if (more) load_trip(i0 + kTrip, nxt);
+      u32x4 nxt[kRows];
+      uint16_t ng[kRows], nk[kRows], nq[kRows];
+      if constexpr (STAGE) {
+        if (more) load_trip(i0 + kTrip, nxt);
+      } else {
+        load_trip(i0 + kTrip, nxt);
+        load_scalars(i0 + kTrip, ng, nk, nq);
+      }
       float e[kRows], ki[kRows], qi[kRows];
 #pragma unroll
       for (int r = 0; r < kRows; ++r) {
-        const int i = i0 + r * RG;
-        if (i < dk) {
-          if constexpr (STAGE) {
+        if constexpr (STAGE) {
+          const int i = i0 + r * RG;
+          if (i < dk) {
             e[r] = gla_rows[i];
             ki[r] = gla_rows[dk + i];
             qi[r] = gla_rows[2 * dk + i];
-          } else {
-            e[r] = expf(widen<DT>(gk[rowbase + i]));
-            ki[r] = widen<DT>(k[rowbase + i]);
-            qi[r] = widen<DT>(q[rowbase + i]);
           }
+        } else {
+          e[r] = expf(widen<DT>(cg[r]));
+          ki[r] = widen<DT>(ck[r]);
+          qi[r] = widen<DT>(cq[r]);
         }
       }
 #pragma unroll
       for (int r = 0; r < kRows; ++r) {
         const int i = i0 + r * RG;
-        if (i < dk) {
+        if constexpr (STAGE) {
+          if (i < dk) {
+            u32x4 nv;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t w = cur[r][c];
+              const float sn = __builtin_fmaf(ki[r], vj[c], e[r] * __builtin_bit_cast(float, w));
+              nv[c] = __builtin_bit_cast(uint32_t, sn);
+              oacc[c] = __builtin_fmaf(qi[r], sn, oacc[c]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(
+                nv, sout_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, SPOL);
+          }
+        } else {
+          // every slot is updated (a row past dk holds the clamped row's
+          // scalars and a zero state) and kept by a select; only the store
+          // is conditional
+          const bool live = i < dk;
           u32x4 nv;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const uint32_t w = cur[r][c];
             const float sn = __builtin_fmaf(ki[r], vj[c], e[r] * __builtin_bit_cast(float, w));
             nv[c] = __builtin_bit_cast(uint32_t, sn);
-            oacc[c] = __builtin_fmaf(qi[r], sn, oacc[c]);
+            const float acc = __builtin_fmaf(qi[r], sn, oacc[c]);
+            oacc[c] = live ? acc : oacc[c];
           }
-          __builtin_amdgcn_raw_buffer_store_b128(
-              nv, sout_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, SPOL);
+          if (live)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                nv, sout_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, SPOL);
         }
       }
-      if (more) {
+      if constexpr (STAGE) {
+        if (more) {
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) cur[r] = nxt[r];
+          for (int r = 0; r < kRows; ++r) cur[r] = nxt[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+          cur[r] = nxt[r];
+          cg[r] = ng[r];
+          ck[r] = nk[r];
+          cq[r] = nq[r];
+        }
       }
     }
   }
