@@ -53,7 +53,7 @@ namespace {
 // Heads of at most this many rows stage exp(gk), k and q in LDS (6 KiB).
 constexpr int64_t kGlaStageRows = 512;
 
-using GlaFn = void (*)(const float*, float*, int, int, int, const uint16_t*, const uint16_t*,
+using GlaFn = void (*)(const float*, float*, int, int, const uint16_t*, const uint16_t*,
                        const uint16_t*, const uint16_t*, uint16_t*, float);
 
 }  // namespace
@@ -94,7 +94,7 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
     if (bh * ((dv + cw - 1) / cw) >= want || c == 0) { sel = c; break; }
   }
   const int64_t cw = 4 * (8 << sel);
-  int nblk = (int)((dv + cw - 1) / cw);
+  const int64_t nblk = (dv + cw - 1) / cw;   // the kernel derives the same count from dv
   const int64_t grid = bh * nblk;
   // staging pays once the grid covers every CU; below that a workgroup's
   // wait for the staged rows sits on the critical path of a latency-bound
@@ -107,7 +107,7 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
                  *gp = (const uint16_t*)gk;
   uint16_t* op = (uint16_t*)o;
   int dki = (int)dk, dvi = (int)dv;
-  void* args[] = {(void*)&S_in, (void*)&S_out, (void*)&dki, (void*)&dvi, (void*)&nblk, (void*)&vp,
+  void* args[] = {(void*)&S_in, (void*)&S_out, (void*)&dki, (void*)&dvi, (void*)&vp,
                   (void*)&gp,   (void*)&kp,    (void*)&qp,  (void*)&op,  (void*)&scale};
   hipError_t e = hipLaunchKernel((const void*)fns[dtype][stage][sel], dim3((unsigned)grid),
                                  dim3(mbd::kGlaThreads), args, lds, stream);

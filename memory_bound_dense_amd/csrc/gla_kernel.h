@@ -34,14 +34,17 @@ constexpr int kGlaThreads = 256;
 // -- by every lane of a row group for every row; the host picks it when the
 // head is short enough for that LDS to stay small.
 template <int DT, int LPR, int ROWS = 4, int LPOL = 0, int SPOL = 0, bool STAGE = false>
-// Parameters in the order a workgroup needs them (the first 14 dwords are
-// preloaded into SGPRs at wave launch).
+// Parameters in the order a workgroup needs them: the first 14 dwords
+// (everything up to q) are preloaded into SGPRs at wave launch, so no load
+// of the trip waits on a kernel-argument fetch; o and scale, needed only at
+// the end, are fetched from the argument segment.
 __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
-    const float* S_in, float* S_out, int dk, int dv, int nblk, const uint16_t* __restrict__ v,
+    const float* S_in, float* S_out, int dk, int dv, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ gk, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, float scale) {
   constexpr int CW = 4 * LPR;                 // columns per block
   constexpr int RG = kGlaThreads / LPR;       // row groups
+  const int nblk = (dv + CW - 1) / CW;        // column blocks per head
   __shared__ float part[RG][CW];
 
   const int t = threadIdx.x;
