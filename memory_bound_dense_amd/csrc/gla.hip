@@ -100,7 +100,9 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
   // wait for the staged rows sits on the critical path of a latency-bound
   // launch (measured on MI355X, 128 x 128 heads: 32 heads 3.50 us without
   // against 3.89 us with; 128 heads 4.84 against 4.71)
-  const int stage = (dk <= kGlaStageRows && grid >= h->num_cus) ? 1 : 0;
+  // dk == 0 (o is the empty sum) always takes the staged form: the other
+  // loads the row scalars at row dk - 1
+  const int stage = (dk == 0 || (dk <= kGlaStageRows && grid >= h->num_cus)) ? 1 : 0;
   const size_t lds = stage ? (size_t)(3 * dk) * sizeof(float) : 0;
   if (grid > ((int64_t)1 << 31) - 1) return report(h, GEMV_ERR_TOO_LARGE, "gla grid");
   const uint16_t *qp = (const uint16_t*)q, *kp = (const uint16_t*)k, *vp = (const uint16_t*)v,

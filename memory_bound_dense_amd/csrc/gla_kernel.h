@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
     }
   };
   // Without staging, the row scalars (gk, k, q) of a trip travel with its
-  // state rows: loaded a trip ahead at a clamped index (always in bounds),
+  // state rows: loaded a trip ahead at a row index clamped to dk - 1 (in
+  // bounds as dk >= 1 here: the host sends dk == 0 to the staged form),
   // as raw 16-bit values, so no branch holds a load back and nothing waits
   // on one memory round trip before issuing the next.  (With both behind
   // conditions the compiler waited for the state before the loop and for
@@ -100,6 +101,8 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
   float vj[4] = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     load_trip(rg, cur);
+    // the clamped index needs a row: the host launches this form only with
+    // dk >= 1 (dk == 0 goes to the staged form, which loads no row scalars)
     if constexpr (!STAGE) load_scalars(rg, cg, ck, cq);
 #pragma unroll
     for (int c = 0; c < 4; ++c) vj[c] = widen<DT>(v[head * dv + j0 + c]);
