@@ -21,12 +21,12 @@ inside the measured region):
     cost to each duration.)
 Algorithmic bytes per step = 2 * (n*k + k + n): B, a and c once each.
 
-K defaults to 2000: on MI355X the first ~20 ms of sustained load after an
-idle gap run 1-5% slower while the memory clocks come up (a kernel trace of
-the headline shows 38.5-39.6 us per launch there, then 37.5-37.6 us), so a
-timed region of a few ms (K = 200 is 7.7 ms for the headline) reads low.
-The K untimed host launches and the untimed graph replay before the timed
-region are that much sustained load already.
+On MI355X the first ~20 ms of sustained load after the GPU has been idle
+run 1-5% slower while the memory clocks come up (a kernel trace of the
+headline shows 38.5-39.6 us per launch there, then 37.5-37.6 us), so the
+timed region is preceded by at least 50 ms of the same launches, untimed
+(graph replays, or host launches with --stream), whatever K is.  K defaults
+to 2000 (75 ms of timed work for the headline).
 
 The K timed steps are replayed from one HIP graph, captured once before the
 timed region (as a decode loop replays its graph); --stream launches each
@@ -117,6 +117,11 @@ def time_launches(launch, steps, stream, dev, graph):
     from host launches, bracketed by one event pair."""
     import torch
     g = capture_steps(launch, steps, stream, dev)[0] if graph else None
+    if g is None:
+        def host_launches():
+            for i in range(steps):
+                launch(i, stream.cuda_stream)
+        sustain(host_launches)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -157,11 +162,29 @@ def stream_probe(nbytes, steps, dev, graph=True):
             "grid": best[1], "xcd_contiguous": best[2]}
 
 
+# Untimed sustained load before a timed region: on MI355X the memory clocks
+# need ~20 ms of sustained traffic to come up after the GPU has been idle.
+SUSTAIN_S = 0.05
+
+
+def sustain(run_once, min_s=SUSTAIN_S, max_runs=10000):
+    """Run `run_once` (enqueue work on the GPU) back to back, untimed, until
+    the GPU has been busy for at least min_s seconds (and at least once)."""
+    import torch
+    t0 = time.perf_counter()
+    for _ in range(max_runs):
+        run_once()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= min_s:
+            break
+
+
 def capture_steps(step, steps, stream, dev):
     """The K steps captured once into one HIP graph on a side stream (every
     path of gemv_run and gla_decode_step is capture-safe: no allocation, no
-    memset, no synchronisation), then replayed once untimed on `stream`.
-    Returns the graph and the host cost of that replay per step (us)."""
+    memset, no synchronisation), then replayed untimed on `stream` for at
+    least SUSTAIN_S seconds.  Returns the graph and the host cost of one
+    replay per step (us)."""
     import torch
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream(dev)
@@ -176,6 +199,7 @@ def capture_steps(step, steps, stream, dev):
     graph.replay()
     host_us = (time.perf_counter() - t) / steps * 1e6
     torch.cuda.synchronize()
+    sustain(graph.replay)
     return graph, host_us
 
 
@@ -217,6 +241,11 @@ def gla_bench(args):
     graph = None
     if not args.stream:
         graph, _ = capture_steps(step, args.steps, stream, dev)
+    else:
+        def host_launches():
+            for i in range(args.steps):
+                step(i)
+        sustain(host_launches)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -389,6 +418,11 @@ def main():
     if not args.stream:
         graph, replay_host_us = capture_steps(step, args.steps, stream, dev)
         log("[bench] captured %d launches into one HIP graph" % args.steps)
+    else:
+        def host_launches():
+            for i in range(args.steps):
+                step(i)
+        sustain(host_launches)
 
     # timed region: whole-job throughput, with one event pair on the stream
     ev0 = torch.cuda.Event(enable_timing=True)
