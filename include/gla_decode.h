@@ -24,7 +24,9 @@
  * Like gemv_run: host validation, one kernel enqueued on `stream`, no
  * allocation, no synchronisation; on any error nothing is launched.
  * bh == 0 or dv == 0 is a no-op; dk == 0 writes o = 0 (the empty sum).
- * Limits: dk, dv <= 65536, dk * dv <= 2^28, bh <= 2^30 (GEMV_ERR_TOO_LARGE).
+ * Limits: dk, dv <= 65536, dk * dv <= 2^28, bh <= 2^30 (GEMV_ERR_TOO_LARGE);
+ * gla_decode_step also returns GEMV_ERR_TOO_LARGE when bh times the number of
+ * column blocks it picks (ceil(dv / 32) to ceil(dv / 128)) exceeds 2^23.
  */
 #ifndef MBD_GLA_DECODE_H
 #define MBD_GLA_DECODE_H

@@ -345,8 +345,9 @@ static gemv_status_t shape_launch(int v, int64_t g, int64_t q, int flags, int64_
   const int64_t nrb = (n + rb - 1) / rb;       // one row range per wave (or workgroup)
   if (g <= 0 || g > nrb) g = nrb;
   // the kernels walk their row ranges, so a smaller grid is always valid;
-  // keep the launch's work-item count well inside 32 bits
-  const int64_t gmax = (int64_t)1 << 24;
+  // keep the launch's work-items along x (workgroups x threads, a 32-bit
+  // field of the dispatch) at most 2^31
+  const int64_t gmax = ((int64_t)1 << 31) / ((int64_t)info.waves * kLanesPerWave);
   if (g > gmax) g = gmax;
   if (info.layout == 1 && (int64_t)kLanesPerWave * k * 2 >= ((int64_t)1 << 32))
     return GEMV_ERR_UNSUPPORTED;   // a wave's 64 rows must fit one buffer descriptor

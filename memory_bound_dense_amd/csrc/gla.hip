@@ -104,7 +104,9 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
   // loads the row scalars at row dk - 1
   const int stage = (dk == 0 || (dk <= kGlaStageRows && grid >= h->num_cus)) ? 1 : 0;
   const size_t lds = stage ? (size_t)(3 * dk) * sizeof(float) : 0;
-  if (grid > ((int64_t)1 << 31) - 1) return report(h, GEMV_ERR_TOO_LARGE, "gla grid");
+  // one workgroup per (head, column block); its work-items along x (a 32-bit
+  // field of the dispatch) are kept at most 2^31
+  if (grid > ((int64_t)1 << 31) / mbd::kGlaThreads) return report(h, GEMV_ERR_TOO_LARGE, "gla grid");
   const uint16_t *qp = (const uint16_t*)q, *kp = (const uint16_t*)k, *vp = (const uint16_t*)v,
                  *gp = (const uint16_t*)gk;
   uint16_t* op = (uint16_t*)o;
