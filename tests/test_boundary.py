@@ -4,6 +4,8 @@ and rejects every bad argument with the documented status before any launch.
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -176,3 +178,37 @@ def test_gla_check_args(args, expect):
 def test_gla_null_handle():
     assert mbd.gla_decode_step(None, Q0, K0, V0, G0, S0, S1, O0, 1, 4, 4, 1.0, 0) == \
         _lib.GEMV_ERR_NULL_HANDLE
+
+
+def test_plain_c_consumer(tmp_path):
+    """The headers compile as C99 and a C program links every entry point
+    from the library and calls the host-only ones (tests/c_abi/consumer.c)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib_dir = os.path.dirname(_lib.LIB_PATH)
+    exe = str(tmp_path / "consumer")
+    build = subprocess.run(
+        [cc, "-std=c99", "-Wall", "-Werror", "-isystem", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+         "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_abi", "consumer.c"),
+         "-L", lib_dir, "-lgemv", "-Wl,-rpath," + lib_dir, "-o", exe],
+        capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stderr
+    out = dict(line.split(" ", 1) for line in run.stdout.splitlines())
+    assert out["linked"] == str(len(_lib.EXPORTS))
+    assert out["status0"] == "GEMV_OK" and out["status5"] == "GEMV_ERR_ALIASING"
+    assert out["check_ok"] == str(_lib.GEMV_OK)
+    assert out["check_misaligned"] == str(_lib.GEMV_ERR_MISALIGNED)
+    assert out["check_too_large"] == str(_lib.GEMV_ERR_TOO_LARGE)
+    assert out["plan_status"] == str(_lib.GEMV_OK)
+    assert out["plan_shape"] == "R2 U4 W4 S4 grid 9216"      # the headline's plan
+    assert out["variants"] == str(mbd.gemv_num_variants())
+    assert out["gla_check"] == str(_lib.GEMV_OK)
+    import torch
+    if torch.cuda.is_available():
+        assert out["create"] == "ok handle"
+    else:
+        assert out["create"] == "error null"
+    assert out["destroy"] == str(_lib.GEMV_OK)
