@@ -111,26 +111,19 @@ def cpu_baseline(B_bits, a_bits, dtype, n, k, target_s=10.0):
             "us_per_call": round(dt / calls * 1e6 * n / rows, 1)}
 
 
-def time_launches(launch, steps, stream, dev, graph):
-    """Average device time (us) of `steps` calls of launch(i, stream_handle),
-    back to back on `stream`: from one HIP graph replay (captured first) or
-    from host launches, bracketed by one event pair."""
+def time_launches(launch, steps, nbuf, stream, dev, graph):
+    """Average device time (us) of `steps` calls of launch(i, stream_handle)
+    over `nbuf` rotating input copies, back to back on `stream` after a
+    sustained untimed run (graph replays, or host launches), bracketed by
+    one event pair."""
     import torch
-    g = capture_steps(launch, steps, stream, dev)[0] if graph else None
-    if g is None:
-        def host_launches():
-            for i in range(steps):
-                launch(i, stream.cuda_stream)
-        sustain(host_launches)
+    lau = Launcher(launch, steps, nbuf, stream, dev, graph)
+    sustain(lau.run)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    if g is not None:
-        g.replay()
-    else:
-        for i in range(steps):
-            launch(i, stream.cuda_stream)
+    lau.run()
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / steps
@@ -143,7 +136,7 @@ def stream_probe(nbytes, steps, dev, graph=True):
     import torch
     from memory_bound_dense_amd import probe
     nbytes = nbytes // probe.CHUNK * probe.CHUNK
-    nbuf = int(min(64, max(2, math.ceil((1 << 30) / nbytes))))
+    nbuf = rotation(nbytes)
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
     out = torch.empty(1 << 20, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -154,7 +147,7 @@ def stream_probe(nbytes, steps, dev, graph=True):
                               True, sp, xcd)
         for i in range(10):
             launch(i, stream.cuda_stream)
-        us = time_launches(launch, steps, stream, dev, graph)
+        us = time_launches(launch, steps, nbuf, stream, dev, graph)
         if best is None or us < best[0]:
             best = (us, grid, xcd)
     del bufs
@@ -179,28 +172,57 @@ def sustain(run_once, min_s=SUSTAIN_S, max_runs=10000):
             break
 
 
-def capture_steps(step, steps, stream, dev):
-    """The K steps captured once into one HIP graph on a side stream (every
-    path of gemv_run and gla_decode_step is capture-safe: no allocation, no
-    memset, no synchronisation), then replayed untimed on `stream` for at
-    least SUSTAIN_S seconds.  Returns the graph and the host cost of one
-    replay per step (us)."""
-    import torch
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            for i in range(steps):
-                step(i, side.cuda_stream)
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    graph.replay()
-    host_us = (time.perf_counter() - t) / steps * 1e6
-    torch.cuda.synchronize()
-    sustain(graph.replay)
-    return graph, host_us
+# Copies of an input kept in rotation: together > 1 GiB, so neither the L2
+# nor the 256 MiB Infinity Cache holds a copy from one use to the next.
+MAX_COPIES = 4096
+
+
+def rotation(nbytes):
+    return int(min(MAX_COPIES, max(2, math.ceil((1 << 30) / max(nbytes, 1)))))
+
+
+class Launcher:
+    """K launches of step(i, stream_handle) per run(); launch i uses input
+    copy i % nbuf and the index keeps counting across runs, so consecutive
+    launches never reuse a copy before nbuf others.  Graph mode: the launches
+    are captured once (every path of gemv_run and gla_decode_step is
+    capture-safe: no allocation, no memset, no synchronisation) as windows of
+    K that together cover every copy, replayed round robin; host_us is the
+    host cost of one replay per launch.  Stream mode: host launches."""
+
+    def __init__(self, step, steps, nbuf, stream, dev, graph):
+        import torch
+        self.step, self.steps, self.stream, self.graph = step, steps, stream, graph
+        self.next = 0
+        self.graphs = []
+        self.host_us = None
+        if graph:
+            windows = 1 if steps >= nbuf else -(-nbuf // steps)
+            side = torch.cuda.Stream(dev)
+            for w in range(windows):
+                gph = torch.cuda.CUDAGraph()
+                side.wait_stream(stream)
+                with torch.cuda.stream(side):
+                    with torch.cuda.graph(gph, stream=side):
+                        for j in range(steps):
+                            step(w * steps + j, side.cuda_stream)
+                stream.wait_stream(side)
+                self.graphs.append(gph)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            self.run()
+            self.host_us = (time.perf_counter() - t) / steps * 1e6
+            torch.cuda.synchronize()
+
+    def run(self):
+        """Enqueue the next K launches on the stream."""
+        if self.graph:
+            self.graphs[self.next % len(self.graphs)].replay()
+            self.next += 1
+        else:
+            for _ in range(self.steps):
+                self.step(self.next, self.stream.cuda_stream)
+                self.next += 1
 
 
 def gla_bench(args):
@@ -219,7 +241,7 @@ def gla_bench(args):
     qd, kd, vd, gd = t(q), t(k), t(v), t(gk)
     S0 = torch.from_numpy(S).to(dev)
     state_bytes = 4 * bh * dk * dv
-    nbuf = int(min(64, max(2, math.ceil((1 << 30) / state_bytes))))
+    nbuf = rotation(state_bytes)
     Ss = [S0] + [S0.clone() for _ in range(nbuf - 1)]
     os_ = [torch.empty((bh, dv), dtype=td, device=dev) for _ in range(nbuf)]
     step_bytes = 2 * state_bytes + 2 * bh * (3 * dk + 2 * dv)
@@ -238,23 +260,13 @@ def gla_bench(args):
 
     for i in range(args.warmup):
         step(i)
-    graph = None
-    if not args.stream:
-        graph, _ = capture_steps(step, args.steps, stream, dev)
-    else:
-        def host_launches():
-            for i in range(args.steps):
-                step(i)
-        sustain(host_launches)
+    lau = Launcher(step, args.steps, nbuf, stream, dev, not args.stream)
+    sustain(lau.run)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
+    lau.run()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -276,7 +288,7 @@ def gla_bench(args):
                                       True, sp)
                 for i in range(5):
                     launch(i, sp)
-                us = time_launches(launch, args.steps, stream, dev, not args.stream)
+                us = time_launches(launch, args.steps, nbuf, stream, dev, not args.stream)
                 best = us if best is None else min(best, us)
             ceiling = {"bytes_moved": 2 * nbytes, "us": round(best, 3),
                        "gbs": round(2 * nbytes / best / 1e3, 1)}
@@ -363,7 +375,7 @@ def main():
     B0 = torch.from_numpy(B_bits.view(np.int16)).to(dev).view(td)
     a0 = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(td)
     step_bytes = algorithmic_bytes(n, k)
-    nbuf = int(min(64, max(2, math.ceil(args.rotate_bytes / (2.0 * n * k)))))
+    nbuf = int(min(MAX_COPIES, max(2, math.ceil(args.rotate_bytes / (2.0 * n * k)))))
     Bs = [B0] + [B0.clone() for _ in range(nbuf - 1)]
     As = [a0] + [a0.clone() for _ in range(nbuf - 1)]
     Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]
@@ -414,15 +426,11 @@ def main():
     torch.cuda.synchronize()
     host_us = host / args.steps * 1e6
 
-    graph, replay_host_us = None, None
-    if not args.stream:
-        graph, replay_host_us = capture_steps(step, args.steps, stream, dev)
-        log("[bench] captured %d launches into one HIP graph" % args.steps)
-    else:
-        def host_launches():
-            for i in range(args.steps):
-                step(i)
-        sustain(host_launches)
+    lau = Launcher(step, args.steps, nbuf, stream, dev, not args.stream)
+    replay_host_us = lau.host_us
+    if lau.graphs:
+        log("[bench] captured %d launches into %d HIP graph(s)" % (args.steps, len(lau.graphs)))
+    sustain(lau.run)
 
     # timed region: whole-job throughput, with one event pair on the stream
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -430,11 +438,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
+    lau.run()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -92,7 +92,7 @@ def run_gemv(workload, launches, variant=-1, grid=0):
     B_bits, a_bits = random_inputs(n, k, dtype, dist, seed=0)
     B0 = torch.from_numpy(B_bits.view(np.int16)).to(dev).view(td)
     a0 = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(td)
-    nbuf = int(min(64, max(2, math.ceil((1 << 30) / (2.0 * n * k)))))
+    nbuf = int(min(4096, max(2, math.ceil((1 << 30) / (2.0 * n * k)))))
     Bs = [B0] + [B0.clone() for _ in range(nbuf - 1)]
     As = [a0] + [a0.clone() for _ in range(nbuf - 1)]
     Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]

@@ -37,6 +37,9 @@ def main():
     ap.add_argument("--include-ablation", action="store_true",
                     help="also time the uncoalesced layout (slow)")
     ap.add_argument("--out", default="", help="append JSON lines here")
+    ap.add_argument("--graph", action="store_true",
+                    help="time each candidate's launches as one HIP graph replay (as bench.py "
+                         "does by default) instead of host launches")
     args = ap.parse_args()
 
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -53,7 +56,7 @@ def main():
     td = torch_dtype(dtype)
     B0 = (torch.randn(n, k, device=dev) / math.sqrt(max(k, 1))).to(td)
     a0 = torch.randn(k, device=dev).to(td)
-    nbuf = int(min(64, max(2, math.ceil((1 << 30) / max(2.0 * n * k, 1.0)))))
+    nbuf = int(min(4096, max(2, math.ceil((1 << 30) / max(2.0 * n * k, 1.0)))))
     Bs = [B0] + [B0.clone() for _ in range(nbuf - 1)]
     As = [a0.clone() for _ in range(nbuf)]
     Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]
@@ -90,6 +93,22 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     times = {i: [] for i in range(len(cands))}
+    graphs = {}
+    if args.graph:
+        # one graph per candidate, captured once (the forced configuration is
+        # baked into the captured launches)
+        side = torch.cuda.Stream(dev)
+        for i, (v, gr, kq, cfg) in enumerate(cands):
+            g.force_config(v, gr, kq)
+            gph = torch.cuda.CUDAGraph()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(gph, stream=side):
+                    for j in range(args.steps):
+                        mbd.gemv_run(g.h, *P[j % nbuf], n, k, dtype, side.cuda_stream)
+            stream.wait_stream(side)
+            graphs[i] = gph
+        torch.cuda.synchronize()
     for rnd in range(args.rounds):
         for i, (v, gr, kq, cfg) in enumerate(cands):
             g.force_config(v, gr, kq)
@@ -99,8 +118,11 @@ def main():
             e1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record(stream)
-            for j in range(args.steps):
-                mbd.gemv_run(g.h, *P[j % nbuf], n, k, dtype, sp)
+            if args.graph:
+                graphs[i].replay()
+            else:
+                for j in range(args.steps):
+                    mbd.gemv_run(g.h, *P[j % nbuf], n, k, dtype, sp)
             e1.record(stream)
             torch.cuda.synchronize()
             times[i].append(e0.elapsed_time(e1) * 1e3 / args.steps)
