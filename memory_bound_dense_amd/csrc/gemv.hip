@@ -192,7 +192,7 @@ int find_variant(const Plan& p) {
 //     the best in that sweep but for one shape, 19%).
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
 //     wave (a read once for both) when n >= 1024 and k >= 6144; a row of at
-//     most 8 steps goes to one wave; longer rows are split along k inside a
+//     most 8 steps goes to one wave (two load slots for rows of 1-2 steps); longer rows are split along k inside a
 //     workgroup until every wave has at most 4 steps (one batch of loads:
 //     measured best on MI355X), further (down to two steps per slice) while
 //     the grid has fewer than 4096 waves.  Two exceptions: rows of >= 96
@@ -242,6 +242,11 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // bf16 below 4096 rows two batches of 4 steps (bf16's widening costs twice
   // the vector work of fp16's mixed FMA; measured on MI355X: one batch is
   // 2-3.4% faster from 4096 rows up, two are up to 2% faster below)
+  // rows of one or two steps (k <= 1024): two load slots, not more slots
+  // that would only be skipped (measured on MI355X under graph replay:
+  // (1024, 1024) 2.75 -> 2.45 us, (256, 512) 2.64 -> 2.35 us)
+  const int64_t nsteps = nfull + (k % mbd::kStep != 0 ? 1 : 0);
+  if (R == 1 && nsteps <= 2) return Plan{1, 2, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
   if (R == 1 && nfull <= 8)
     return Plan{1, (dtype == GEMV_F16 || n >= 4096) ? 8 : 4, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // up to 16 steps and at most 768 rows: four slices in four-wave workgroups

@@ -34,7 +34,7 @@ def shape_of(info):
 # a_mode 0 = a staged in LDS, 1 = a through the caches, 2 = the realigning
 # kernel's shifted LDS copies
 WORKLOAD_PLANS = {
-    "tiny_256x512_f16": (1, 8, 4, 1, 1, 0),
+    "tiny_256x512_f16": (1, 2, 4, 1, 1, 0),
     "gemv_18432x7168_f16": (2, 4, 4, 4, 1, 0),
     "gemv_7168x16384_bf16": (2, 4, 8, 8, 1, 0),
     "sweep_4096x4096_f16": (1, 8, 4, 1, 1, 0),
@@ -54,7 +54,7 @@ WORKLOAD_PLANS = {
     "large_28672x8192_bf16": (2, 4, 4, 4, 1, 0),
     "large_57344x7168_f16": (2, 4, 4, 4, 1, 0),
     "large_57344x7168_bf16": (2, 4, 4, 4, 1, 0),
-    "square_1024x1024_f16": (1, 8, 4, 1, 1, 0),
+    "square_1024x1024_f16": (1, 2, 4, 1, 1, 0),
 }
 
 
@@ -135,6 +135,10 @@ def test_plan_misaligned_tiers(n, k, want):
     (256, 5120, (1, 4, 4, 4, 1, 0)),
     (1000, 8192, (1, 4, 8, 8, 1, 0)),      # more rows: the general split
     (768, 4096, (1, 8, 4, 1, 1, 0)),       # <= 8 steps: one wave per row
+    (1024, 1024, (1, 2, 4, 1, 1, 0)),      # 1-2 steps: two load slots
+    (256, 512, (1, 2, 4, 1, 1, 0)),
+    (3000, 1000, (1, 2, 4, 1, 1, 0)),
+    (3000, 1536, (1, 8, 4, 1, 1, 0)),      # 3 steps
 ])
 def test_plan_aligned_rules(n, k, want):
     assert shape_of(plan(n, k, F16)[1]) == want, (n, k)
