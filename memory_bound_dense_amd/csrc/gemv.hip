@@ -191,16 +191,18 @@ int find_variant(const Plan& p) {
 //     take the plan of 4 as it stands, with unaligned loads (within 5% of
 //     the best in that sweep but for one shape, 19%).
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
-//     wave (a read once for both) when n >= 1024 and k >= 6144; a row of at
-//     most 8 steps goes to one wave (two load slots for rows of 1-2 steps); longer rows are split along k inside a
-//     workgroup until every wave has at most 4 steps (one batch of loads:
-//     measured best on MI355X), further (down to two steps per slice) while
-//     the grid has fewer than 4096 waves.  Two exceptions: rows of >= 96
-//     steps with n >= 1536 are not split (two rows per one-wave workgroup),
-//     and up to 768 rows of 9..16 steps take four slices in four-wave
-//     workgroups.  (A tuner sweep over n = 256..3072, k = 4096..65536 on
-//     MI355X: this rule is within 1.7% of the best compiled plan on average,
-//     12% at worst; without the two exceptions 2.8% and 12.6%.)
+//     wave (a read once for both) when n >= 896 and k >= 6144; a row of at
+//     most 8 steps goes to one wave in one batch (two load slots for rows of
+//     1-2 steps); longer rows are split along k inside a workgroup until
+//     every wave has at most 4 steps (one batch of loads), further (down to
+//     two steps per slice) while the grid has fewer than 2048 waves.  Two
+//     exceptions: rows of >= 96 steps with n >= 1536 are not split (two rows
+//     per one-wave workgroup), and up to 512 rows of 5..16 steps (768 rows of
+//     9..16) take four slices in four-wave workgroups.  (A tuner sweep under
+//     graph replay over n = 256..3072, k = 4096..65536, fp16 and bf16, 22
+//     candidate variants each, on MI355X: this rule is within 1.3% of the
+//     best compiled plan on average, 10% at worst; the previous one, fitted
+//     to host-launched timing, 2.7% and 24%.)
 Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned) {
   const int64_t nfull0 = k / mbd::kStep;
   const bool misaligned = k > 0 && (k % 8 != 0 || !b_aligned);
@@ -237,24 +239,22 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // very long rows (k >= 48K) and enough of them: no split, two rows per
   // one-wave workgroup (the split's per-slice combine no longer pays)
   if (nfull >= 96 && n >= 1536) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  const int R = (n >= 1024 && k >= 6144) ? 2 : 1;
-  // a row of at most 8 steps: one wave takes all of it, in one batch; for
-  // bf16 below 4096 rows two batches of 4 steps (bf16's widening costs twice
-  // the vector work of fp16's mixed FMA; measured on MI355X: one batch is
-  // 2-3.4% faster from 4096 rows up, two are up to 2% faster below)
+  const int R = (n >= 896 && k >= 6144) ? 2 : 1;
   // rows of one or two steps (k <= 1024): two load slots, not more slots
   // that would only be skipped (measured on MI355X under graph replay:
   // (1024, 1024) 2.75 -> 2.45 us, (256, 512) 2.64 -> 2.35 us)
   const int64_t nsteps = nfull + (k % mbd::kStep != 0 ? 1 : 0);
   if (R == 1 && nsteps <= 2) return Plan{1, 2, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  if (R == 1 && nfull <= 8)
-    return Plan{1, (dtype == GEMV_F16 || n >= 4096) ? 8 : 4, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  // up to 16 steps and at most 768 rows: four slices in four-wave workgroups
-  if (R == 1 && nfull <= 16 && n <= 768) return Plan{1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
+  // up to 512 rows of 5..16 steps, and up to 768 rows of 9..16: four slices
+  // in four-wave workgroups
+  if (R == 1 && nfull <= 16 && ((n <= 512 && nfull >= 5) || (n <= 768 && nfull > 8)))
+    return Plan{1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
+  // otherwise a row of at most 8 steps goes to one wave, in one batch
+  if (R == 1 && nfull <= 8) return Plan{1, 8, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
   const int smax = R == 1 ? 16 : 8;
   int S = 1;
   while (S < smax && (nfull + S - 1) / S > 4) S *= 2;   // at most 4 steps per wave: one batch
-  while (S < smax && ((n + R - 1) / R) * S < 4096 && nfull >= 2 * (2 * S)) S *= 2;
+  while (S < smax && ((n + R - 1) / R) * S < 2048 && nfull >= 2 * (2 * S)) S *= 2;
   // two rows per wave: one row group per workgroup (S waves; measured 0.4-5%
   // faster than two row groups of 8 waves at S = 4 on MI355X, the headline
   // (18432, 7168) fp16 among them)

@@ -48,7 +48,7 @@ WORKLOAD_PLANS = {
     "sweep_4096x14336_f16": (1, 4, 4, 1, 1, 0),
     "sweep_4096x14336_bf16": (1, 4, 4, 1, 1, 0),
     "ragged_64x65536_bf16": (1, 4, 8, 8, 1, 1),
-    "ragged_1000x7000_bf16": (1, 4, 8, 4, 1, 0),
+    "ragged_1000x7000_bf16": (2, 4, 4, 4, 1, 0),
     "ragged_18433x7169_bf16": (1, 4, 8, 1, 2, 0),
     "large_28672x8192_f16": (2, 4, 4, 4, 1, 0),
     "large_28672x8192_bf16": (2, 4, 4, 4, 1, 0),
@@ -110,9 +110,10 @@ def test_plan_grids_of_the_production_shapes():
     (3072, 12289, (2, 4, 1, 1, 1, 0)),
     (2048, 32769, (2, 4, 1, 1, 1, 0)),
     (2048, 65537, (2, 4, 1, 1, 1, 0)),
-    # fewer rows: the split plan of aligned rows (two rows per wave from 1024)
+    # fewer rows: the split plan of aligned rows (two rows per wave from 896)
     (1024, 16385, (2, 4, 8, 8, 1, 0)),
-    (1000, 16385, (1, 4, 8, 8, 1, 0)),
+    (1000, 16385, (2, 4, 8, 8, 1, 0)),
+    (800, 16385, (1, 4, 8, 8, 1, 0)),
     # fewer than 3072 rows of k <= 8192: the plan of aligned rows as well
     (2048, 5121, (1, 4, 8, 4, 1, 0)),
     (2048, 7169, (2, 4, 4, 4, 1, 0)),
@@ -133,20 +134,24 @@ def test_plan_misaligned_tiers(n, k, want):
     (1024, 65536, (2, 4, 8, 8, 1, 0)),     # fewer rows: still split
     (768, 8192, (1, 4, 4, 4, 1, 0)),       # <= 768 rows of 9..16 steps: 4 slices, 4 waves
     (256, 5120, (1, 4, 4, 4, 1, 0)),
-    (1000, 8192, (1, 4, 8, 8, 1, 0)),      # more rows: the general split
+    (800, 8192, (1, 4, 8, 4, 1, 0)),       # more rows: the general split
+    (1000, 8192, (2, 4, 8, 8, 1, 0)),      # n >= 896, k >= 6144: two rows per wave
     (768, 4096, (1, 8, 4, 1, 1, 0)),       # <= 8 steps: one wave per row
     (1024, 1024, (1, 2, 4, 1, 1, 0)),      # 1-2 steps: two load slots
     (256, 512, (1, 2, 4, 1, 1, 0)),
     (3000, 1000, (1, 2, 4, 1, 1, 0)),
     (3000, 1536, (1, 8, 4, 1, 1, 0)),      # 3 steps
+    (512, 4096, (1, 4, 4, 4, 1, 0)),       # <= 512 rows of 5..8 steps: 4 slices, 4 waves
+    (640, 4096, (1, 8, 4, 1, 1, 0)),
 ])
 def test_plan_aligned_rules(n, k, want):
     assert shape_of(plan(n, k, F16)[1]) == want, (n, k)
 
 
 @pytest.mark.parametrize("n,k,want", [
-    (4096, 4096, (1, 8, 4, 1, 1, 0)),      # bf16, <= 8 steps, n >= 4096: one batch of 8
-    (2048, 4096, (1, 4, 4, 1, 1, 0)),      # below 4096 rows: two batches of 4
+    (4096, 4096, (1, 8, 4, 1, 1, 0)),      # bf16, <= 8 steps: one batch of 8 as for fp16
+    (2048, 4096, (1, 8, 4, 1, 1, 0)),
+    (1000, 4096, (1, 8, 4, 1, 1, 0)),
 ])
 def test_plan_bf16_short_rows(n, k, want):
     assert shape_of(plan(n, k, BF16)[1]) == want, (n, k)
