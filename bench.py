@@ -197,7 +197,8 @@ class Launcher:
         self.graphs = []
         self.host_us = None
         if graph:
-            windows = 1 if steps >= nbuf else -(-nbuf // steps)
+            # (at most 256 windows: a very short K covers fewer copies)
+            windows = 1 if steps >= nbuf else min(256, -(-nbuf // steps))
             side = torch.cuda.Stream(dev)
             for w in range(windows):
                 gph = torch.cuda.CUDAGraph()
