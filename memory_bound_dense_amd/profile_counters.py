@@ -176,9 +176,14 @@ def summarize_trace(stats_csv, trace_csv, command, out, last=0):
                          "(the timed region), us:" % last)
             for nm, d in durs.items():
                 if len(d) >= last:
-                    t = d[-last:]
-                    lines.append("  %s: avg %.3f median %.3f min %.3f max %.3f" % (
-                        nm, statistics.fmean(t), statistics.median(t), min(t), max(t)))
+                    t = sorted(d[-last:])
+                    med = statistics.median(t)
+                    sd = statistics.pstdev(t)
+                    lines.append("  %s: avg %.3f median %.3f min %.3f max %.3f p10 %.3f p90 %.3f "
+                                 "sd/median %.4f%s" % (
+                                     nm, statistics.fmean(t), med, t[0], t[-1],
+                                     t[int(0.1 * (len(t) - 1))], t[int(0.9 * (len(t) - 1))],
+                                     sd / med, "  (> 0.10: contaminated)" if sd / med > 0.10 else ""))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
