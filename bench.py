@@ -55,14 +55,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     from memory_bound_dense_amd.profile_counters import kernel_source_hash as ksh
-    return ksh()
+    return ksh(sources)
 
 
-def read_traffic(workload, n_launch_bytes, plan):
+def read_traffic(workload, n_launch_bytes, plan, sources=None):
     """HBM traffic per launch from the committed counter summary, if it was
-    taken on the current kernel source and the same plan; else None."""
+    taken on the current kernel source (`sources`: the GEMV's by default)
+    and the same plan; else None."""
     path = os.path.join(ROOT, "profiles", "%s.counters.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -71,7 +72,7 @@ def read_traffic(workload, n_launch_bytes, plan):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash() or kv.get("plan") != plan:
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(sources) or kv.get("plan") != plan:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -232,7 +233,9 @@ def gla_bench(args):
     import numpy as np
     import torch
     import memory_bound_dense_amd as mbd
-    from gemv_inputs import DTYPE_NAMES, GLA_BATCHED, GLA_DECODE, gla_inputs, torch_dtype
+    from gemv_inputs import (DTYPE_NAMES, GLA_BATCHED, GLA_DECODE, gla_inputs, gla_step_bytes,
+                             torch_dtype)
+    from memory_bound_dense_amd.profile_counters import GLA_PLAN, GLA_SOURCES
     wl = {w[0]: w for w in (GLA_DECODE, GLA_BATCHED)}.get(args.workload, GLA_DECODE)
     name, bh, dk, dv, dtype = wl
     dev = torch.device("cuda", 0)
@@ -245,7 +248,7 @@ def gla_bench(args):
     nbuf = rotation(state_bytes)
     Ss = [S0] + [S0.clone() for _ in range(nbuf - 1)]
     os_ = [torch.empty((bh, dv), dtype=td, device=dev) for _ in range(nbuf)]
-    step_bytes = 2 * state_bytes + 2 * bh * (3 * dk + 2 * dv)
+    step_bytes = gla_step_bytes(bh, dk, dv)
     g = mbd.Gemv()
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -306,7 +309,7 @@ def gla_bench(args):
            "roofline": {"bound": "hbm", "achieved": round(step_bytes / avg_us / 1e3, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(step_bytes / avg_us / 1e3 / HBM_PEAK_GBS, 4),
-                        "traffic": None}}
+                        "traffic": read_traffic(name, step_bytes, GLA_PLAN, GLA_SOURCES)}}
     if ceiling:
         out["stream_copy_probe"] = ceiling
     g.close()

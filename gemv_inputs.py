@@ -125,3 +125,17 @@ def gla_inputs(bh: int, dk: int, dv: int, dtype: int, seed: int = 0):
 
 GLA_DECODE = ("gla_decode_b1h32_128x128_bf16", 32, 128, 128, BF16)
 GLA_BATCHED = ("gla_decode_b64h32_128x128_bf16", 64 * 32, 128, 128, BF16)
+GLA_WORKLOADS = [GLA_DECODE, GLA_BATCHED]
+
+
+def find_gla_workload(name):
+    for w in GLA_WORKLOADS:
+        if w[0] == name:
+            return w
+    return None
+
+
+def gla_step_bytes(bh: int, dk: int, dv: int, elem_bytes: int = 2) -> int:
+    """Bytes one GLA decode step must move at least once: the fp32 state read
+    and written, q, k, gk (bh x dk) and v, o (bh x dv)."""
+    return 8 * bh * dk * dv + elem_bytes * bh * (3 * dk + 2 * dv)

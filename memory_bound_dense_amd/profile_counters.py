@@ -7,6 +7,9 @@ Programs (run as the profiled program, after ``rocprofv3 ... --``):
       N launches of the GEMV in its automatic configuration (or the one given
       by --variant/--grid), rotating over copies of the inputs that exceed
       1 GiB (as bench.py does).
+  python3 -m memory_bound_dense_amd.profile_counters gla --workload NAME --launches N
+      N in-place GLA decode steps of a workload, rotating over > 1 GiB of
+      state copies.
   python3 -m memory_bound_dense_amd.profile_counters copy --bytes X --launches N
       N device-to-device copies of X bytes (a plain copy kernel of known
       traffic: X bytes read and X bytes written), to calibrate the counters.
@@ -36,7 +39,15 @@ ROOT = os.path.dirname(PKG)
 # workload runs (the plan) is recorded and checked separately
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemv_kernel.h", "gemv_staged.h")] + \
     [os.path.join(PKG, "build.py")]
+# the GLA step: its device code (which uses gemv_kernel.h's helpers), the host
+# code that picks its launch, and the build flags
+GLA_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gla_kernel.h", "gla.hip", "gemv_kernel.h")] + \
+    [os.path.join(PKG, "build.py")]
 GEMV_KERNEL = "gemv_"              # every GEMV kernel (row, realigning, row-per-lane)
+GLA_KERNEL = "gla_decode_kernel"
+# the GLA step's launch is picked on the host from the shape; the summary's
+# hash covers that host code, so its plan line is this fixed text
+GLA_PLAN = "the launch gla_decode_step picks (its host code is hashed above)"
 COPY_KERNEL = "copyBuffer"
 
 
@@ -48,11 +59,12 @@ def _strip_comments(text):
     return " ".join(text.split())
 
 
-def kernel_source_hash():
-    """Hash of the GEMV device code and its build flags, blind to comments and
-    whitespace: a summary taken on other code is not reused."""
+def kernel_source_hash(sources=None):
+    """Hash of the GEMV device code and its build flags (or of `sources`),
+    blind to comments and whitespace: a summary taken on other code is not
+    reused."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (KERNEL_SOURCES if sources is None else sources):
         with open(p) as f:
             h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
@@ -107,6 +119,39 @@ def run_gemv(workload, launches, variant=-1, grid=0):
     g.close()
     print("gemv %s: %d launches, variant %d grid %d x %d" % (name, launches, v, grid, kgroups),
           flush=True)
+
+
+def run_gla(workload, launches):
+    """`launches` GLA decode steps of a workload, the state updated in place,
+    rotating over copies of the state that exceed 1 GiB (as bench.py does)."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+    import memory_bound_dense_amd as mbd
+    from gemv_inputs import find_gla_workload, gla_inputs, torch_dtype
+    name, bh, dk, dv, dtype = find_gla_workload(workload)
+    dev = torch.device("cuda", 0)
+    td = torch_dtype(dtype)
+    q, k, v, gk, S = gla_inputs(bh, dk, dv, dtype, seed=0)
+    t = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(td)
+    qd, kd, vd, gd = t(q), t(k), t(v), t(gk)
+    S0 = torch.from_numpy(S).to(dev)
+    nbuf = int(min(4096, max(2, math.ceil((1 << 30) / (4.0 * bh * dk * dv)))))
+    Ss = [S0] + [S0.clone() for _ in range(nbuf - 1)]
+    os_ = [torch.empty((bh, dv), dtype=td, device=dev) for _ in range(nbuf)]
+    torch.cuda.synchronize()
+    g = mbd.Gemv()
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(launches):
+        p = Ss[i % nbuf].data_ptr()
+        rc = mbd.gla_decode_step(g.h, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), gd.data_ptr(),
+                                 p, p, os_[i % nbuf].data_ptr(), bh, dk, dv,
+                                 1.0 / math.sqrt(dk), dtype, sp)
+        if rc != 0:
+            raise mbd.GemvError(rc, "gla_decode_step")
+    torch.cuda.synchronize()
+    g.close()
+    print("gla %s: %d launches" % (name, launches), flush=True)
 
 
 def run_copy(nbytes, launches):
@@ -191,22 +236,35 @@ def summarize_trace(stats_csv, trace_csv, command, out, last=0):
 
 def summarize_counters(workload, fetch, write, copy_fetch, copy_write, copy_bytes, commands, out):
     sys.path.insert(0, ROOT)
-    from gemv_inputs import algorithmic_bytes, find_workload
-    name, n, k, dtype, dist = find_workload(workload)
-    alg = algorithmic_bytes(n, k)
-    f_g = statistics.median(counter_per_dispatch(fetch, GEMV_KERNEL, "FETCH_SIZE")) * 1024
-    w_g = statistics.median(counter_per_dispatch(write, GEMV_KERNEL, "WRITE_SIZE")) * 1024
+    from gemv_inputs import algorithmic_bytes, find_gla_workload, find_workload, gla_step_bytes
+    gla = find_gla_workload(workload)
+    if gla is not None:
+        name, bh, dk, dv, dtype = gla
+        n = bh * dv                     # outputs: o; bytes per output below are per o element
+        alg = gla_step_bytes(bh, dk, dv)
+        kernel, sources = GLA_KERNEL, GLA_SOURCES
+        what = "%s (bh=%d dk=%d dv=%d)" % (name, bh, dk, dv)
+        plan = GLA_PLAN
+    else:
+        name, n, k, dtype, dist = find_workload(workload)
+        alg = algorithmic_bytes(n, k)
+        kernel, sources = GEMV_KERNEL, None
+        what = "%s (n=%d k=%d)" % (name, n, k)
+        plan = workload_plan_signature(n, k, dtype)
+    f_g = statistics.median(counter_per_dispatch(fetch, kernel, "FETCH_SIZE")) * 1024
+    w_g = statistics.median(counter_per_dispatch(write, kernel, "WRITE_SIZE")) * 1024
     f_c = statistics.median(counter_per_dispatch(copy_fetch, COPY_KERNEL, "FETCH_SIZE")) * 1024
     w_c = statistics.median(counter_per_dispatch(copy_write, COPY_KERNEL, "WRITE_SIZE")) * 1024
     sf, sw = copy_bytes / f_c, copy_bytes / w_c
     traffic = f_g * sf + w_g * sw
     lines = [
-        "# HBM traffic of the GEMV kernel from rocprofv3 counters (median per dispatch)",
-        "workload: %s (n=%d k=%d)" % (name, n, k),
+        "# HBM traffic of the %s kernel from rocprofv3 counters (median per dispatch)" % (
+            "GLA decode" if gla is not None else "GEMV"),
+        "workload: %s" % what,
         "commands:",
     ] + ["  " + c for c in commands] + [
-        "kernel_source_sha256_16: %s" % kernel_source_hash(),
-        "plan: %s" % workload_plan_signature(n, k, dtype),
+        "kernel_source_sha256_16: %s" % kernel_source_hash(sources),
+        "plan: %s" % plan,
         "copy_kernel_bytes: %d" % copy_bytes,
         "copy_fetch_counted_bytes: %.0f" % f_c,
         "copy_write_counted_bytes: %.0f" % w_c,
@@ -233,6 +291,9 @@ def main():
     p.add_argument("--launches", type=int, default=20)
     p.add_argument("--variant", type=int, default=-1, help="force this variant (-1: automatic)")
     p.add_argument("--grid", type=int, default=0, help="grid of a forced variant (0: full)")
+    p = sub.add_parser("gla")
+    p.add_argument("--workload", default="gla_decode_b64h32_128x128_bf16")
+    p.add_argument("--launches", type=int, default=20)
     p = sub.add_parser("copy")
     p.add_argument("--bytes", type=int, default=256 << 20)
     p.add_argument("--launches", type=int, default=10)
@@ -255,6 +316,8 @@ def main():
     a = ap.parse_args()
     if a.cmd == "gemv":
         run_gemv(a.workload, a.launches, a.variant, a.grid)
+    elif a.cmd == "gla":
+        run_gla(a.workload, a.launches)
     elif a.cmd == "copy":
         run_copy(a.bytes, a.launches)
     elif a.cmd == "summarize-trace":
