@@ -61,3 +61,27 @@ def test_json_line_gla():
     out = _line(_bench("--op", "gla", "--steps", "20", "--warmup", "5", "--no-probe"))
     assert out["config"]["workload"] == "gla_decode_b1h32_128x128_bf16"
     assert out["config"]["launch"] == "graph" and out["roofline"]["frac"] > 0
+
+
+def test_rotation_exceeds_the_infinity_cache():
+    import bench
+    for nbytes in (263680, 2 << 20, 8 << 20, 264292352, 940 << 20):
+        m = bench.rotation(nbytes)
+        assert m >= 2 and m <= bench.MAX_COPIES
+        assert m * nbytes > (1 << 30), (nbytes, m)          # > 1 GiB between two uses of a copy
+    assert bench.rotation(1) == bench.MAX_COPIES
+
+
+def test_host_launches_keep_rotating_across_runs():
+    import bench
+
+    class FakeStream:
+        cuda_stream = None
+
+    seen = []
+    lau = bench.Launcher(lambda i, sp: seen.append(i), 3, 5, FakeStream(), None, graph=False)
+    for _ in range(4):
+        lau.run()
+    # the launch index keeps counting, so copies are used round robin: copy i % 5
+    assert seen == list(range(12))
+    assert [i % 5 for i in seen[:10]] == [0, 1, 2, 3, 4, 0, 1, 2, 3, 4]
