@@ -187,9 +187,9 @@ int find_variant(const Plan& p) {
 //     otherwise the plan of 4.  (Measured on MI355X over misaligned shapes
 //     with k from 4097 to 65537: the realigning kernel leads up to k ~ 14K
 //     and then falls behind, 13-40% at k >= 16K, as its LDS cuts the waves
-//     per CU.)  Misaligned rows up to k = 8192 and fewer than 3072 of them
-//     take the plan of 4 as it stands, with unaligned loads (within 5% of
-//     the best in that sweep but for one shape, 19%).
+//     per CU.)  Misaligned rows up to k = 8192 and fewer than 3072 of them:
+//     from 768 rows with at most 12 full steps, one row per wave in two-wave
+//     workgroups; otherwise the plan of 4 as it stands, with unaligned loads.
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
 //     wave (a read once for both) when n >= 896 and k >= 6144; a row of at
 //     most 8 steps goes to one wave in one batch (two load slots for rows of
@@ -217,6 +217,12 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
                     : (k > 12 * mbd::kStep && l4 <= (size_t)40 * 1024) ? pr4 : pr;
     if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
   }
+  // fewer misaligned rows (768..3071) of at most 12 full steps: one row per
+  // wave in two-wave workgroups, unaligned loads (measured under graph
+  // replay over n = 768..2560, k = 2049..6143 bf16: 2.6% off the best
+  // compiled plan on average, 7.8% at worst, against 6.8% and 46% for (4))
+  if (misaligned && k <= kShortMisaligned && n >= 768 && n < 3072 && nfull0 <= 12)
+    return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
   if (misaligned && k > kShortMisaligned && n >= 4096) {
     const Plan p16 = {1, 4, 16, 1, mbd::A_LDS_SHIFTED, kPolNT, 0, 1};
     const size_t l = lds_bytes(kVariants[find_variant(p16)].info, k);

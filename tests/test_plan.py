@@ -114,8 +114,11 @@ def test_plan_grids_of_the_production_shapes():
     (1024, 16385, (2, 4, 8, 8, 1, 0)),
     (1000, 16385, (2, 4, 8, 8, 1, 0)),
     (800, 16385, (1, 4, 8, 8, 1, 0)),
-    # fewer than 3072 rows of k <= 8192: the plan of aligned rows as well
-    (2048, 5121, (1, 4, 8, 4, 1, 0)),
+    # 768..3071 rows of at most 12 full steps: one row per two-wave workgroup
+    (2048, 5121, (1, 4, 2, 1, 1, 0)),
+    (768, 2049, (1, 4, 2, 1, 1, 0)),
+    (2560, 6143, (1, 4, 2, 1, 1, 0)),
+    # otherwise, below 3072 rows of k <= 8192, the plan of aligned rows
     (2048, 7169, (2, 4, 4, 4, 1, 0)),
     (512, 5121, (1, 4, 4, 4, 1, 0)),
 ])
