@@ -162,10 +162,14 @@ int find_variant(const Plan& p) {
 
 // The general rule, for shapes without a measured entry, in this order:
 //  1. rows that do not start on 16-byte boundaries (k % 8 != 0, or B itself
-//     misaligned) and at least 3072 of them.  Up to k = 8192: for up to 6144
+//     misaligned) and at least 3072 of them.  Up to k = 8192: for up to 8192
 //     rows (or rows of at most 3 steps) one row per wave, a staged in LDS
-//     and B read with unaligned 16-byte loads, on at most 1536 four-wave
-//     workgroups; beyond that the realigning kernel (aligned granules of B
+//     and B read with unaligned 16-byte loads, on at most 2048 four-wave
+//     workgroups (one full occupancy; 1536 for rows of at most 3 steps, and
+//     for rows of 4..16 steps 6144 < n <= 8192 lost 2-8% on 1536 under
+//     graph replay); rows of 4 full steps and a partial one from 4096 rows
+//     (whose second batch in the one-row kernel would carry only the partial
+//     step), and any rows beyond those bounds, take the realigning kernel (aligned granules of B
 //     from each row's 128-byte line, a staged twice in LDS) in eight-wave
 //     workgroups: two steps per batch on a persistent grid of 1024 (8192
 //     waves: 32 per CU, one full occupancy), and for rows of more than 12
@@ -210,10 +214,13 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // 1.
   if (misaligned && k <= kShortMisaligned && n >= 3072) {
     const Plan pl = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 1536, 1};
+    const Plan pl2 = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 2048, 1};
     const Plan pr = {1, 2, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1024, 1};
     const Plan pr4 = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
     const size_t l4 = lds_bytes(kVariants[find_variant(pr4)].info, k);
-    const Plan& p = (n <= 6144 || k <= 3 * mbd::kStep) ? pl
+    const Plan& p = k <= 3 * mbd::kStep ? pl
+                    : (k > 4 * mbd::kStep && k < 5 * mbd::kStep && n >= 4096) ? pr
+                    : n <= 8192 ? pl2
                     : (k > 12 * mbd::kStep && l4 <= (size_t)40 * 1024) ? pr4 : pr;
     if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
   }

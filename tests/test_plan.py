@@ -77,22 +77,35 @@ def test_plan_grids_of_the_production_shapes():
     # more than 12 steps, else 1024 (8192 waves)
     assert plan(18433, 7169, BF16)[0].grid == 1536
     assert plan(18433, 4097, BF16)[0].grid == 1024
-    # one row per wave, a in LDS: at most 1536 workgroups
+    # one row per wave, a in LDS: at most 2048 workgroups (1536 for rows of
+    # at most 3 steps)
     assert plan(3072, 7169, BF16)[0].grid == 768
+    assert plan(8192, 4097, BF16)[0].grid == 2048
+    assert plan(7000, 7169, BF16)[0].grid == 1750
     assert plan(16384, 1025, BF16)[0].grid == 1536
+    assert plan(8192, 1025, BF16)[0].grid == 1536
     # 64 rows: k shared by 4 workgroups per row range
     assert plan(64, 65536, BF16)[0].kgroups == 4
 
 
 @pytest.mark.parametrize("n,k,want", [
-    # >= 3072 rows of k <= 8192: up to 6144 rows, or rows of <= 3 steps, one
+    # >= 3072 rows of k <= 8192: up to 8192 rows, or rows of <= 3 steps, one
     # row per wave with a in LDS and unaligned B loads
     (3072, 7169, (1, 4, 4, 1, 0, 0)),
     (6144, 4097, (1, 4, 4, 1, 0, 0)),
+    (6145, 1545, (1, 4, 4, 1, 0, 0)),
+    (8192, 8191, (1, 4, 4, 1, 0, 0)),
     (16384, 1025, (1, 4, 4, 1, 0, 0)),
     (65536, 1535, (1, 4, 4, 1, 0, 0)),
-    # more rows of 4..12 steps: the realigning kernel, two steps per batch
-    (6145, 1545, (1, 2, 8, 1, 2, 0)),
+    # more rows of 4..12 steps, or from 4096 rows those of 4 full steps and a
+    # partial one: the realigning kernel, two steps per batch
+    (8193, 1545, (1, 2, 8, 1, 2, 0)),
+    (4096, 2051, (1, 2, 8, 1, 2, 0)),
+    (6144, 2053, (1, 2, 8, 1, 2, 0)),
+    (8192, 2559, (1, 2, 8, 1, 2, 0)),
+    (4095, 2049, (1, 4, 4, 1, 0, 0)),
+    (4096, 2561, (1, 4, 4, 1, 0, 0)),
+    (4096, 1545, (1, 4, 4, 1, 0, 0)),
     (14336, 4097, (1, 2, 8, 1, 2, 0)),
     (32768, 6143, (1, 2, 8, 1, 2, 0)),
     # longer rows: four steps per batch while its LDS is <= 40 KiB
