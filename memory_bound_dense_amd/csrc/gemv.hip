@@ -146,6 +146,9 @@ struct TunedShape {
 };
 const TunedShape kTuned[] = {
     {4096, 14336, {1, 4, 4, 1, mbd::A_CACHED, kPolNT, 512, 1}},
+    // misaligned rows (k odd): the realigning kernel in 8-wave workgroups on
+    // 1536 workgroups, 2-4% ahead of the rule's 16-wave plan on three boxes
+    {18433, 7169, {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1}},
 };
 
 int find_variant(const Plan& p) {
@@ -172,8 +175,12 @@ int find_variant(const Plan& p) {
 //     step), and any rows beyond those bounds, take the realigning kernel (aligned granules of B
 //     from each row's 128-byte line, a staged twice in LDS) in eight-wave
 //     workgroups: two steps per batch on a persistent grid of 1024 (8192
-//     waves: 32 per CU, one full occupancy), and for rows of more than 12
-//     steps four per batch on a grid of 1536 while its LDS is <= 40 KiB.
+//     waves: 32 per CU, one full occupancy); rows of more than 12 steps go
+//     to its 16-wave form (one row per wave) on 1024 workgroups (graph-
+//     replayed sweeps over n = 12288..65536, k = 6147..8001, 21 bf16 shapes:
+//     1.4% off the best compiled plan on average, 4.7% at worst; the 8-wave
+//     form on 1536 workgroups taken before: 3.7% and 8.9%; the 16-wave form
+//     on its full grid: 1.9% and 7.1%).
 //     (A tuner sweep over 70 misaligned bf16 shapes with n = 512..65536,
 //     k = 1025..8001 on MI355X: within 3.5% of the best compiled plan on
 //     average; the realigning kernel alone, with four steps per batch on a
@@ -216,12 +223,11 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     const Plan pl = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 1536, 1};
     const Plan pl2 = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 2048, 1};
     const Plan pr = {1, 2, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1024, 1};
-    const Plan pr4 = {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1};
-    const size_t l4 = lds_bytes(kVariants[find_variant(pr4)].info, k);
+    const Plan p16 = {1, 4, 16, 1, mbd::A_LDS_SHIFTED, kPolNT, 1024, 1};
     const Plan& p = k <= 3 * mbd::kStep ? pl
                     : (k > 4 * mbd::kStep && k < 5 * mbd::kStep && n >= 4096) ? pr
                     : n <= 8192 ? pl2
-                    : (k > 12 * mbd::kStep && l4 <= (size_t)40 * 1024) ? pr4 : pr;
+                    : k > 12 * mbd::kStep ? p16 : pr;
     if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
   }
   // fewer misaligned rows (768..3071) of at most 12 full steps: one row per

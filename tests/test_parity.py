@@ -423,11 +423,12 @@ def test_realigned_rows_do_not_leak(g, dtype):
 def test_auto_plan_realigns_misaligned_rows(g):
     """Misaligned rows: from 3072 rows up to k = 8192, one row per wave with
     a in LDS (up to 8192 rows, or rows of <= 3 steps), else the realigning
-    kernel with 8 waves per workgroup; longer rows the realigning kernel
+    kernel with 8 waves per workgroup (16 for rows of more than 12 steps;
+    8 for the measured (18433, 7169)); longer rows the realigning kernel
     with 16 waves while its LDS is <= 70 KiB, then unaligned loads (two rows
     per one-wave workgroup); fewer rows the plan of aligned rows."""
     for n, k, want in [(18433, 7169, (2, 8)), (3072, 7169, (0, 4)), (16384, 1025, (0, 4)),
-                       (8192, 7169, (0, 4)), (8193, 7169, (2, 8)),
+                       (8192, 7169, (0, 4)), (8193, 7169, (2, 16)), (8193, 6143, (2, 8)),
                        (8192, 12289, (2, 16)), (8192, 16383, (1, 1)), (100, 1000, (1, None))]:
         v, grid, q = g.query_config(n, k, BF16)
         info = mbd.gemv_variant_info(v)[1]

@@ -73,10 +73,14 @@ def test_plan_grids_of_the_production_shapes():
     assert plan(7168, 16384, BF16)[0].grid == 3584
     # the measured entry for (4096, 14336): 512 workgroups, 2 rows per wave
     assert plan(4096, 14336, F16)[0].grid == 512
-    # the realigning kernel's persistent grids: 1536 workgroups for rows of
-    # more than 12 steps, else 1024 (8192 waves)
+    # the realigning kernel: persistent grids of 1024 (8192 waves of its
+    # 8-wave form for rows of 4..12 steps, 16384 of its 16-wave form for
+    # longer ones), and the measured 1536 workgroups of the 8-wave form for
+    # (18433, 7169)
     assert plan(18433, 7169, BF16)[0].grid == 1536
     assert plan(18433, 4097, BF16)[0].grid == 1024
+    assert plan(18432, 7169, BF16)[0].grid == 1024
+    assert plan(12288, 7169, BF16)[0].grid == 768
     # one row per wave, a in LDS: at most 2048 workgroups (1536 for rows of
     # at most 3 steps)
     assert plan(3072, 7169, BF16)[0].grid == 768
@@ -108,10 +112,13 @@ def test_plan_grids_of_the_production_shapes():
     (4096, 1545, (1, 4, 4, 1, 0, 0)),
     (14336, 4097, (1, 2, 8, 1, 2, 0)),
     (32768, 6143, (1, 2, 8, 1, 2, 0)),
-    # longer rows: four steps per batch while its LDS is <= 40 KiB
-    (18433, 7169, (1, 4, 8, 1, 2, 0)),
-    (32768, 8121, (1, 4, 8, 1, 2, 0)),
-    (32768, 8185, (1, 2, 8, 1, 2, 0)),
+    # longer rows: its 16-wave form, one row per wave (the measured entry
+    # for (18433, 7169), the 8-wave form, is pinned with the workloads)
+    (18432, 7169, (1, 4, 16, 1, 2, 0)),
+    (16384, 6147, (1, 4, 16, 1, 2, 0)),
+    (32768, 8121, (1, 4, 16, 1, 2, 0)),
+    (32768, 8185, (1, 4, 16, 1, 2, 0)),
+    (32768, 6143, (1, 2, 8, 1, 2, 0)),
     # k > 8192: the realigning kernel with 16 waves per workgroup (n >= 4096)
     # while its LDS is <= 70 KiB
     (8192, 9217, (1, 4, 16, 1, 2, 0)),
