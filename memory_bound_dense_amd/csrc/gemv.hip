@@ -190,9 +190,16 @@ int find_variant(const Plan& p) {
 //     LDS is <= 70 KiB (k ~ 15.8K; measured: ahead by 9% at k = 14337,
 //     behind by 7% at k = 16383);
 //  2. too few rows to give the GPU 2048 waves even with 16 waves per row
-//     (n < 128): k split across workgroups as well (cross-workgroup
-//     variants; measured best for n = 32 and 64, 22-43% behind the
-//     in-workgroup split for n = 128 and 200);
+//     (n < 128), with rows of at least 32 steps: one row per 8-wave
+//     workgroup, eight k-slices; for at most 64 rows of at least 128 steps
+//     k is split across Q workgroups as well, Q = steps / 32 (one batch of
+//     4 steps per wave).  (Measured under graph replay over n = 16..127,
+//     k = 16384..65536: the cross-workgroup split, with its combine's
+//     serial latency, wins only there -- by 3-17%, best at Q = 4 for
+//     k = 65536 -- and loses 21-52% elsewhere; the 8 x 8 in-workgroup split
+//     is within 1% of the best in-workgroup plan on every shape.  Below 8
+//     rows Q is doubled: for one row Q = 8 is within 4.5% of the best
+//     compiled plan, Q = 4 12% behind.)
 //  3. misaligned rows longer than k = 8192 and not taken by 1: unaligned
 //     16-byte loads, two rows per one-wave workgroup when n >= 2048,
 //     otherwise the plan of 4.  (Measured on MI355X over misaligned shapes
@@ -241,16 +248,14 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     const size_t l = lds_bytes(kVariants[find_variant(p16)].info, k);
     if (l <= (size_t)70 * 1024 && l <= max_lds) return p16;
   }
-  // 2. 8 waves per row per workgroup, Q groups, about 2048 waves in all (more
-  // k-groups cost more than they bring on MI355X), keeping at least two
-  // 512-element steps per wave.
-  if (n * 16 < 2048 && nfull0 >= 2 * 8 * 2) {
-    int64_t Q = (2048 + n * 8 - 1) / (n * 8);
-    const int64_t qmax = nfull0 / (2 * 8);
-    if (Q > qmax) Q = qmax;
+  // 2. 8 waves per row per workgroup, Q groups sized so that every wave has
+  // one batch of 4 steps (2 steps below 8 rows, to have more waves).
+  if (n <= 64 && nfull0 >= 128) {
+    int64_t Q = nfull0 / (8 * (n < 8 ? 2 : 4));
     if (Q > 64) Q = 64;
-    if (Q * n <= (int64_t)kWsFloats && Q > 1) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
+    if (Q * n <= (int64_t)kWsFloats) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
+  if (n < 128 && nfull0 >= 32) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
   // 3.
   if (misaligned && k > kShortMisaligned && n >= 2048) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.

@@ -181,14 +181,29 @@ def test_plan_bf16_short_rows(n, k, want):
 
 
 @pytest.mark.parametrize("n,k,xwg", [
-    (32, 131072, True), (64, 65536, True), (127, 65536, True),
+    (32, 131072, True), (64, 65536, True), (1, 65536, True), (7, 65536, True), (8, 65536, True),
+    (65, 65536, False), (127, 65536, False),    # more rows: the in-workgroup split
+    (64, 65535, False), (64, 32768, False),     # shorter rows: the in-workgroup split
     (128, 32768, False), (200, 16384, False),
-    (64, 511, False), (64, 16383, False),       # too few full steps to share
+    (64, 511, False), (64, 16383, False),
 ])
 def test_plan_cross_workgroup_only_for_few_rows(n, k, xwg):
     cfg, info = plan(n, k, BF16)
     assert bool(info.cross_wg) == xwg, (n, k, shape_of(info))
     assert (cfg.kgroups > 1) == xwg
+    if xwg:
+        # k-groups sized for one batch of 4 steps per wave (8 slices each;
+        # 2 steps below 8 rows)
+        assert cfg.kgroups == min(64, (k // 512) // (16 if n < 8 else 32))
+        assert shape_of(info) == (1, 4, 8, 8, 1, 1)
+
+
+@pytest.mark.parametrize("n,k", [(127, 65536), (96, 65536), (64, 32768), (32, 16384), (1, 16384)])
+def test_plan_few_rows_split_in_workgroup(n, k):
+    # fewer than 128 rows of >= 32 steps, not split across workgroups: one
+    # row per 8-wave workgroup, eight k-slices
+    cfg, info = plan(n, k, BF16)
+    assert shape_of(info) == (1, 4, 8, 8, 1, 0) and cfg.kgroups == 1 and cfg.grid == n
 
 
 def test_plan_properties_over_a_sweep():
