@@ -441,7 +441,7 @@ def test_auto_plan_realigns_misaligned_rows(g):
 
 LONG_MIS = [(4096, 12289, BF16, 3), (4096, 16001, F16, 1), (1000, 16383, BF16, 5),
             (6144, 4097, BF16, 2), (6400, 2049, F16, 7), (3072, 1025, F16, 0),
-            (8192, 4097, BF16, 3)]
+            (8192, 4097, BF16, 3), (6144, 20003, BF16, 1)]
 
 
 @pytest.mark.parametrize("n,k,dtype,shift", LONG_MIS,
