@@ -37,6 +37,8 @@ def main():
     ap.add_argument("--include-ablation", action="store_true",
                     help="also time the uncoalesced layout (slow)")
     ap.add_argument("--out", default="", help="append JSON lines here")
+    ap.add_argument("--xcd", action="store_true",
+                    help="also time every candidate with its row ranges numbered XCD by XCD")
     ap.add_argument("--graph", action="store_true",
                     help="time each candidate's launches as one HIP graph replay (as bench.py "
                          "does by default) instead of host launches")
@@ -68,7 +70,7 @@ def main():
     grids = [int(x) for x in args.grids.split(",")]
     kgs = [int(x) for x in args.kgroups.split(",")]
 
-    cands = []                         # (variant, grid asked, kgroups asked, resolved config)
+    cands = []                         # (variant, grid asked, kgroups asked, resolved config, flags)
     for v in variants:
         info = mbd.gemv_variant_info(v)[1]
         if info.layout == 1 and not args.include_ablation:
@@ -83,10 +85,11 @@ def main():
                     continue
                 if cfg not in seen:
                     seen.add(cfg)
-                    cands.append((v, gr, kq, cfg))
+                    for fl in ((0, 1) if args.xcd else (0,)):
+                        cands.append((v, gr, kq, cfg, fl))
     g.force_config(-1)
-    if auto not in [c[3] for c in cands]:
-        cands.append((-1, 0, 0, auto))
+    if auto not in [c[3] for c in cands if c[4] == 0]:
+        cands.append((-1, 0, 0, auto, 0))
     print("[tune] %s: %d candidates, %d rounds of %d launches, %d rotating buffers" % (
         name, len(cands), args.rounds, args.steps, nbuf), file=sys.stderr, flush=True)
 
@@ -98,8 +101,8 @@ def main():
         # one graph per candidate, captured once (the forced configuration is
         # baked into the captured launches)
         side = torch.cuda.Stream(dev)
-        for i, (v, gr, kq, cfg) in enumerate(cands):
-            g.force_config(v, gr, kq)
+        for i, (v, gr, kq, cfg, fl) in enumerate(cands):
+            g.force_config(v, gr, kq, fl)
             gph = torch.cuda.CUDAGraph()
             side.wait_stream(stream)
             with torch.cuda.stream(side):
@@ -110,8 +113,8 @@ def main():
             graphs[i] = gph
         torch.cuda.synchronize()
     for rnd in range(args.rounds):
-        for i, (v, gr, kq, cfg) in enumerate(cands):
-            g.force_config(v, gr, kq)
+        for i, (v, gr, kq, cfg, fl) in enumerate(cands):
+            g.force_config(v, gr, kq, fl)
             for j in range(5):
                 mbd.gemv_run(g.h, *P[j % nbuf], n, k, dtype, sp)
             e0 = torch.cuda.Event(enable_timing=True)
@@ -131,7 +134,7 @@ def main():
 
     nbytes = algorithmic_bytes(n, k)
     rows = []
-    for i, (v, gr, kq, cfg) in enumerate(cands):
+    for i, (v, gr, kq, cfg, fl) in enumerate(cands):
         med = statistics.median(times[i])
         info = mbd.gemv_variant_info(cfg[0])[1]
         rows.append({"workload": name, "n": n, "k": k, "variant": cfg[0], "grid": cfg[1],
@@ -140,18 +143,18 @@ def main():
                      "b_policy": info.b_policy, "cross_wg": info.cross_wg, "layout": info.layout,
                      "stages": info.stages, "b_lds": info.b_lds,
                      "us_median": round(med, 3), "us_min": round(min(times[i]), 3),
-                     "gbs": round(nbytes / med / 1e3, 1), "auto": cfg == auto})
+                     "gbs": round(nbytes / med / 1e3, 1), "xcd": fl, "auto": cfg == auto and fl == 0})
     rows.sort(key=lambda r: r["us_median"])
     best = rows[0]["us_median"]
-    print("%4s %4s %6s %3s | %2s %2s %2s %2s %2s %2s %2s %2s %2s | %9s %8s %7s" % (
-        "rank", "var", "grid", "kg", "R", "U", "W", "S", "am", "pl", "x", "P", "L", "us", "GB/s",
+    print("%4s %4s %6s %3s | %2s %2s %2s %2s %2s %2s %2s %2s %2s %2s | %9s %8s %7s" % (
+        "rank", "var", "grid", "kg", "R", "U", "W", "S", "am", "pl", "x", "P", "L", "X", "us", "GB/s",
         "vs best"))
     for r_i, r in enumerate(rows):
         if r_i < args.top or r["auto"]:
-            print("%4d %4d %6d %3d | %2d %2d %2d %2d %2d %2d %2d %2d %2d | %9.3f %8.1f %6.1f%%%s" % (
+            print("%4d %4d %6d %3d | %2d %2d %2d %2d %2d %2d %2d %2d %2d %2d | %9.3f %8.1f %6.1f%%%s" % (
                 r_i + 1, r["variant"], r["grid"], r["kgroups"], r["rows"], r["unroll"], r["waves"],
                 r["splits"], r["a_mode"], r["b_policy"], r["cross_wg"], r["stages"], r["b_lds"],
-                r["us_median"], r["gbs"],
+                r["xcd"], r["us_median"], r["gbs"],
                 100 * (r["us_median"] / best - 1), "  <- automatic plan" if r["auto"] else ""))
     if args.out:
         with open(args.out, "a") as f:
