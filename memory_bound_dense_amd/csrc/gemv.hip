@@ -282,6 +282,11 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // two rows per wave: one row group per workgroup (S waves; measured 0.4-5%
   // faster than two row groups of 8 waves at S = 4 on MI355X, the headline
   // (18432, 7168) fp16 among them)
+  // fp16 rows of 32 full steps, two rows per wave: four slices of two
+  // batches, two row groups per 8-wave workgroup (graph replay, n = 1024 to
+  // 28672, k = 16384: the best compiled plan or within 0.8%, where eight
+  // slices were 0.8-7% behind; not so for bf16, nor for 36 steps)
+  if (dtype == GEMV_F16 && R == 2 && nfull == 32) return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
   const int W = R == 2 ? S : (S == 1 ? 4 : (S <= 8 ? 8 : 16));
   return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0, 1};
 }

@@ -131,8 +131,8 @@ def test_plan_grids_of_the_production_shapes():
     (2048, 32769, (2, 4, 1, 1, 1, 0)),
     (2048, 65537, (2, 4, 1, 1, 1, 0)),
     # fewer rows: the split plan of aligned rows (two rows per wave from 896)
-    (1024, 16385, (2, 4, 8, 8, 1, 0)),
-    (1000, 16385, (2, 4, 8, 8, 1, 0)),
+    (1024, 16897, (2, 4, 8, 8, 1, 0)),
+    (1000, 16897, (2, 4, 8, 8, 1, 0)),
     (800, 16385, (1, 4, 8, 8, 1, 0)),
     # 768..3071 rows of at most 12 full steps: one row per two-wave workgroup
     (2048, 5121, (1, 4, 2, 1, 1, 0)),
@@ -178,6 +178,17 @@ def test_plan_aligned_rules(n, k, want):
 ])
 def test_plan_bf16_short_rows(n, k, want):
     assert shape_of(plan(n, k, BF16)[1]) == want, (n, k)
+
+
+@pytest.mark.parametrize("n,k,dtype,want", [
+    (7168, 16384, F16, (2, 4, 8, 4, 1, 0)),     # fp16, 32 full steps: four slices
+    (1024, 16384, F16, (2, 4, 8, 4, 1, 0)),
+    (28672, 16384, F16, (2, 4, 8, 4, 1, 0)),
+    (7168, 16384, BF16, (2, 4, 8, 8, 1, 0)),    # bf16: eight
+    (7168, 18432, F16, (2, 4, 8, 8, 1, 0)),     # 36 steps: eight
+])
+def test_plan_rows_of_32_steps(n, k, dtype, want):
+    assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
 
 
 @pytest.mark.parametrize("n,k,xwg", [
