@@ -191,6 +191,19 @@ def test_plan_rows_of_32_steps(n, k, dtype, want):
     assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
 
 
+@pytest.mark.parametrize("n,k,want", [
+    (1280, 65536, (1, 4, 2, 1, 1, 0)),      # >= 128 steps on 1280..2048 rows: one row per wave
+    (2048, 65536, (1, 4, 2, 1, 1, 0)),
+    (1500, 131072, (1, 4, 2, 1, 1, 0)),
+    (2049, 65536, (2, 4, 1, 1, 1, 0)),      # more rows: two rows per one-wave workgroup
+    (1536, 49152, (2, 4, 1, 1, 1, 0)),      # 96 steps: the same
+    (1279, 65536, (2, 4, 8, 8, 1, 0)),      # fewer rows: the split
+])
+def test_plan_very_long_rows(n, k, want):
+    for dtype in (F16, BF16):
+        assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
+
+
 @pytest.mark.parametrize("n,k,xwg", [
     (32, 131072, True), (64, 65536, True), (1, 65536, True), (7, 65536, True), (8, 65536, True),
     (65, 65536, False), (127, 65536, False),    # more rows: the in-workgroup split
