@@ -100,9 +100,9 @@ extern "C" gemv_status_t gla_decode_step(gemv_handle_t h, const void* q, const v
   // wait for the staged rows sits on the critical path of a latency-bound
   // launch (measured on MI355X, 128 x 128 heads: 32 heads 3.50 us without
   // against 3.89 us with; 128 heads 4.84 against 4.71)
-  // dk == 0 (o is the empty sum) always takes the staged form: the other
-  // loads the row scalars at row dk - 1
-  const int stage = (dk == 0 || (dk <= kGlaStageRows && grid >= h->num_cus)) ? 1 : 0;
+  // (dk == 0, o the empty sum, runs in either form: neither reads a row
+  // scalar, a state row or v then, so those inputs may be null)
+  const int stage = (dk <= kGlaStageRows && grid >= h->num_cus) ? 1 : 0;
   const size_t lds = stage ? (size_t)(3 * dk) * sizeof(float) : 0;
   // one workgroup per (head, column block); its work-items along x (a 32-bit
   // field of the dispatch) are kept at most 2^31

@@ -79,21 +79,26 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
     }
   };
   // Without staging, the row scalars (gk, k, q) of a trip travel with its
-  // state rows: loaded a trip ahead at a row index clamped to dk - 1 (in
-  // bounds as dk >= 1 here: the host sends dk == 0 to the staged form),
-  // as raw 16-bit values, so no branch holds a load back and nothing waits
-  // on one memory round trip before issuing the next.  (With both behind
-  // conditions the compiler waited for the state before the loop and for
-  // each row's scalars in turn: several round trips where one suffices.)
+  // state rows: loaded a trip ahead, as raw 16-bit values, through buffer
+  // descriptors whose range is the head's dk rows -- a row past dk (every
+  // row when dk == 0) reads zero with no memory access -- so no branch holds
+  // a load back and nothing waits on one memory round trip before issuing
+  // the next.  (With both behind conditions the compiler waited for the
+  // state before the loop and for each row's scalars in turn: several round
+  // trips where one suffices.)  A zero row gives e = 1, k = q = 0 and a
+  // zero state: its update is computed and dropped by the selects below.
+  const __amdgpu_buffer_rsrc_t gk_r = make_rsrc(gk + rowbase, (uint32_t)dk * 2u);
+  const __amdgpu_buffer_rsrc_t k_r = make_rsrc(k + rowbase, (uint32_t)dk * 2u);
+  const __amdgpu_buffer_rsrc_t q_r = make_rsrc(q + rowbase, (uint32_t)dk * 2u);
   auto load_scalars = [&](int i0, uint16_t (&sg)[kRows], uint16_t (&sk)[kRows],
                           uint16_t (&sq)[kRows]) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int i = i0 + r * RG;
-      const int64_t ic = rowbase + (i < dk ? i : dk - 1);
-      sg[r] = gk[ic];
-      sk[r] = k[ic];
-      sq[r] = q[ic];
+      const uint32_t off = i < dk ? (uint32_t)i * 2u : kOffsetOutOfRange;
+      sg[r] = __builtin_amdgcn_raw_buffer_load_b16(gk_r, off, 0u, 0);
+      sk[r] = __builtin_amdgcn_raw_buffer_load_b16(k_r, off, 0u, 0);
+      sq[r] = __builtin_amdgcn_raw_buffer_load_b16(q_r, off, 0u, 0);
     }
   };
   u32x4 cur[kRows];
@@ -101,11 +106,13 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
   float vj[4] = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     load_trip(rg, cur);
-    // the clamped index needs a row: the host launches this form only with
-    // dk >= 1 (dk == 0 goes to the staged form, which loads no row scalars)
     if constexpr (!STAGE) load_scalars(rg, cg, ck, cq);
+    // v is read only when there is a state row to update: with dk == 0 the
+    // inputs other than o may be empty (null) buffers
+    if (dk > 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vj[c] = widen<DT>(v[head * dv + j0 + c]);
+      for (int c = 0; c < 4; ++c) vj[c] = widen<DT>(v[head * dv + j0 + c]);
+    }
   }
 
   extern __shared__ float gla_rows[];        // STAGE: e[0..dk), k[dk..2dk), q[2dk..3dk)

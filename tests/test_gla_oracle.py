@@ -96,6 +96,32 @@ def test_integer_inputs_exact(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_absolute_sum_of_the_output(dtype):
+    """oabs (it scales the GPU tolerance of o) is |scale| * sum_i |q_i S_new[i][j]|
+    with S_new = S + outer(k, v) at gk = 0: integer inputs of both signs and a
+    negative power-of-two scale make it an exact integer computation.  A
+    missing |scale|, a signed sum, or the old state in place of S_new each
+    give a different value here."""
+    rng = np.random.default_rng(17)
+    bh, dk, dv = 3, 41, 12
+    qi = rng.integers(-3, 4, size=(bh, dk))
+    ki = rng.integers(-3, 4, size=(bh, dk))
+    vi = rng.integers(-3, 4, size=(bh, dv))
+    Si = rng.integers(-20, 21, size=(bh, dk, dv))
+    q, k, v = (values_to_bits(x.astype(np.float32), dtype) for x in (qi, ki, vi))
+    gk = np.zeros((bh, dk), np.uint16)
+    scale = -0.25
+    _, _, _, o64, oabs = oracle.gla_decode(dtype, q, k, v, gk, Si.astype(np.float32), scale)
+    Snew = Si + ki[:, :, None] * vi[:, None, :]
+    want = np.abs(qi[:, :, None] * Snew).sum(axis=1)          # exact integers
+    assert np.array_equal(oabs, 0.25 * want.astype(np.float64))
+    assert np.array_equal(o64, scale * np.einsum("hi,hij->hj", qi, Snew).astype(np.float64))
+    # the pin tells these readings apart on this input
+    assert not np.array_equal(want, np.abs(np.einsum("hi,hij->hj", qi, Snew)))
+    assert not np.array_equal(want, np.abs(qi[:, :, None] * Si).sum(axis=1))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_linear_in_q(dtype):
     q, k, v, gk, S = gla_inputs(2, 64, 32, dtype, seed=5)
     _, _, _, o1, a1 = oracle.gla_decode(dtype, q, k, v, gk, S, 1.0)
