@@ -41,19 +41,21 @@
  * with B or a, current device == handle device; then the launch, whose
  * failure is GEMV_ERR_HIP.
  *
- * Workspace.  gemv_create allocates a small device workspace (4 MiB of
- * partial sums and 256 KiB of counters) for the k-split across workgroups
- * that small n takes; gemv_run never allocates.  The counters return to zero
- * at the end of every such kernel.
+ * Scratch.  The handle owns no device memory.  gemv_run and gemv_run_ex use
+ * none: for few rows they split k inside a workgroup.  Splitting k across
+ * workgroups as well (faster for a few long rows, e.g. 64 rows of 65536)
+ * needs device scratch for the partial sums and arrival counters, which the
+ * caller brings to gemv_run_ws (GEMV_WORKSPACE_BYTES).
  *
- * Threading.  The handle's settings are read-only after gemv_create
- * (gemv_force_config aside), but its workspace is shared: calls on one handle
- * must not run concurrently on the GPU (issue them on one stream, or order
- * them with events).  For concurrent streams use one handle per stream.
+ * Threading.  The handle is read-only after gemv_create (gemv_force_config,
+ * a benchmarking aid, aside), so gemv_run and gemv_run_ex calls on one handle
+ * may run concurrently on different streams.  gemv_run_ws calls may too, as
+ * long as calls that can overlap on the GPU use different workspaces.
  */
 #ifndef MBD_GEMV_H
 #define MBD_GEMV_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -86,9 +88,15 @@ typedef enum {
 #define GEMV_MAX_N 1073741824LL
 #define GEMV_MAX_K 134217728LL
 
+/* Bytes of caller scratch that gemv_run_ws needs for its cross-workgroup
+ * k-split: 256 KiB of arrival counters (64 banks of 1024, one bank per
+ * k-group count) and 1 MiB of fp32 partial sums (k-groups x n <= 2^18). */
+#define GEMV_WORKSPACE_BYTES 1310720LL
+
 /* Create a handle bound to the current HIP device.  Queries the device (it
- * must be a gfx950), sets kernel attributes, allocates the workspace and
- * fixes the variant table.  *out receives the handle, or NULL on error. */
+ * must be a gfx950), sets kernel attributes and fixes the variant table; it
+ * allocates host memory for the handle only.  *out receives the handle, or
+ * NULL on error. */
 gemv_status_t gemv_create(gemv_handle_t* out);
 
 /* c = B @ a on `stream` (0 = the null stream).  B: n*k elements, row-major;
@@ -114,6 +122,31 @@ gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void* a, void* c
                           int64_t n, int64_t k, gemv_dtype_t dtype, const gemv_epilogue_t* ep,
                           hipStream_t stream);
 
+/* gemv_run_ex with caller scratch, which lets the plan split k across
+ * workgroups where that is faster (few rows of many columns: the Q
+ * workgroups that share a row range each write fp32 partials; the last to
+ * arrive, told by an arrival counter, sums them in a fixed order, so results
+ * do not depend on timing).  Pages: TileLang Case Studies, Case B.3 (few rows
+ * underfill the GPU) and Case C (split-k plus a reduction).
+ *   workspace:       NULL (then exactly gemv_run_ex), or device memory on the
+ *                    handle's device, 16-byte aligned, at least
+ *                    workspace_bytes >= GEMV_WORKSPACE_BYTES (else
+ *                    GEMV_ERR_INVALID_ARG / GEMV_ERR_MISALIGNED), overlapping
+ *                    none of B, a, c and bias (GEMV_ERR_ALIASING).  Owned by
+ *                    the caller; the library keeps no reference after the
+ *                    call's kernel completes.
+ *   contents:        zero-filled once before its first use (e.g. hipMemset);
+ *                    from then on every completed call leaves its counters
+ *                    at zero, so it needs no clearing between calls.
+ *   concurrency:     calls that may overlap on the GPU need different
+ *                    workspaces; overlapping calls on one workspace race (c
+ *                    undefined), though the counters still return to zero
+ *                    once those calls have completed.
+ * Validation as gemv_run_ex, then (n > 0) the workspace checks above. */
+gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void* a, void* c,
+                          int64_t n, int64_t k, gemv_dtype_t dtype, const gemv_epilogue_t* ep,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Every check gemv_run makes that needs neither a handle nor a GPU, in the
  * same order and with the same result: GEMV_OK means gemv_run would go on to
  * the device check and the launch (or return GEMV_OK at once when n == 0).
@@ -125,9 +158,8 @@ gemv_status_t gemv_check_args(const void* B, const void* a, const void* c, int64
 gemv_status_t gemv_check_args_ex(const void* B, const void* a, const void* c, int64_t n, int64_t k,
                                  gemv_dtype_t dtype, const gemv_epilogue_t* ep);
 
-/* Release the handle and its workspace.  NULL is a no-op.  Waits for the
- * handle's device to finish outstanding work first (a kernel in flight may
- * still use the workspace). */
+/* Release the handle.  NULL is a no-op.  Kernels already enqueued do not
+ * read the handle, so they may still be running. */
 gemv_status_t gemv_destroy(gemv_handle_t h);
 
 /* Static, human-readable name of a status code. */
@@ -155,7 +187,8 @@ typedef struct {
   int32_t a_mode;
   int32_t b_policy;   /* cache-policy bits of the B loads (0 = default) */
   int32_t cross_wg;   /* 1: kgroups workgroups share each row range along k,
-                         combining through the handle's workspace */
+                         combining through the caller's scratch: runs only
+                         from gemv_run_ws with a workspace */
   int32_t layout;     /* 0: lanes along k (coalesced); 1: one row per lane,
                          one element per step -- the uncoalesced layout of
                          TileLang Case Studies, Case B, kept for measurement
@@ -196,19 +229,23 @@ gemv_status_t gemv_variant_info(int32_t v, gemv_variant_info_t* info);
 
 /* Force a configuration on every later gemv_run of this handle (NULL or
  * variant -1 restores automatic selection).  Not thread-safe with concurrent
- * gemv_run calls on the same handle. */
+ * gemv_run calls on the same handle.  A cross_wg variant then runs only
+ * from gemv_run_ws with a workspace (elsewhere GEMV_ERR_UNSUPPORTED). */
 gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t* cfg);
 
 /* The configuration gemv_run would use for (n, k, dtype) on this handle,
- * for a 16-byte-aligned B (gemv_run also looks at B's alignment).  grid is
- * reported as the number of workgroups actually launched. */
+ * for a 16-byte-aligned B (gemv_run also looks at B's alignment), without
+ * (with_workspace == 0: gemv_run, gemv_run_ex) or with (gemv_run_ws with a
+ * workspace) caller scratch.  grid is reported as the number of workgroups
+ * actually launched. */
 gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k, gemv_dtype_t dtype,
-                                gemv_config_t* out);
+                                int32_t with_workspace, gemv_config_t* out);
 
 /* The configuration the automatic plan picks for (n, k, dtype), worked out on
  * the host alone -- no handle, no device, no HIP call -- for a device whose
  * per-workgroup LDS limit is `max_lds` bytes (163840 on MI355X) and a B that
- * is (b_aligned != 0) or is not 16-byte aligned.  It is the rule gemv_run
+ * is (b_aligned != 0) or is not 16-byte aligned, and without (with_workspace
+ * == 0) or with caller scratch (see gemv_query_config).  It is the rule gemv_run
  * applies (TileLang Case Studies, Case B.4: the choice is fixed host logic,
  * not per-call tuning), so tools and CPU tests can inspect it; on a real
  * handle gemv_query_config gives the same answer (it also checks the LDS the
@@ -217,7 +254,7 @@ gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k, gemv_dtyp
  * limits, max_lds <= 0), GEMV_ERR_UNSUPPORTED_DTYPE, GEMV_ERR_UNSUPPORTED (no
  * compiled variant fits). */
 gemv_status_t gemv_plan_config(int64_t n, int64_t k, gemv_dtype_t dtype, int32_t b_aligned,
-                               int64_t max_lds, gemv_config_t* out);
+                               int64_t max_lds, int32_t with_workspace, gemv_config_t* out);
 
 #ifdef __cplusplus
 }

@@ -33,9 +33,11 @@ GEMV_FLAG_XCD_CONTIGUOUS = 1
 
 GEMV_MAX_N = 1073741824
 GEMV_MAX_K = 134217728
+GEMV_WORKSPACE_BYTES = 1310720
 
 # every symbol include/gemv.h and include/gla_decode.h declare
-EXPORTS = ("gemv_create", "gemv_run", "gemv_run_ex", "gemv_destroy", "gemv_status_string",
+EXPORTS = ("gemv_create", "gemv_run", "gemv_run_ex", "gemv_run_ws", "gemv_destroy",
+           "gemv_status_string",
            "gemv_check_args", "gemv_check_args_ex", "gemv_num_variants", "gemv_variant_info",
            "gemv_force_config", "gemv_query_config", "gemv_plan_config", "gla_decode_step",
            "gla_check_args")
@@ -85,6 +87,9 @@ def load():
     lib.gemv_run_ex.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int,
                                 ctypes.POINTER(gemv_epilogue_t), vp]
     lib.gemv_run_ex.restype = st
+    lib.gemv_run_ws.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int,
+                                ctypes.POINTER(gemv_epilogue_t), vp, ctypes.c_size_t, vp]
+    lib.gemv_run_ws.restype = st
     lib.gemv_check_args_ex.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int,
                                        ctypes.POINTER(gemv_epilogue_t)]
     lib.gemv_check_args_ex.restype = st
@@ -100,9 +105,11 @@ def load():
     lib.gemv_variant_info.restype = st
     lib.gemv_force_config.argtypes = [vp, ctypes.POINTER(gemv_config_t)]
     lib.gemv_force_config.restype = st
-    lib.gemv_query_config.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.POINTER(gemv_config_t)]
+    lib.gemv_query_config.argtypes = [vp, i64, i64, ctypes.c_int, i32,
+                                      ctypes.POINTER(gemv_config_t)]
     lib.gemv_query_config.restype = st
-    lib.gemv_plan_config.argtypes = [i64, i64, ctypes.c_int, i32, i64, ctypes.POINTER(gemv_config_t)]
+    lib.gemv_plan_config.argtypes = [i64, i64, ctypes.c_int, i32, i64, i32,
+                                     ctypes.POINTER(gemv_config_t)]
     lib.gemv_plan_config.restype = st
     lib.gla_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
                                     ctypes.c_int, vp]
@@ -131,6 +138,16 @@ def gemv_run_ex(h, B, a, c, n, k, dtype, alpha=1.0, bias=None, stream=None):
     """gemv_run with the epilogue c = alpha * (B @ a) + bias (bias: address or None)."""
     ep = gemv_epilogue_t(alpha, bias)
     return load().gemv_run_ex(h, B, a, c, n, k, dtype, ctypes.byref(ep), stream)
+
+
+def gemv_run_ws(h, B, a, c, n, k, dtype, workspace, workspace_bytes=GEMV_WORKSPACE_BYTES,
+                alpha=None, bias=None, stream=None):
+    """gemv_run_ex with caller scratch (workspace: a device address or None);
+    no epilogue when alpha and bias are both None."""
+    ep = None
+    if alpha is not None or bias is not None:
+        ep = ctypes.byref(gemv_epilogue_t(1.0 if alpha is None else alpha, bias))
+    return load().gemv_run_ws(h, B, a, c, n, k, dtype, ep, workspace, workspace_bytes, stream)
 
 
 def gemv_check_args_ex(B, a, c, n, k, dtype, alpha=None, bias=None):
@@ -169,16 +186,17 @@ def gemv_force_config(h, variant=-1, grid=0, kgroups=0, flags=0):
     return load().gemv_force_config(h, ctypes.byref(cfg))
 
 
-def gemv_query_config(h, n, k, dtype):
+def gemv_query_config(h, n, k, dtype, with_workspace=0):
     cfg = gemv_config_t()
-    s = load().gemv_query_config(h, n, k, dtype, ctypes.byref(cfg))
+    s = load().gemv_query_config(h, n, k, dtype, int(with_workspace), ctypes.byref(cfg))
     return s, cfg
 
 
-def gemv_plan_config(n, k, dtype, b_aligned=1, max_lds=160 * 1024):
+def gemv_plan_config(n, k, dtype, b_aligned=1, max_lds=160 * 1024, with_workspace=0):
     """The automatic plan for a shape, on the host alone (no device)."""
     cfg = gemv_config_t()
-    s = load().gemv_plan_config(n, k, dtype, int(b_aligned), max_lds, ctypes.byref(cfg))
+    s = load().gemv_plan_config(n, k, dtype, int(b_aligned), max_lds, int(with_workspace),
+                                ctypes.byref(cfg))
     return s, cfg
 
 
@@ -202,20 +220,42 @@ def _dtype_code(t):
     raise GemvError(GEMV_ERR_UNSUPPORTED_DTYPE, str(t.dtype))
 
 
+def _check_devices(tensors, device):
+    """Every tensor on `device`, a GPU: the library takes raw addresses and
+    cannot tell a host address from a device one, so a CPU tensor (or one on
+    another GPU) is refused here, before anything is launched."""
+    if device.type != "cuda":
+        raise GemvError(GEMV_ERR_INVALID_ARG, "tensors must be on a GPU, got %s" % device)
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise GemvError(GEMV_ERR_INVALID_ARG, "tensors on %s and %s" % (device, t.device))
+
+
 class Gemv:
     """One handle on the current device.  ``gemv(B, a, c)`` enqueues c = B @ a
-    on the current torch stream (or ``stream``); tensors must be dense."""
+    on the current torch stream (or ``stream``); tensors must be dense and on
+    the handle's GPU.  With ``workspace=True`` the object also owns caller
+    scratch (GEMV_WORKSPACE_BYTES, zero-filled once) and calls gemv_run_ws,
+    whose plan may split k across workgroups; calls through one such object
+    must then not overlap on the GPU (one stream, or ordered by events)."""
 
-    def __init__(self):
+    def __init__(self, workspace=False):
+        self.h = None
+        self.ws = None
         s, h = gemv_create()
         if s != GEMV_OK:
             raise GemvError(s, "gemv_create")
         self.h = h
+        if workspace:
+            import torch
+            self.ws = torch.zeros(GEMV_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+            torch.cuda.synchronize()     # zero-filled before any stream uses it
 
     def close(self):
         if self.h is not None:
             gemv_destroy(self.h)
             self.h = None
+        self.ws = None
 
     def __del__(self):
         try:
@@ -228,15 +268,21 @@ class Gemv:
         if s != GEMV_OK:
             raise GemvError(s, "gemv_force_config")
 
-    def query_config(self, n, k, dtype):
-        s, cfg = gemv_query_config(self.h, n, k, dtype)
+    def query_config(self, n, k, dtype, with_workspace=None):
+        """(variant, grid, kgroups) of the plan a call would launch; by default
+        for the entry point this object calls (with or without scratch)."""
+        if with_workspace is None:
+            with_workspace = self.ws is not None
+        s, cfg = gemv_query_config(self.h, n, k, dtype, with_workspace)
         if s != GEMV_OK:
             raise GemvError(s, "gemv_query_config")
         return cfg.variant, cfg.grid, cfg.kgroups
 
-    def __call__(self, B, a, c, stream=None, alpha=None, bias=None):
+    def __call__(self, B, a, c, stream=None, alpha=None, bias=None, use_workspace=True):
         """c = B @ a, or c = alpha * (B @ a) + bias when alpha or bias is given
-        (bias: an (n,) tensor of the same dtype, possibly c itself)."""
+        (bias: an (n,) tensor of the same dtype, possibly c itself).
+        use_workspace=False calls gemv_run / gemv_run_ex even when the object
+        owns scratch."""
         import torch
         if B.dim() != 2 or a.dim() != 1 or c.dim() != 1:
             raise GemvError(GEMV_ERR_INVALID_ARG, "B must be 2-D, a and c 1-D")
@@ -246,20 +292,26 @@ class Gemv:
                 tuple(B.shape), tuple(a.shape), tuple(c.shape)))
         if not (B.is_contiguous() and a.is_contiguous() and c.is_contiguous()):
             raise GemvError(GEMV_ERR_INVALID_ARG, "tensors must be contiguous")
+        _check_devices((a, c, bias), B.device)
         dt = _dtype_code(B)
         if a.dtype != B.dtype or c.dtype != B.dtype:
             raise GemvError(GEMV_ERR_UNSUPPORTED_DTYPE, "B, a and c must share one dtype")
+        bp = None
+        if bias is not None:
+            if bias.dim() != 1 or bias.shape[0] != n or bias.dtype != B.dtype or \
+                    not bias.is_contiguous():
+                raise GemvError(GEMV_ERR_INVALID_ARG, "bias must be a dense (n,) tensor of B's dtype")
+            bp = bias.data_ptr()
         if stream is None:
             stream = torch.cuda.current_stream(B.device).cuda_stream
-        if alpha is None and bias is None:
+        if self.ws is not None and use_workspace:
+            if self.ws.device != B.device:
+                raise GemvError(GEMV_ERR_INVALID_ARG, "the workspace is on %s" % self.ws.device)
+            s = gemv_run_ws(self.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, dt,
+                            self.ws.data_ptr(), self.ws.numel(), alpha, bp, stream)
+        elif alpha is None and bias is None:
             s = gemv_run(self.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, dt, stream)
         else:
-            bp = None
-            if bias is not None:
-                if bias.dim() != 1 or bias.shape[0] != n or bias.dtype != B.dtype or \
-                        not bias.is_contiguous():
-                    raise GemvError(GEMV_ERR_INVALID_ARG, "bias must be a dense (n,) tensor of B's dtype")
-                bp = bias.data_ptr()
             s = gemv_run_ex(self.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, dt,
                             1.0 if alpha is None else float(alpha), bp, stream)
         if s != GEMV_OK:
@@ -284,6 +336,7 @@ class GlaDecode:
                          (S_in, (bh, dk, dv)), (S_out, (bh, dk, dv))):
             if tuple(t.shape) != shape or not t.is_contiguous():
                 raise GemvError(GEMV_ERR_INVALID_ARG, "shape/contiguity of a GLA argument")
+        _check_devices((k, v, gk, S_in, S_out, o), q.device)
         dt = _dtype_code(q)
         if any(t.dtype != q.dtype for t in (k, v, gk, o)) or S_in.dtype != torch.float32 or \
                 S_out.dtype != torch.float32:

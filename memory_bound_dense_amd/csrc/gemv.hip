@@ -125,10 +125,16 @@ size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
 // Rows a workgroup covers per trip (layout 1: rows == 64, one per lane).
 int64_t rows_per_block(const gemv_variant_info_t& v) { return (int64_t)(v.waves / v.splits) * v.rows; }
 
-// Device workspace of a handle: fp32 partial sums (kgroups x n) and one
-// arrival counter per row range, for the cross-workgroup variants.
-constexpr size_t kWsFloats = (size_t)1 << 20;   // 4 MiB
-constexpr int kWsCounters = 1 << 16;            // 256 KiB
+// Caller scratch of the cross-workgroup split (gemv_run_ws): first the
+// arrival counters, one bank of kXwgRanges per k-group count Q = 1..kXwgMaxQ
+// (so that a counter only ever sees one Q), then the fp32 partial sums, Q
+// per row (k-group q of row i at q * n + i).
+constexpr int kXwgMaxQ = 64;
+constexpr int kXwgRanges = 1024;
+constexpr size_t kWsCounterBytes = (size_t)kXwgMaxQ * kXwgRanges * sizeof(unsigned);   // 256 KiB
+constexpr size_t kWsFloats = (size_t)1 << 18;                                             // 1 MiB
+static_assert(kWsCounterBytes + kWsFloats * sizeof(float) == (size_t)GEMV_WORKSPACE_BYTES,
+              "the header's workspace size is the layout's");
 
 // Shape of a launch plan: a variant shape plus a workgroup count (0 = one
 // row range per wave, i.e. no persistence).
@@ -221,7 +227,8 @@ int find_variant(const Plan& p) {
 //     candidate variants each, on MI355X: this rule is within 1.3% of the
 //     best compiled plan on average, 10% at worst; the previous one, fitted
 //     to host-launched timing, 2.7% and 24%.)
-Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned) {
+Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned,
+               bool with_ws) {
   const int64_t nfull0 = k / mbd::kStep;
   const bool misaligned = k > 0 && (k % 8 != 0 || !b_aligned);
   constexpr int64_t kShortMisaligned = 8192;   // the k range of the measured tiers of 1
@@ -249,10 +256,12 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     if (l <= (size_t)70 * 1024 && l <= max_lds) return p16;
   }
   // 2. 8 waves per row per workgroup, Q groups sized so that every wave has
-  // one batch of 4 steps (2 steps below 8 rows, to have more waves).
-  if (n <= 64 && nfull0 >= 128) {
+  // one batch of 4 steps (2 steps below 8 rows, to have more waves) -- only
+  // with caller scratch for the partials and counters (gemv_run_ws); without
+  // it, the in-workgroup split below.
+  if (with_ws && n <= 64 && nfull0 >= 128) {
     int64_t Q = nfull0 / (8 * (n < 8 ? 2 : 4));
-    if (Q > 64) Q = 64;
+    if (Q > kXwgMaxQ) Q = kXwgMaxQ;
     if (Q * n <= (int64_t)kWsFloats) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
   if (n < 128 && nfull0 >= 32) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
@@ -295,11 +304,12 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0, 1};
 }
 
-Plan auto_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned) {
+Plan auto_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned,
+               bool with_ws) {
   if (b_aligned)
     for (const TunedShape& t : kTuned)
       if (t.n == n && t.k == k) return t.plan;
-  return rule_plan(n, k, dtype, max_lds, b_aligned);
+  return rule_plan(n, k, dtype, max_lds, b_aligned, with_ws);
 }
 
 }  // namespace
@@ -391,9 +401,11 @@ static gemv_status_t shape_launch(int v, int64_t g, int64_t q, int flags, int64_
     return GEMV_ERR_UNSUPPORTED;   // a wave's 64 rows must fit one buffer descriptor
   if (info.cross_wg) {
     if (q <= 0) q = 4;
-    if (q > 1024) return GEMV_ERR_UNSUPPORTED;
-    // the workspace must hold q partials per row and one counter per row range
-    if (q * n > (int64_t)kWsFloats || g > kWsCounters) return GEMV_ERR_UNSUPPORTED;
+    if (q > kXwgMaxQ) return GEMV_ERR_UNSUPPORTED;
+    // the scratch holds q partials per row and one counter per row range
+    // (a smaller grid is valid: each workgroup walks a longer row range)
+    if (g > kXwgRanges) g = kXwgRanges;
+    if (q * n > (int64_t)kWsFloats) return GEMV_ERR_UNSUPPORTED;
   } else {
     if (q > 1) return GEMV_ERR_INVALID_ARG;
     q = 1;
@@ -407,7 +419,7 @@ static gemv_status_t shape_launch(int v, int64_t g, int64_t q, int flags, int64_
 }
 
 static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_dtype_t dtype,
-                             bool b_aligned, Launch* L) {
+                             bool b_aligned, bool with_ws, Launch* L) {
   int v;
   int64_t g, q;
   int flags = 0;
@@ -416,8 +428,10 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_
     g = h->forced.grid;
     q = h->forced.kgroups;
     flags = h->forced.flags;
+    // the cross-workgroup split needs the caller's scratch
+    if (kVariants[v].info.cross_wg && !with_ws) return GEMV_ERR_UNSUPPORTED;
   } else {
-    const Plan p = auto_plan(n, k, dtype, h->max_lds, b_aligned);
+    const Plan p = auto_plan(n, k, dtype, h->max_lds, b_aligned, with_ws);
     v = find_variant(p);
     if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
     g = p.grid;
@@ -431,11 +445,12 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_
 }
 
 extern "C" gemv_status_t gemv_plan_config(int64_t n, int64_t k, gemv_dtype_t dtype, int32_t b_aligned,
-                                          int64_t max_lds, gemv_config_t* out) {
+                                          int64_t max_lds, int32_t with_workspace,
+                                          gemv_config_t* out) {
   if (!out) return GEMV_ERR_INVALID_ARG;
   if (dtype != GEMV_F16 && dtype != GEMV_BF16) return GEMV_ERR_UNSUPPORTED_DTYPE;
   if (n <= 0 || k < 0 || n > GEMV_MAX_N || k > GEMV_MAX_K || max_lds <= 0) return GEMV_ERR_INVALID_ARG;
-  const Plan p = auto_plan(n, k, dtype, (size_t)max_lds, b_aligned != 0);
+  const Plan p = auto_plan(n, k, dtype, (size_t)max_lds, b_aligned != 0, with_workspace != 0);
   const int v = find_variant(p);
   if (v < 0) return GEMV_ERR_UNSUPPORTED;
   Launch L;
@@ -481,18 +496,6 @@ extern "C" gemv_status_t gemv_create(gemv_handle_t* out) {
       }
     }
   }
-  void* mem = nullptr;
-  const size_t bytes = kWsFloats * sizeof(float) + (size_t)kWsCounters * sizeof(unsigned);
-  if (hipMalloc(&mem, bytes) != hipSuccess) {
-    free(h);
-    return report(nullptr, GEMV_ERR_HIP, "hipMalloc(workspace)");
-  }
-  // the counters start at zero; every kernel that uses one leaves it at zero
-  if (hipMemset(mem, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-    (void)hipFree(mem);
-    free(h);
-    return report(nullptr, GEMV_ERR_HIP, "hipMemset(workspace)");
-  }
   h->magic = kMagic;
   h->device = dev;
   h->num_cus = prop.multiProcessorCount;
@@ -503,8 +506,6 @@ extern "C" gemv_status_t gemv_create(gemv_handle_t* out) {
   h->forced.grid = 0;
   h->forced.kgroups = 0;
   h->forced.flags = 0;
-  h->ws = (float*)mem;
-  h->cnt = (unsigned*)((char*)mem + kWsFloats * sizeof(float));
   *out = h;
   return GEMV_OK;
 }
@@ -512,17 +513,10 @@ extern "C" gemv_status_t gemv_create(gemv_handle_t* out) {
 extern "C" gemv_status_t gemv_destroy(gemv_handle_t h) {
   if (!h) return GEMV_OK;
   if (h->magic != kMagic) return GEMV_ERR_NULL_HANDLE;
-  gemv_status_t st = GEMV_OK;
-  int cur = -1;
-  if (hipGetDevice(&cur) != hipSuccess) st = GEMV_ERR_HIP;
-  // a kernel still in flight may use the workspace: let the device drain first
-  if (st == GEMV_OK && cur != h->device && hipSetDevice(h->device) != hipSuccess) st = GEMV_ERR_HIP;
-  if (hipDeviceSynchronize() != hipSuccess) st = GEMV_ERR_HIP;
-  if (hipFree(h->ws) != hipSuccess) st = GEMV_ERR_HIP;
-  if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
+  // the handle holds no device memory: kernels still in flight never read it
   h->magic = kDead;
   free(h);
-  return st;
+  return GEMV_OK;
 }
 
 extern "C" gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t* cfg) {
@@ -543,13 +537,14 @@ extern "C" gemv_status_t gemv_force_config(gemv_handle_t h, const gemv_config_t*
 }
 
 extern "C" gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k,
-                                           gemv_dtype_t dtype, gemv_config_t* out) {
+                                           gemv_dtype_t dtype, int32_t with_workspace,
+                                           gemv_config_t* out) {
   if (!h || h->magic != kMagic) return GEMV_ERR_NULL_HANDLE;
   if (!out) return GEMV_ERR_INVALID_ARG;
   if (dtype != GEMV_F16 && dtype != GEMV_BF16) return GEMV_ERR_UNSUPPORTED_DTYPE;
   if (n <= 0 || k < 0 || n > GEMV_MAX_N || k > GEMV_MAX_K) return GEMV_ERR_INVALID_ARG;
   Launch L;
-  gemv_status_t s = resolve(h, n, k, dtype, true, &L);
+  gemv_status_t s = resolve(h, n, k, dtype, true, with_workspace != 0, &L);
   if (s != GEMV_OK) return s;
   out->variant = L.variant;
   out->grid = L.grid;
@@ -560,22 +555,51 @@ extern "C" gemv_status_t gemv_query_config(gemv_handle_t h, int64_t n, int64_t k
 
 extern "C" gemv_status_t gemv_run(gemv_handle_t h, const void* B, const void* a, void* c,
                                   int64_t n, int64_t k, gemv_dtype_t dtype, hipStream_t stream) {
-  return gemv_run_ex(h, B, a, c, n, k, dtype, nullptr, stream);
+  return gemv_run_ws(h, B, a, c, n, k, dtype, nullptr, nullptr, 0, stream);
 }
 
 extern "C" gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void* a, void* c,
                                      int64_t n, int64_t k, gemv_dtype_t dtype,
                                      const gemv_epilogue_t* ep, hipStream_t stream) {
+  return gemv_run_ws(h, B, a, c, n, k, dtype, ep, nullptr, 0, stream);
+}
+
+// The workspace checks of gemv_run_ws, after gemv_check_args_ex has passed
+// and n > 0: size, alignment, no overlap with B, a, c or the bias.
+static gemv_status_t check_workspace(const void* B, const void* a, const void* c, int64_t n,
+                                     int64_t k, const gemv_epilogue_t* ep, const void* ws,
+                                     size_t ws_bytes) {
+  if (!ws) return GEMV_OK;
+  if (ws_bytes < (size_t)GEMV_WORKSPACE_BYTES) return GEMV_ERR_INVALID_ARG;
+  if ((uintptr_t)ws & 15u) return GEMV_ERR_MISALIGNED;
+  const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)GEMV_WORKSPACE_BYTES;
+  auto hits = [&](const void* p, uintptr_t bytes) {
+    const uintptr_t p0 = (uintptr_t)p;
+    return p && bytes && p0 < w1 && w0 < p0 + bytes;
+  };
+  if (hits(c, (uintptr_t)n * 2u) || (k > 0 && (hits(B, (uintptr_t)n * (uintptr_t)k * 2u) ||
+                                                hits(a, (uintptr_t)k * 2u))) ||
+      (ep && hits(ep->bias, (uintptr_t)n * 2u)))
+    return GEMV_ERR_ALIASING;
+  return GEMV_OK;
+}
+
+extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void* a, void* c,
+                                     int64_t n, int64_t k, gemv_dtype_t dtype,
+                                     const gemv_epilogue_t* ep, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
   if (!h || h->magic != kMagic) return report(nullptr, GEMV_ERR_NULL_HANDLE, "gemv_run");
   gemv_status_t s = gemv_check_args_ex(B, a, c, n, k, dtype, ep);
   if (s != GEMV_OK) return report(h, s, "gemv_run arguments");
   if (n == 0) return GEMV_OK;
+  s = check_workspace(B, a, c, n, k, ep, workspace, workspace_bytes);
+  if (s != GEMV_OK) return report(h, s, "gemv_run_ws workspace");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return report(h, GEMV_ERR_HIP, "hipGetDevice");
   if (dev != h->device) return report(h, GEMV_ERR_WRONG_DEVICE, "gemv_run");
   Launch L;
-  s = resolve(h, n, k, dtype, ((uintptr_t)B & 15u) == 0, &L);
-  if (s != GEMV_OK) return report(h, s, "no variant fits (LDS or workspace)");
+  s = resolve(h, n, k, dtype, ((uintptr_t)B & 15u) == 0, workspace != nullptr, &L);
+  if (s != GEMV_OK) return report(h, s, "no variant fits (LDS, or scratch for the k-split)");
   const Variant& var = kVariants[L.variant];
   const gemv_variant_info_t& vi = var.info;
   mbd::GemvArgs p;
@@ -583,8 +607,9 @@ extern "C" gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void*
   p.a = (const uint16_t*)a;
   p.c = (uint16_t*)c;
   p.bias = ep ? (const uint16_t*)ep->bias : nullptr;
-  p.ws = h->ws;
-  p.cnt = h->cnt;
+  // the scratch: the counter bank of this k-group count, then the partials
+  p.cnt = workspace ? (unsigned*)workspace + (size_t)(L.kgroups - 1) * kXwgRanges : nullptr;
+  p.ws = workspace ? (float*)((char*)workspace + kWsCounterBytes) : nullptr;
   p.n = (int)n;
   p.k = (int)k;
   p.flags = L.flags | (ep ? mbd::kFlagEpilogue : 0);

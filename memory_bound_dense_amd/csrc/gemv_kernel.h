@@ -22,9 +22,9 @@
 //   * with S > 1 the k-slices of a row group are summed through LDS in slice
 //     order (fixed order, so results do not depend on timing);
 //   * with XWG, Q = gridDim.y workgroups also share a row range along k:
-//     each writes its fp32 row partials to a workspace, and the workgroup
-//     that arrives last (a device-scope counter per row range) sums the Q
-//     partials in a fixed order and writes c;
+//     each writes its fp32 row partials to the caller's scratch, and the
+//     workgroup that arrives last (a device-scope counter per row range)
+//     sums the Q partials in a fixed order and writes c;
 //   * an optional fused epilogue (alpha, bias) is one FMA before the store.
 // gemv_realign_kernel -- rows that do not start on 16-byte boundaries: B in
 // aligned granules, a realigned through two shifted LDS copies.
@@ -186,8 +186,8 @@ struct GemvArgs {
   const uint16_t* a;
   uint16_t* c;
   const uint16_t* bias;   // fused epilogue (flags & kFlagEpilogue), may be null
-  float* ws;              // cross-workgroup partials
-  unsigned* cnt;          // cross-workgroup arrival counters
+  float* ws;              // cross-workgroup partials (caller scratch)
+  unsigned* cnt;          // cross-workgroup arrival counters of this Q
   int n, k, flags;
   float alpha;
   int rows_q, rows_r;     // rows per row unit (per wave, or per workgroup)
@@ -447,18 +447,36 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
   }
 
   if constexpr (XWG) {
-    // Publish, count, combine.  The partials were stored at agent scope
-    // (write-through); waiting for every store of the workgroup to complete
-    // before the barrier orders them before the counter update.  The last of
-    // the Q workgroups of this row range reads the partials at agent scope
-    // (past the non-coherent L2) and sums them in a fixed order.  No L2-wide
-    // write-back or invalidate is needed: only these accesses cross XCDs.
+    // Publish, count, combine.  Agent-scope accesses are coherent across the
+    // XCDs' separate L2s: an agent-scope store is written through to the
+    // memory side (sc1), an agent-scope load fetches past L1 and L2 (sc1),
+    // and agent-scope atomics on one address are serialised device-wide.  So:
+    //  * each leader's partial went out as an agent-scope store above;
+    //    s_waitcnt(0) returns once every store of this wave has been
+    //    acknowledged, i.e. is visible to any later agent-scope access, and
+    //    the barrier makes every wave of the workgroup reach that point
+    //    before thread 0 counts the workgroup in (a release without an L2
+    //    write-back: the partials never sat dirty in an L2);
+    //  * the counter is advanced by a wrapping increment (old >= Q-1 -> 0,
+    //    else old + 1).  The workgroup that reads Q-1 is the last of the Q:
+    //    the other Q-1 increments were performed before its own, each after
+    //    its workgroup's partials were visible;
+    //  * that workgroup then reads the Q partials with agent-scope loads,
+    //    issued only after its increment returned (an acquire without an L2
+    //    invalidate: the loads themselves bypass the caches), and sums them
+    //    in k-group order.
+    // The wrap leaves the counter at zero after the Q-th increment, in the
+    // same atomic step, so a counter goes back to zero whenever whole calls
+    // with this Q have completed -- even calls that raced on it (their c is
+    // then undefined).  The host gives every Q its own bank of counters, so
+    // a counter only ever sees one Q.  (A __threadfence() here compiles to a
+    // full L2 write-back and invalidate and made the split 10x slower.)
     __shared__ int last;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-      last = __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(Q - 1);
+      last = __builtin_amdgcn_atomic_inc32(&cnt[blockIdx.x], (unsigned)(Q - 1), __ATOMIC_RELAXED,
+                                           "agent") == (unsigned)(Q - 1);
     }
     __syncthreads();
     if (last) {
@@ -471,8 +489,6 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
         s = wave_sum(s);
         if (lane == 0) c[r] = to_bits<DT>(finish<DT>(s, flags, alpha, bias, r));
       }
-      if (threadIdx.x == 0)   // ready for the next call
-        __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -28,8 +28,6 @@ struct gemv_handle_s {
   size_t max_lds;
   int log;
   gemv_config_t forced;
-  float* ws;           // partial sums of the cross-workgroup split (device)
-  unsigned* cnt;       // its arrival counters (device), zero between kernels
   size_t static_lds[mbd_host::kMaxVariants][2];   // LDS each kernel declares statically
 };
 

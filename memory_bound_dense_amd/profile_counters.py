@@ -81,10 +81,11 @@ def plan_signature(variant, grid, kgroups):
 
 
 def workload_plan_signature(n, k, dtype):
-    """The automatic plan of a workload (host rule, 16-byte aligned B)."""
+    """The automatic plan of a workload (host rule, 16-byte aligned B, with
+    caller scratch: the plan gemv_run_ws launches and the benchmark times)."""
     sys.path.insert(0, ROOT)
     import memory_bound_dense_amd as mbd
-    s, cfg = mbd.gemv_plan_config(n, k, dtype, 1, 160 * 1024)
+    s, cfg = mbd.gemv_plan_config(n, k, dtype, 1, 160 * 1024, 1)
     if s != mbd.GEMV_OK:
         raise RuntimeError(mbd.gemv_status_string(s))
     return plan_signature(cfg.variant, cfg.grid, cfg.kgroups)
@@ -109,7 +110,7 @@ def run_gemv(workload, launches, variant=-1, grid=0):
     As = [a0] + [a0.clone() for _ in range(nbuf - 1)]
     Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]
     torch.cuda.synchronize()
-    g = mbd.Gemv()
+    g = mbd.Gemv(workspace=True)
     if variant >= 0:
         g.force_config(variant, grid)
     v, grid, kgroups = g.query_config(n, k, dtype)

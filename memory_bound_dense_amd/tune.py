@@ -63,7 +63,10 @@ def main():
     As = [a0.clone() for _ in range(nbuf)]
     Cs = [torch.empty(n, dtype=td, device=dev) for _ in range(nbuf)]
     P = [(Bs[i].data_ptr(), As[i].data_ptr(), Cs[i].data_ptr()) for i in range(nbuf)]
-    g = mbd.Gemv()
+    # with caller scratch, so that the cross-workgroup variants run too (the
+    # automatic plan is then gemv_run_ws's, as the benchmark times it)
+    g = mbd.Gemv(workspace=True)
+    ws, wsb = g.ws.data_ptr(), g.ws.numel()
     auto = g.query_config(n, k, dtype)
     nv = mbd.gemv_num_variants()
     variants = [int(x) for x in args.variants.split(",")] if args.variants else list(range(nv))
@@ -108,7 +111,7 @@ def main():
             with torch.cuda.stream(side):
                 with torch.cuda.graph(gph, stream=side):
                     for j in range(args.steps):
-                        mbd.gemv_run(g.h, *P[j % nbuf], n, k, dtype, side.cuda_stream)
+                        mbd.gemv_run_ws(g.h, *P[j % nbuf], n, k, dtype, ws, wsb, stream=side.cuda_stream)
             stream.wait_stream(side)
             graphs[i] = gph
         torch.cuda.synchronize()
@@ -116,7 +119,7 @@ def main():
         for i, (v, gr, kq, cfg, fl) in enumerate(cands):
             g.force_config(v, gr, kq, fl)
             for j in range(5):
-                mbd.gemv_run(g.h, *P[j % nbuf], n, k, dtype, sp)
+                mbd.gemv_run_ws(g.h, *P[j % nbuf], n, k, dtype, ws, wsb, stream=sp)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -125,7 +128,7 @@ def main():
                 graphs[i].replay()
             else:
                 for j in range(args.steps):
-                    mbd.gemv_run(g.h, *P[j % nbuf], n, k, dtype, sp)
+                    mbd.gemv_run_ws(g.h, *P[j % nbuf], n, k, dtype, ws, wsb, stream=sp)
             e1.record(stream)
             torch.cuda.synchronize()
             times[i].append(e0.elapsed_time(e1) * 1e3 / args.steps)

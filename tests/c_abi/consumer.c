@@ -13,6 +13,7 @@
 int main(void) {
   /* every entry point, taken by address: a missing export fails the link */
   void* fns[] = {(void*)&gemv_create,        (void*)&gemv_run,          (void*)&gemv_run_ex,
+                 (void*)&gemv_run_ws,
                  (void*)&gemv_destroy,       (void*)&gemv_status_string, (void*)&gemv_check_args,
                  (void*)&gemv_check_args_ex, (void*)&gemv_num_variants,  (void*)&gemv_variant_info,
                  (void*)&gemv_force_config,  (void*)&gemv_query_config,  (void*)&gemv_plan_config,
@@ -35,7 +36,7 @@ int main(void) {
 
   gemv_config_t cfg;
   memset(&cfg, 0, sizeof cfg);
-  gemv_status_t s = gemv_plan_config(18432, 7168, GEMV_F16, 1, 163840, &cfg);
+  gemv_status_t s = gemv_plan_config(18432, 7168, GEMV_F16, 1, 163840, 0, &cfg);
   gemv_variant_info_t info;
   memset(&info, 0, sizeof info);
   if (s == GEMV_OK) s = gemv_variant_info(cfg.variant, &info);
@@ -43,6 +44,11 @@ int main(void) {
   printf("plan_shape R%d U%d W%d S%d grid %d\n", info.rows, info.unroll, info.waves, info.splits,
          cfg.grid);
   printf("variants %d\n", (int)gemv_num_variants());
+  gemv_config_t xw;
+  memset(&xw, 0, sizeof xw);
+  s = gemv_plan_config(64, 65536, GEMV_BF16, 1, 163840, 1, &xw);
+  printf("plan_ws_kgroups %d %d\n", (int)s, xw.kgroups);
+  printf("workspace_bytes %lld\n", (long long)GEMV_WORKSPACE_BYTES);
 
   printf("gla_check %d\n", (int)gla_check_args((const void*)(uintptr_t)(1ull << 40), a, c,
                                                (const void*)(uintptr_t)(1ull << 38),
@@ -55,6 +61,8 @@ int main(void) {
   s = gemv_create(&h);
   /* no GPU: a clean error and no handle; with a GPU: a handle, destroyed */
   printf("create %s %s\n", s == GEMV_OK ? "ok" : "error", h ? "handle" : "null");
+  printf("run_ws_null_handle %d\n",
+         (int)gemv_run_ws(NULL, B, a, (void*)c, 4, 8, GEMV_F16, NULL, NULL, 0, 0));
   printf("destroy %d\n", (int)gemv_destroy(h));
   return 0;
 }

@@ -75,9 +75,38 @@ def test_variant_table():
 
 def test_null_handle_rejected():
     assert mbd.gemv_run(None, 256, 512, 1 << 20, 4, 8, 0, None) == _lib.GEMV_ERR_NULL_HANDLE
+    assert mbd.gemv_run_ws(None, 256, 512, 1 << 20, 4, 8, 0, 1 << 30) == _lib.GEMV_ERR_NULL_HANDLE
     assert mbd.gemv_force_config(None, 0, 0) == _lib.GEMV_ERR_NULL_HANDLE
     assert mbd.gemv_query_config(None, 4, 8, 0)[0] == _lib.GEMV_ERR_NULL_HANDLE
     assert mbd.gemv_destroy(None) == mbd.GEMV_OK
+
+
+def test_binding_refuses_tensors_off_the_gpu():
+    """The library takes raw addresses and cannot tell host memory from
+    device memory: the binding refuses CPU tensors, and tensors on another
+    device than B's (q's for GLA), before any call into the library."""
+    import torch
+    g = mbd.Gemv.__new__(mbd.Gemv)       # no handle: the device check comes first
+    g.h, g.ws = None, None
+    B = torch.zeros((4, 8), dtype=torch.float16)
+    a = torch.zeros(8, dtype=torch.float16)
+    c = torch.zeros(4, dtype=torch.float16)
+    with pytest.raises(mbd.GemvError) as e:
+        g(B, a, c)
+    assert e.value.status == _lib.GEMV_ERR_INVALID_ARG and "GPU" in str(e.value)
+    gpu = torch.device("cuda", 0)
+    for t in (a, torch.empty(8, dtype=torch.float16, device="meta")):
+        with pytest.raises(mbd.GemvError) as e:
+            _lib._check_devices((t,), gpu)
+        assert e.value.status == _lib.GEMV_ERR_INVALID_ARG
+    _lib._check_devices((None,), gpu)     # an absent bias is fine
+    gla = mbd.GlaDecode(gemv=g)
+    q = torch.zeros((2, 4), dtype=torch.bfloat16)
+    S = torch.zeros((2, 4, 4), dtype=torch.float32)
+    v = torch.zeros((2, 4), dtype=torch.bfloat16)
+    with pytest.raises(mbd.GemvError) as e:
+        gla(q, q, v, q, S, S, v, 1.0)
+    assert e.value.status == _lib.GEMV_ERR_INVALID_ARG
 
 
 def test_create_without_gpu_fails_cleanly():
@@ -205,6 +234,9 @@ def test_plain_c_consumer(tmp_path):
     assert out["plan_status"] == str(_lib.GEMV_OK)
     assert out["plan_shape"] == "R2 U4 W4 S4 grid 9216"      # the headline's plan
     assert out["variants"] == str(mbd.gemv_num_variants())
+    assert out["plan_ws_kgroups"] == "%d 4" % _lib.GEMV_OK   # 64 x 65536: 4 k-groups with scratch
+    assert out["workspace_bytes"] == str(_lib.GEMV_WORKSPACE_BYTES)
+    assert out["run_ws_null_handle"] == str(_lib.GEMV_ERR_NULL_HANDLE)
     assert out["gla_check"] == str(_lib.GEMV_OK)
     import torch
     if torch.cuda.is_available():

@@ -5,7 +5,7 @@ on the same seeded input bits.
   tails), every compiled variant, full oracle;
 * integer inputs: every variant bit-exact (the fp32 sum is exact);
 * closed forms on the GPU: identity, permutation, one-hot columns;
-* every workload shape at full size, sampled rows, in the automatic
+* every workload shape at full size, every row, in the automatic
   configuration the benchmark times and in every variant;
 * determinism, misaligned base pointers, special values, empty and tiny
   sizes, rejected calls that must not touch c.
@@ -18,25 +18,28 @@ import memory_bound_dense_amd as mbd
 import oracle
 from gemv_inputs import (ALL_WORKLOADS, BF16, EXTRA_WORKLOADS, F16, integer_inputs, random_inputs,
                          torch_dtype, values_to_bits)
-from parity import compare, oracle_rows, sample_rows, to_bits, to_device
+from parity import compare, to_bits, to_device
 
 pytestmark = pytest.mark.gpu
 
 NV = mbd.gemv_num_variants()
 VARIANTS = list(range(NV))
+# The automatic plan through gemv_run_ws with a workspace (-1, the plan the
+# benchmark times) and through gemv_run, which has no scratch (-2).
+AUTO = [-1, -2]
 
 
-def _extra_adds(g, n, k, dtype):
+def _extra_adds(g, n, k, dtype, use_ws=True):
     """fp32 additions after the per-lane sums, beyond the wave tree: the
     in-workgroup slices plus the cross-workgroup k-groups of the plan in use."""
-    v, _, q = g.query_config(n, k, dtype)
+    v, _, q = g.query_config(n, k, dtype, with_workspace=use_ws)
     return mbd.gemv_variant_info(v)[1].splits + (q if q > 1 else 0)
 
 
 @pytest.fixture(scope="module")
 def g():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
-    h = mbd.Gemv()
+    h = mbd.Gemv(workspace=True)
     yield h
     h.close()
 
@@ -69,8 +72,10 @@ def staged_rejects(v, Bd):
 
 
 def run(g, Bd, ad, variant=-1, grid=0, kgroups=0):
-    """c = B @ a with a forced configuration; None if the variant cannot run
-    this shape."""
+    """c = B @ a with a forced configuration (-1: the automatic plan with the
+    workspace, -2: without); None if the variant cannot run this shape."""
+    use_ws = variant != -2
+    variant = max(variant, -1)
     n, k = Bd.shape
     dtype = mbd.GEMV_F16 if Bd.dtype == torch.float16 else mbd.GEMV_BF16
     if not fits(g, variant, n, k, dtype):
@@ -79,7 +84,7 @@ def run(g, Bd, ad, variant=-1, grid=0, kgroups=0):
     g.force_config(variant, grid, kgroups)
     try:
         if n > 0:
-            LAST_EXTRA[0] = _extra_adds(g, n, k, dtype)
+            LAST_EXTRA[0] = _extra_adds(g, n, k, dtype, use_ws)
         if staged_rejects(variant, Bd):
             with pytest.raises(mbd.GemvError) as ei:
                 g(Bd, ad, c)
@@ -87,7 +92,7 @@ def run(g, Bd, ad, variant=-1, grid=0, kgroups=0):
             torch.cuda.synchronize()
             assert torch.all(torch.isnan(c))     # nothing was launched
             return None
-        g(Bd, ad, c)
+        g(Bd, ad, c, use_workspace=use_ws)
     finally:
         g.force_config(-1)
     torch.cuda.synchronize()
@@ -116,7 +121,7 @@ def test_small_shapes_every_variant(g, n, k, dtype, dist):
     B, a = random_inputs(n, k, dtype, dist, seed=0)
     ref, _, ab = oracle.gemv(dtype, B, a)
     Bd, ad = to_device(B, dtype), to_device(a, dtype)
-    for v in [-1] + VARIANTS:
+    for v in AUTO + VARIANTS:
         got = run(g, Bd, ad, v)
         if got is None:
             continue
@@ -132,7 +137,7 @@ def test_integer_inputs_bit_exact_every_variant(g, n, k, dtype):
     B, a = integer_inputs(n, k, dtype, seed=13)
     ref, _, _ = oracle.gemv(dtype, B, a)
     Bd, ad = to_device(B, dtype), to_device(a, dtype)
-    for v in [-1] + VARIANTS:
+    for v in AUTO + VARIANTS:
         got = run(g, Bd, ad, v)
         if got is None:
             continue
@@ -151,7 +156,7 @@ def test_identity_and_permutation(g, dtype):
         Bv[np.arange(n), cols] = 1.0
         _, a = random_inputs(1, k, dtype, seed=5)
         Bd, ad = to_device(values_to_bits(Bv, dtype), dtype), to_device(a, dtype)
-        for v in [-1] + VARIANTS:
+        for v in AUTO + VARIANTS:
             got = run(g, Bd, ad, v)
             assert got is None or np.array_equal(got, a[cols]), (n, k, v)
 
@@ -177,17 +182,20 @@ def test_column_extraction(g, dtype):
 @pytest.mark.parametrize("wl", ALL_WORKLOADS + EXTRA_WORKLOADS,
                          ids=[w[0] for w in ALL_WORKLOADS + EXTRA_WORKLOADS])
 def test_workload_full_size(g, wl):
+    """Every workload at its full size, in every variant and both automatic
+    plans, against the oracle on every row (c starts as NaN, so a row that
+    no workgroup writes fails)."""
     name, n, k, dtype, dist = wl
     B, a = random_inputs(n, k, dtype, dist, seed=0)
-    rows = sample_rows(n)
-    ref, _, ab = oracle_rows(dtype, B, a, rows)
+    ref, _, ab = oracle.gemv(dtype, B, a)
     Bd, ad = to_device(B, dtype), to_device(a, dtype)
     del B
-    for v in [-1] + VARIANTS:
+    print("full-size %s: oracle done, %d variants" % (name, NV), flush=True)
+    for v in AUTO + VARIANTS:
         got = run(g, Bd, ad, v)
         if got is None:
             continue
-        _check(dtype, got[rows], ref, ab, k, v, name)
+        _check(dtype, got, ref, ab, k, v, name)
 
 
 def test_deterministic(g):
@@ -213,7 +221,7 @@ def test_misaligned_base_pointers(g, dtype):
     Bd = Bbig[1:].view(n, k)
     ad = abig[3:]
     assert Bd.data_ptr() % 16 != 0 and ad.data_ptr() % 16 != 0
-    for v in [-1] + VARIANTS:
+    for v in AUTO + VARIANTS:
         if not fits(g, v, n, k, dtype):
             continue
         if staged_rejects(v, Bd):
@@ -221,9 +229,9 @@ def test_misaligned_base_pointers(g, dtype):
             continue
         cbig = torch.full((n + 5,), 7.0, dtype=torch_dtype(dtype), device="cuda")
         c = cbig[5:]
-        g.force_config(v)
-        LAST_EXTRA[0] = _extra_adds(g, n, k, dtype)
-        g(Bd, ad, c)
+        g.force_config(max(v, -1))
+        LAST_EXTRA[0] = _extra_adds(g, n, k, dtype, v != -2)
+        g(Bd, ad, c, use_workspace=v != -2)
         g.force_config(-1)
         torch.cuda.synchronize()
         _check(dtype, to_bits(c), ref, ab, k, v, "misaligned")
@@ -249,7 +257,7 @@ def test_special_values(g, dtype):
     ref, _, _ = oracle.gemv(dtype, Bb, ab)
     Bd, ad = to_device(Bb, dtype), to_device(ab, dtype)
     r = oracle.decode(dtype, ref)
-    for v in [-1] + VARIANTS:
+    for v in AUTO + VARIANTS:
         gb = run(g, Bd, ad, v)
         if gb is None:
             continue
@@ -257,6 +265,108 @@ def test_special_values(g, dtype):
         assert np.array_equal(np.isnan(got), np.isnan(r)), (v, got, r)
         fin = ~np.isnan(r)
         assert np.array_equal(got[fin], r[fin]), (v, got, r)
+
+
+def _golden_cases():
+    """The hand-worked cases of tests/golden/gemv_hand_cases.txt (parsed as
+    the oracle's own pins parse them)."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "gemv_hand_cases.txt")
+    cases, cur = [], None
+    for raw in open(path):
+        line = raw.split("#", 1)[0].strip()
+        if not line:
+            continue
+        tok = line.split()
+        if tok[0] == "case":
+            cur = {"name": tok[1], "dtype": F16 if tok[2] == "f16" else BF16, "B": []}
+        elif tok[0] in ("a", "c"):
+            cur[tok[0]] = [float(t) for t in tok[1:]]
+        elif tok[0] == "end":
+            cases.append(cur)
+        else:
+            cur["B"].append([float(t) for t in tok])
+    return cases
+
+
+def _scaled_integers(n, k, dtype, eb, ea, seed, lo=-2, hi=2):
+    """B = Bi * 2^eb, a = ai * 2^ea with small integers Bi, ai: every value,
+    product and partial sum is exact in fp32, so any summation order gives
+    the exact sum and the GPU must match the oracle bit for bit."""
+    rng = np.random.default_rng(seed)
+    Bv = rng.integers(lo, hi + 1, size=(n, k)).astype(np.float64) * 2.0 ** eb
+    av = rng.integers(lo, hi + 1, size=k).astype(np.float64) * 2.0 ** ea
+    return Bv, av
+
+
+def _edge_cases():
+    """(name, dtype, B values, a values): hand cases and the edges of the
+    dtypes that no random input reaches."""
+    out = [("hand_" + c["name"], c["dtype"], np.array(c["B"]), np.array(c["a"]))
+           for c in _golden_cases()]
+    for n, k in ((37, 1031), (5, 65), (3, 4100)):
+        # bf16: products in [2^-133, 2^-131], fp32 subnormals, summed to
+        # subnormal and small normal bf16 outputs
+        out.append(("bf16_subnormal_products_%dx%d" % (n, k), BF16)
+                   + _scaled_integers(n, k, BF16, -64, -69, seed=n + k))
+        # bf16 subnormal inputs (B = i * 2^-133), normal products
+        out.append(("bf16_subnormal_inputs_%dx%d" % (n, k), BF16)
+                   + _scaled_integers(n, k, BF16, -133, 100, seed=n + k + 1))
+        # fp16: products of normals on a 2^-25 grid, subnormal outputs
+        out.append(("f16_subnormal_outputs_%dx%d" % (n, k), F16)
+                   + _scaled_integers(n, k, F16, -12, -13, seed=n + k + 2, lo=-1, hi=1))
+        # fp16 subnormal inputs (B = i * 2^-24)
+        out.append(("f16_subnormal_inputs_%dx%d" % (n, k), F16)
+                   + _scaled_integers(n, k, F16, -24, 10, seed=n + k + 3))
+    # bf16 overflow at the tie: (2 - 2^-7) 2^127 (the largest bf16) plus half
+    # its spacing rounds to even, i.e. to inf; a quarter of the spacing
+    # rounds back to the largest value.  The fp32 sums stay finite.  The
+    # rows are long, with the two terms far apart, so the sum crosses the
+    # main loop and a k-split.
+    k = 3000
+    Bv = np.zeros((4, k))
+    big = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    Bv[0, 3], Bv[0, 2900] = big, 2.0 ** 119
+    Bv[1, 3], Bv[1, 2900] = big, 2.0 ** 118
+    Bv[2, 3], Bv[2, 2900] = -big, -(2.0 ** 119)
+    Bv[3, 0] = 1.0
+    out.append(("bf16_overflow_tie", BF16, Bv, np.ones(k)))
+    # fp16: a finite fp32 sum past the largest fp16 (1100 * 64 = 70400 -> inf),
+    # and 65504 + 16 = 65520 spread over a long row (the tie -> inf)
+    k = 1100
+    Bv = np.zeros((3, k))
+    Bv[0, :] = 64.0
+    Bv[1, 0], Bv[1, 1099] = 65504.0, 16.0
+    Bv[2, 0], Bv[2, 1099] = 65504.0, 8.0
+    out.append(("f16_finite_sum_overflow", F16, Bv, np.ones(k)))
+    return out
+
+
+EDGE = _edge_cases()
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_values_bit_exact_every_variant(g, case):
+    """Subnormal inputs and outputs (no flush to zero in the fp32 FMAs or in
+    the conversions), the overflow ties and finite sums past the largest
+    16-bit value, and the hand-worked cases: every sum is exact in fp32, so
+    every variant must give the oracle's bits."""
+    name, dtype, Bv, av = case
+    Bb, ab = values_to_bits(Bv, dtype), values_to_bits(av, dtype)
+    assert np.array_equal(oracle.decode(dtype, Bb), Bv), "inputs must be representable"
+    assert np.array_equal(oracle.decode(dtype, ab), av)
+    ref, _, _ = oracle.gemv(dtype, Bb, ab)
+    Bd, ad = to_device(Bb, dtype), to_device(ab, dtype)
+    ran = 0
+    for v in AUTO + VARIANTS:
+        got = run(g, Bd, ad, v)
+        if got is None:
+            continue
+        ran += 1
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, "%s variant %d rows %s: gpu %s ref %s" % (
+            name, v, bad[:5], oracle.decode(dtype, got[bad[:5]]), oracle.decode(dtype, ref[bad[:5]]))
+    assert ran >= len(VARIANTS) // 2
 
 
 def test_empty_and_tiny(g):
@@ -272,12 +382,12 @@ def test_empty_and_tiny(g):
         B = torch.empty((5, 0), dtype=td, device=dev)
         a = torch.empty(0, dtype=td, device=dev)
         c = torch.full((5,), 3.0, dtype=td, device=dev)
-        for v in [-1] + VARIANTS:
+        for v in AUTO + VARIANTS:
             if not fits(g, v, 5, 0, dtype):
                 continue
             c.fill_(3.0)
-            g.force_config(v)
-            g(B, a, c)
+            g.force_config(max(v, -1))
+            g(B, a, c, use_workspace=v != -2)
             g.force_config(-1)
             torch.cuda.synchronize()
             assert torch.all(c == 0), v
@@ -337,7 +447,7 @@ def test_cross_workgroup_split(g, n, k, dtype):
     for v in XWG:
         for q in (1, 2, 3, 8, 33, 64):
             for grid in (0, 1, 3):
-                if q * n > (1 << 20):
+                if q * n > (1 << 18):       # the partials' share of the workspace
                     continue
                 for _ in range(2):
                     got = run(g, Bd, ad, v, grid, q)
@@ -360,9 +470,33 @@ def test_cross_workgroup_config_rules(g):
     a = torch.zeros(k, dtype=torch.float16, device="cuda")
     c = torch.full((n,), 5.0, dtype=torch.float16, device="cuda")
     g.force_config(v, 0, 64)
-    with pytest.raises(mbd.GemvError):
+    with pytest.raises(mbd.GemvError) as e:
         g(B, a, c)
+    assert e.value.status == mbd._lib.GEMV_ERR_UNSUPPORTED
     g.force_config(-1)
+    torch.cuda.synchronize()
+    assert torch.all(c == 5.0)
+    # a cross-workgroup variant needs the caller's scratch: not from gemv_run
+    n, k = 64, 4096
+    B, a, c = B[:n, :k].contiguous(), a[:k].contiguous(), c[:n].contiguous()
+    g.force_config(v, 0, 4)
+    try:
+        with pytest.raises(mbd.GemvError) as e:
+            g(B, a, c, use_workspace=False)
+        assert e.value.status == mbd._lib.GEMV_ERR_UNSUPPORTED
+    finally:
+        g.force_config(-1)
+    # workspace checks: too small, misaligned, overlapping c or B
+    sp = torch.cuda.current_stream().cuda_stream
+    ws, nb = g.ws.data_ptr(), g.ws.numel()
+    big = torch.zeros(nb + 4096, dtype=torch.uint8, device="cuda")
+    for wptr, wbytes, want in [(ws, nb - 1, mbd._lib.GEMV_ERR_INVALID_ARG),
+                               (big.data_ptr() + 8, nb, mbd._lib.GEMV_ERR_MISALIGNED),
+                               (c.data_ptr() - 1024, nb, mbd._lib.GEMV_ERR_ALIASING),
+                               (B.data_ptr() + 4096, nb, mbd._lib.GEMV_ERR_ALIASING)]:
+        s = mbd.gemv_run_ws(g.h, B.data_ptr(), a.data_ptr(), c.data_ptr(), n, k, mbd.GEMV_F16,
+                            wptr, wbytes, stream=sp)
+        assert s == want, (wptr - ws, wbytes, s)
     torch.cuda.synchronize()
     assert torch.all(c == 5.0)
 
@@ -382,10 +516,11 @@ def test_query_config_matches_the_host_plan(g):
     for n in (1, 64, 127, 128, 1000, 2048, 4096, 18432, 18433):
         for k in (1, 512, 7168, 7169, 12289, 16383, 65536):
             for dtype in (F16, BF16):
-                v, grid, q = g.query_config(n, k, dtype)
-                s, cfg = mbd.gemv_plan_config(n, k, dtype, 1, 160 * 1024)
-                assert s == mbd.GEMV_OK
-                assert (v, grid, q) == (cfg.variant, cfg.grid, cfg.kgroups), (n, k, dtype)
+                for ws in (0, 1):
+                    v, grid, q = g.query_config(n, k, dtype, with_workspace=ws)
+                    s, cfg = mbd.gemv_plan_config(n, k, dtype, 1, 160 * 1024, ws)
+                    assert s == mbd.GEMV_OK
+                    assert (v, grid, q) == (cfg.variant, cfg.grid, cfg.kgroups), (n, k, dtype, ws)
 
 
 REALIGN = [v for v in VARIANTS if mbd.gemv_variant_info(v)[1].a_mode == 2]
@@ -468,11 +603,12 @@ def run_ex(g, Bd, ad, alpha, bias, variant=-1, c=None):
         return None
     if c is None:
         c = torch.full((n,), float("nan"), dtype=Bd.dtype, device=Bd.device)
-    g.force_config(variant)
+    use_ws = variant != -2
+    g.force_config(max(variant, -1))
     try:
         if n > 0:
-            LAST_EXTRA[0] = _extra_adds(g, n, k, dtype)
-        g(Bd, ad, c, alpha=alpha, bias=bias)
+            LAST_EXTRA[0] = _extra_adds(g, n, k, dtype, use_ws)
+        g(Bd, ad, c, alpha=alpha, bias=bias, use_workspace=use_ws)
     finally:
         g.force_config(-1)
     torch.cuda.synchronize()
@@ -498,7 +634,7 @@ def test_epilogue_every_variant(g, n, k, dtype):
         for with_bias in (False, True):
             ref, y, ab = oracle.gemv_epilogue(dtype, B, a, alpha, bias_bits if with_bias else None)
             a32 = abs(float(np.float32(alpha)))
-            for v in [-1] + VARIANTS:
+            for v in AUTO + VARIANTS:
                 got = run_ex(g, Bd, ad, alpha, biasd if with_bias else None, v)
                 if got is None:
                     continue
@@ -524,7 +660,7 @@ def test_epilogue_integer_exact_and_in_place(g, dtype):
     Bd, ad = to_device(B, dtype), to_device(a, dtype)
     for alpha in (2.0, -0.25):
         ref, _, _ = oracle.gemv_epilogue(dtype, B, a, alpha, bias_bits)
-        for v in [-1] + VARIANTS:
+        for v in AUTO + VARIANTS:
             biasd = to_device(bias_bits, dtype)
             got = run_ex(g, Bd, ad, alpha, biasd, v)
             if got is None:

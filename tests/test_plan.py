@@ -19,8 +19,10 @@ from gemv_inputs import ALL_WORKLOADS, BF16, EXTRA_WORKLOADS, F16
 MAX_LDS = 160 * 1024          # bytes of LDS per workgroup on MI355X
 
 
-def plan(n, k, dtype, aligned=True):
-    s, cfg = mbd.gemv_plan_config(n, k, dtype, 1 if aligned else 0, MAX_LDS)
+def plan(n, k, dtype, aligned=True, ws=True):
+    """The plan of gemv_run_ws with a workspace (ws=True, what the benchmark
+    times) or of gemv_run / gemv_run_ex (ws=False)."""
+    s, cfg = mbd.gemv_plan_config(n, k, dtype, 1 if aligned else 0, MAX_LDS, 1 if ws else 0)
     assert s == mbd.GEMV_OK, (n, k, dtype, aligned, mbd.gemv_status_string(s))
     info = mbd.gemv_variant_info(cfg.variant)[1]
     return cfg, info
@@ -222,6 +224,24 @@ def test_plan_cross_workgroup_only_for_few_rows(n, k, xwg):
         assert shape_of(info) == (1, 4, 8, 8, 1, 1)
 
 
+def test_plan_without_workspace_never_splits_across_workgroups():
+    """gemv_run and gemv_run_ex bring no scratch: their plan is the
+    workspace plan wherever that is not a cross-workgroup split, and the
+    in-workgroup split (one row per 8-wave workgroup, eight k-slices) where
+    it is."""
+    ns = [1, 7, 8, 32, 63, 64, 65, 127, 128, 1000, 18432]
+    ks = [0, 511, 16384, 32768, 65535, 65536, 131072, 200000]
+    for n, k, dtype in itertools.product(ns, ks, (F16, BF16)):
+        cfg0, info0 = plan(n, k, dtype, ws=False)
+        cfg1, info1 = plan(n, k, dtype, ws=True)
+        assert not info0.cross_wg and cfg0.kgroups == 1
+        if info1.cross_wg:
+            assert shape_of(info0) == (1, 4, 8, 8, 1, 0) and cfg0.grid == n, (n, k)
+        else:
+            assert (cfg0.variant, cfg0.grid, cfg0.kgroups) == \
+                (cfg1.variant, cfg1.grid, cfg1.kgroups), (n, k, dtype)
+
+
 @pytest.mark.parametrize("n,k", [(127, 65536), (96, 65536), (64, 32768), (32, 16384), (1, 16384)])
 def test_plan_few_rows_split_in_workgroup(n, k):
     # fewer than 128 rows of >= 32 steps, not split across workgroups: one
@@ -265,4 +285,5 @@ def test_plan_rejects_bad_arguments(args, expect):
 
 def test_plan_null_output():
     lib = _lib.load()
-    assert lib.gemv_plan_config(4, 8, 0, 1, MAX_LDS, None) == _lib.GEMV_ERR_INVALID_ARG
+    assert lib.gemv_plan_config(4, 8, 0, 1, MAX_LDS, 0, None) == _lib.GEMV_ERR_INVALID_ARG
+    assert lib.gemv_plan_config(4, 8, 0, 1, MAX_LDS, 1, None) == _lib.GEMV_ERR_INVALID_ARG

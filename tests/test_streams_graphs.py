@@ -4,8 +4,9 @@
   each path: rows, in-workgroup split, cross-workgroup split, realigned
   rows) replay correctly, every replay checked against the eager result,
   with eager work and synchronisations between replays;
-* streams: two handles driving two streams (default priority) with host
-  delays in between give bitwise the same c as a quiet run.
+* streams: ONE handle driving two streams (default priority) at once, with
+  host delays in between -- gemv_run with no scratch, and gemv_run_ws with
+  one workspace per stream -- gives bitwise the same c as a quiet run.
 """
 import random
 import time
@@ -33,7 +34,7 @@ def _inputs():
 
 
 def test_graph_capture_replays():
-    g = mbd.Gemv()
+    g = mbd.Gemv(workspace=True)
     ins = _inputs()
     eager = []
     for Bd, ad in ins:
@@ -69,36 +70,59 @@ def test_graph_capture_replays():
     g.close()
 
 
-def test_two_streams_two_handles_repeatable():
+def test_two_streams_one_handle_repeatable():
+    """The handle is read-only after gemv_create, so one handle may serve two
+    streams at once.  Every shape (the 64 x 65536 one included, whose
+    scratch-free plan splits k inside a workgroup) runs on both streams,
+    interleaved in random order with random host delays: through gemv_run,
+    and through gemv_run_ws with a workspace per stream (the 64 x 65536 plan
+    then splits k across workgroups on both streams at once).  Every result
+    must have the bits of a quiet run of the same entry point."""
     ins = _inputs()
-    g1, g2 = mbd.Gemv(), mbd.Gemv()
+    g = mbd.Gemv()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-    ref = []
-    for Bd, ad in ins:
-        c = torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda")
-        g1(Bd, ad, c)
-        torch.cuda.synchronize()
-        ref.append(to_bits(c))
+    ws = [torch.zeros(mbd._lib.GEMV_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+          for _ in range(2)]
+    sp = (s1.cuda_stream, s2.cuda_stream)
+    torch.cuda.synchronize()          # inputs and zeroed workspaces ready for both streams
+    dt = lambda Bd: mbd.GEMV_F16 if Bd.dtype == torch.float16 else mbd.GEMV_BF16
+
+    def call(Bd, ad, c, which, use_ws):
+        n, k = Bd.shape
+        if use_ws:
+            st = mbd.gemv_run_ws(g.h, Bd.data_ptr(), ad.data_ptr(), c.data_ptr(), n, k, dt(Bd),
+                                 ws[which].data_ptr(), ws[which].numel(), stream=sp[which])
+        else:
+            st = mbd.gemv_run(g.h, Bd.data_ptr(), ad.data_ptr(), c.data_ptr(), n, k, dt(Bd),
+                              sp[which])
+        assert st == mbd.GEMV_OK
+
+    assert g.query_config(64, 65536, mbd.GEMV_BF16, with_workspace=1)[2] > 1
+    assert g.query_config(64, 65536, mbd.GEMV_BF16, with_workspace=0)[2] == 1
     rng = random.Random(0)
-    outs1 = [torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda") for Bd, _ in ins]
-    outs2 = [torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda") for Bd, _ in ins]
-    for it in range(40):
-        order = list(range(len(ins)))
-        rng.shuffle(order)
-        for i in order:
-            Bd, ad = ins[i]
-            with torch.cuda.stream(s1):
-                g1(Bd, ad, outs1[i])
-            if rng.random() < 0.3:
-                time.sleep(rng.random() * 1e-4)
-            with torch.cuda.stream(s2):
-                g2(Bd, ad, outs2[i])
-        torch.cuda.synchronize()
-        for i in range(len(ins)):
-            assert np.array_equal(to_bits(outs1[i]), ref[i]), (it, SHAPES[i])
-            assert np.array_equal(to_bits(outs2[i]), ref[i]), (it, SHAPES[i])
-    g1.close()
-    g2.close()
+    for use_ws in (False, True):
+        ref = []
+        for Bd, ad in ins:
+            c = torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda")
+            call(Bd, ad, c, 0, use_ws)
+            torch.cuda.synchronize()
+            ref.append(to_bits(c))
+        outs = [[torch.empty(Bd.shape[0], dtype=Bd.dtype, device="cuda") for Bd, _ in ins]
+                for _ in range(2)]
+        for it in range(40):
+            order = list(range(len(ins)))
+            rng.shuffle(order)
+            for i in order:
+                Bd, ad = ins[i]
+                call(Bd, ad, outs[0][i], 0, use_ws)
+                if rng.random() < 0.3:
+                    time.sleep(rng.random() * 1e-4)
+                call(Bd, ad, outs[1][i], 1, use_ws)
+            torch.cuda.synchronize()
+            for i in range(len(ins)):
+                for w in range(2):
+                    assert np.array_equal(to_bits(outs[w][i]), ref[i]), (use_ws, it, w, SHAPES[i])
+    g.close()
 
 
 def test_stress_split_and_lds_variants_repeatable():
@@ -107,7 +131,7 @@ def test_stress_split_and_lds_variants_repeatable():
     explicit waits): 150 back-to-back runs each with
     random host delays and eager work between them must all give the bits
     of the first run."""
-    g = mbd.Gemv()
+    g = mbd.Gemv(workspace=True)
     rng = random.Random(7)
     picks = []
     for v in range(mbd.gemv_num_variants()):
