@@ -77,7 +77,9 @@ typedef enum {
   GEMV_ERR_UNSUPPORTED_DTYPE = 3, /* dtype is not GEMV_F16 / GEMV_BF16 */
   GEMV_ERR_MISALIGNED = 4,        /* a pointer is not 2-byte aligned */
   GEMV_ERR_ALIASING = 5,          /* c overlaps B or a */
-  GEMV_ERR_TOO_LARGE = 6,         /* n > 2^30 or k > 2^27 */
+  GEMV_ERR_TOO_LARGE = 6,         /* n > 2^30 or k > 2^27, or a forced k-split
+                                     across workgroups whose partials
+                                     (k-groups x n) exceed the scratch */
   GEMV_ERR_WRONG_DEVICE = 7,      /* current HIP device != the handle's */
   GEMV_ERR_UNSUPPORTED = 8,       /* no kernel for this GPU / configuration */
   GEMV_ERR_HIP = 9,               /* a HIP runtime call failed */

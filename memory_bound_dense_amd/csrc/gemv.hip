@@ -405,7 +405,7 @@ static gemv_status_t shape_launch(int v, int64_t g, int64_t q, int flags, int64_
     // the scratch holds q partials per row and one counter per row range
     // (a smaller grid is valid: each workgroup walks a longer row range)
     if (g > kXwgRanges) g = kXwgRanges;
-    if (q * n > (int64_t)kWsFloats) return GEMV_ERR_UNSUPPORTED;
+    if (q * n > (int64_t)kWsFloats) return GEMV_ERR_TOO_LARGE;   // more partials than the scratch holds
   } else {
     if (q > 1) return GEMV_ERR_INVALID_ARG;
     q = 1;
@@ -599,7 +599,9 @@ extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void*
   if (dev != h->device) return report(h, GEMV_ERR_WRONG_DEVICE, "gemv_run");
   Launch L;
   s = resolve(h, n, k, dtype, ((uintptr_t)B & 15u) == 0, workspace != nullptr, &L);
-  if (s != GEMV_OK) return report(h, s, "no variant fits (LDS, or scratch for the k-split)");
+  if (s != GEMV_OK)
+    return report(h, s, s == GEMV_ERR_TOO_LARGE ? "k-groups x rows exceed the scratch's 2^18 partials"
+                                                : "no variant fits (LDS, or scratch for the k-split)");
   const Variant& var = kVariants[L.variant];
   const gemv_variant_info_t& vi = var.info;
   mbd::GemvArgs p;

@@ -1,5 +1,5 @@
 """Helpers shared by the GPU parity tests: device transfer of raw 16-bit
-patterns, the comparison rules, and row sampling for full-size shapes.
+patterns and the comparison rules.
 
 Comparison rules for c = B @ a in fp16/bf16 with an fp32 sum:
   * grading tolerance  |c_gpu - c_ref| <= 4e-3 * sum_j |B_ij a_j| + ulp(c_ref)
@@ -68,17 +68,3 @@ def compare(dtype, c_gpu_bits, c_ref_bits, absum, k, splits=1):
         first = dict(row=i, gpu=float(g[i]), ref=float(r[i]), abs=float(absum[i]))
     return (bool(ok_g.all()), bool(ok_s.all()), float(np.max(rg, initial=0.0)),
             float(np.max(rs, initial=0.0)), first)
-
-
-def sample_rows(n: int, count: int = 192, seed: int = 0) -> np.ndarray:
-    """First and last rows, rows around every multiple of 64, and random rows."""
-    rng = np.random.default_rng(seed)
-    rows = set(range(min(n, 8))) | set(range(max(0, n - 8), n))
-    rows |= set(int(x) for x in rng.integers(0, n, size=count))
-    return np.array(sorted(rows), dtype=np.int64)
-
-
-def oracle_rows(dtype, B_bits, a_bits, rows):
-    """The oracle on a subset of rows (gathering rows is plumbing)."""
-    c, s, ab = oracle.gemv(dtype, B_bits[rows], a_bits)
-    return c, s, ab
