@@ -149,6 +149,23 @@ gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void* a, void* c
                           int64_t n, int64_t k, gemv_dtype_t dtype, const gemv_epilogue_t* ep,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gemv_run_ws with the library's own static scratch in place of a caller
+ * workspace -- GEMV_WORKSPACE_BYTES per GPU, in the library's image, its
+ * device address resolved and zero-filled by gemv_create on each GPU and
+ * held until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine) and never synchronises.  Every call on one
+ * GPU shares that GPU's scratch: calls that may overlap on the GPU (other
+ * streams, other handles, other threads) race -- their c is undefined --
+ * so issue them on one stream or order them; gemv_run_ws with a workspace
+ * per stream has no such limit.  A forced k-split across workgroups whose
+ * partials (k-groups x n) exceed the scratch's 2^18 is GEMV_ERR_TOO_LARGE;
+ * the automatic plan never needs more.  Otherwise as gemv_run_ws. */
+gemv_status_t gemv_run_noalloc(gemv_handle_t h, const void* B, const void* a, void* c,
+                               int64_t n, int64_t k, gemv_dtype_t dtype,
+                               const gemv_epilogue_t* ep, hipStream_t stream);
+
 /* Every check gemv_run makes that needs neither a handle nor a GPU, in the
  * same order and with the same result: GEMV_OK means gemv_run would go on to
  * the device check and the launch (or return GEMV_OK at once when n == 0).

@@ -36,7 +36,8 @@ GEMV_MAX_K = 134217728
 GEMV_WORKSPACE_BYTES = 1310720
 
 # every symbol include/gemv.h and include/gla_decode.h declare
-EXPORTS = ("gemv_create", "gemv_run", "gemv_run_ex", "gemv_run_ws", "gemv_destroy",
+EXPORTS = ("gemv_create", "gemv_run", "gemv_run_ex", "gemv_run_ws", "gemv_run_noalloc",
+           "gemv_destroy",
            "gemv_status_string",
            "gemv_check_args", "gemv_check_args_ex", "gemv_num_variants", "gemv_variant_info",
            "gemv_force_config", "gemv_query_config", "gemv_plan_config", "gla_decode_step",
@@ -90,6 +91,9 @@ def load():
     lib.gemv_run_ws.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int,
                                 ctypes.POINTER(gemv_epilogue_t), vp, ctypes.c_size_t, vp]
     lib.gemv_run_ws.restype = st
+    lib.gemv_run_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int,
+                                     ctypes.POINTER(gemv_epilogue_t), vp]
+    lib.gemv_run_noalloc.restype = st
     lib.gemv_check_args_ex.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int,
                                        ctypes.POINTER(gemv_epilogue_t)]
     lib.gemv_check_args_ex.restype = st
@@ -148,6 +152,15 @@ def gemv_run_ws(h, B, a, c, n, k, dtype, workspace, workspace_bytes=GEMV_WORKSPA
     if alpha is not None or bias is not None:
         ep = ctypes.byref(gemv_epilogue_t(1.0 if alpha is None else alpha, bias))
     return load().gemv_run_ws(h, B, a, c, n, k, dtype, ep, workspace, workspace_bytes, stream)
+
+
+def gemv_run_noalloc(h, B, a, c, n, k, dtype, alpha=None, bias=None, stream=None):
+    """gemv_run_ws on the library's static scratch (allocates nothing); no
+    epilogue when alpha and bias are both None."""
+    ep = None
+    if alpha is not None or bias is not None:
+        ep = ctypes.byref(gemv_epilogue_t(1.0 if alpha is None else alpha, bias))
+    return load().gemv_run_noalloc(h, B, a, c, n, k, dtype, ep, stream)
 
 
 def gemv_check_args_ex(B, a, c, n, k, dtype, alpha=None, bias=None):

@@ -8,6 +8,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gemv_kernel.h"
 #include "gemv_staged.h"
 #include "handle.h"
@@ -316,6 +318,37 @@ Plan auto_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
 
 static_assert(kNumVariants <= kMaxVariants, "the handle keeps per-variant LDS for kMaxVariants");
 
+// The scratch of gemv_run_noalloc, for callers that cannot allocate: the
+// layout of a gemv_run_ws workspace (counters, then partials), one copy per
+// GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address on each GPU comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[GEMV_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];   // this GPU's copy of `scratch`, once resolved
+}  // namespace
+
+// With device `dev` current: the device address of its copy of `scratch`,
+// resolved and zero-filled on the first call for that device.
+static gemv_status_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return GEMV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GEMV_ERR_HIP;
+    // the arrival counters start at zero (every completed call leaves them so)
+    if (hipMemset(p, 0, (size_t)GEMV_WORKSPACE_BYTES) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
+      return GEMV_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return GEMV_OK;
+}
+
 extern "C" const char* gemv_status_string(gemv_status_t s) {
   switch (s) {
     case GEMV_OK: return "GEMV_OK";
@@ -477,8 +510,12 @@ extern "C" gemv_status_t gemv_create(gemv_handle_t* out) {
   int max_lds = 0;
   if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return report(nullptr, GEMV_ERR_HIP, "hipDeviceGetAttribute(max LDS)");
+  void* scr = nullptr;
+  const gemv_status_t ss = scratch_address(dev, &scr);
+  if (ss != GEMV_OK) return report(nullptr, ss, "hipGetSymbolAddress(scratch)");
   gemv_handle_s* h = (gemv_handle_s*)calloc(1, sizeof(gemv_handle_s));
   if (!h) return GEMV_ERR_OOM;
+  h->scratch = scr;
   for (int v = 0; v < kNumVariants; ++v) {
     for (int d = 0; d < 2; ++d) {
       hipFuncAttributes fa;
@@ -637,4 +674,14 @@ extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void*
                                  dim3((unsigned)(var.info.waves * mbd::kLanes)), args, L.lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));
   return GEMV_OK;
+}
+
+extern "C" gemv_status_t gemv_run_noalloc(gemv_handle_t h, const void* B, const void* a, void* c,
+                                          int64_t n, int64_t k, gemv_dtype_t dtype,
+                                          const gemv_epilogue_t* ep, hipStream_t stream) {
+  if (!h || h->magic != kMagic) return report(nullptr, GEMV_ERR_NULL_HANDLE, "gemv_run_noalloc");
+  // gemv_run_ws on this GPU's static scratch: validation, plan and launch
+  // allocate nothing; a plan needing more partials than the scratch holds
+  // (a forced k-split only) is GEMV_ERR_TOO_LARGE
+  return gemv_run_ws(h, B, a, c, n, k, dtype, ep, h->scratch, (size_t)GEMV_WORKSPACE_BYTES, stream);
 }

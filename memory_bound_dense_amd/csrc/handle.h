@@ -28,6 +28,7 @@ struct gemv_handle_s {
   size_t max_lds;
   int log;
   gemv_config_t forced;
+  void* scratch;       // device address of this GPU's copy of the library's static scratch
   size_t static_lds[mbd_host::kMaxVariants][2];   // LDS each kernel declares statically
 };
 

@@ -13,7 +13,7 @@
 int main(void) {
   /* every entry point, taken by address: a missing export fails the link */
   void* fns[] = {(void*)&gemv_create,        (void*)&gemv_run,          (void*)&gemv_run_ex,
-                 (void*)&gemv_run_ws,
+                 (void*)&gemv_run_ws,        (void*)&gemv_run_noalloc,
                  (void*)&gemv_destroy,       (void*)&gemv_status_string, (void*)&gemv_check_args,
                  (void*)&gemv_check_args_ex, (void*)&gemv_num_variants,  (void*)&gemv_variant_info,
                  (void*)&gemv_force_config,  (void*)&gemv_query_config,  (void*)&gemv_plan_config,
@@ -63,6 +63,8 @@ int main(void) {
   printf("create %s %s\n", s == GEMV_OK ? "ok" : "error", h ? "handle" : "null");
   printf("run_ws_null_handle %d\n",
          (int)gemv_run_ws(NULL, B, a, (void*)c, 4, 8, GEMV_F16, NULL, NULL, 0, 0));
+  printf("run_noalloc_null_handle %d\n",
+         (int)gemv_run_noalloc(NULL, B, a, (void*)c, 4, 8, GEMV_F16, NULL, 0));
   printf("destroy %d\n", (int)gemv_destroy(h));
   return 0;
 }

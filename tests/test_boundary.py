@@ -237,6 +237,7 @@ def test_plain_c_consumer(tmp_path):
     assert out["plan_ws_kgroups"] == "%d 4" % _lib.GEMV_OK   # 64 x 65536: 4 k-groups with scratch
     assert out["workspace_bytes"] == str(_lib.GEMV_WORKSPACE_BYTES)
     assert out["run_ws_null_handle"] == str(_lib.GEMV_ERR_NULL_HANDLE)
+    assert out["run_noalloc_null_handle"] == str(_lib.GEMV_ERR_NULL_HANDLE)
     assert out["gla_check"] == str(_lib.GEMV_OK)
     import torch
     if torch.cuda.is_available():
