@@ -82,6 +82,17 @@ def read_traffic(workload, n_launch_bytes, plan, sources=None):
         return None
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(B_bits, a_bits, dtype, n, k, target_s=10.0):
     """The oracle, as it is, timed on the host: whole calls on the same
     inputs, repeated until about `target_s` seconds have passed (or, if one
@@ -109,8 +120,8 @@ def cpu_baseline(B_bits, a_bits, dtype, n, k, target_s=10.0):
         what = "%d whole calls" % calls
     nbytes = 2 * (rows * k + k + rows) * calls
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%s (n=%d, k=%d), %.1f s single-threaded on %s" % (
-                what, n, k, dt, platform.processor() or platform.machine()),
+            "sample": "%s (n=%d, k=%d), %.1f s on 1 thread" % (what, n, k, dt),
+            "host_cores": os.cpu_count(), "host_cpu": cpu_model(),
             "us_per_call": round(dt / calls * 1e6 * n / rows, 1)}
 
 
@@ -134,28 +145,51 @@ def time_launches(launch, steps, nbuf, stream, dev, graph):
 
 def stream_probe(nbytes, steps, dev, graph=True):
     """A plain streaming read of the same number of bytes (rounded down to
-    whole 16 KiB chunks), timed like the GEMV (the same launch mode): the
-    practical read ceiling."""
+    whole KiB), timed like the GEMV (the same launch mode), best of a few
+    launch shapes: the practical read ceiling."""
     import torch
     from memory_bound_dense_amd import probe
-    nbytes = nbytes // probe.CHUNK * probe.CHUNK
+    nbytes = nbytes // probe.READ_BLOCK * probe.READ_BLOCK
     nbuf = rotation(nbytes)
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
-    out = torch.empty(1 << 20, dtype=torch.int32, device=dev)
+    out = torch.empty(1 << 24, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     best = None
-    for grid, xcd in ((0, False), (512, False), (512, True), (1024, False), (2048, False)):
-        def launch(i, sp, grid=grid, xcd=xcd):
-            probe.stream_read(bufs[i % nbuf].data_ptr(), nbytes, out.data_ptr(), out.numel(), grid,
-                              True, sp, xcd)
-        for i in range(10):
-            launch(i, stream.cuda_stream)
-        us = time_launches(launch, steps, nbuf, stream, dev, graph)
-        if best is None or us < best[0]:
-            best = (us, grid, xcd)
+    for unroll in (4, 8, 16):
+        for grid in (0, 1024, 2048, 4096):
+            def launch(i, sp, grid=grid, unroll=unroll):
+                probe.stream_read(bufs[i % nbuf].data_ptr(), nbytes, out.data_ptr(), out.numel(),
+                                  grid, unroll, True, sp)
+            for i in range(10):
+                launch(i, stream.cuda_stream)
+            us = time_launches(launch, steps, nbuf, stream, dev, graph)
+            if best is None or us < best[0]:
+                best = (us, grid, unroll)
     del bufs
     return {"bytes": nbytes, "us": round(best[0], 3), "gbs": round(nbytes / best[0] / 1e3, 1),
-            "grid": best[1], "xcd_contiguous": best[2]}
+            "grid": best[1], "unroll": best[2]}
+
+
+def access_probe(vinfo, Bs, n, k, grid, kgroups, ws_ptr, steps, dev, graph=True):
+    """The GEMV launch itself with its arithmetic taken out (the same B
+    loads, grid, k-slices and reductions; a never read), on the same rotated
+    copies of B: what the plan's access pattern costs alone.  None when the
+    probe library has no build of this plan shape."""
+    import torch
+    from memory_bound_dense_amd import probe
+    if not probe.gemv_probe_has(vinfo) or k % 8 != 0:
+        return None
+    nbuf = len(Bs)
+    outs = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(nbuf)]
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(i, sp):
+        probe.gemv_probe(vinfo, Bs[i % nbuf].data_ptr(), n, k, outs[i % nbuf].data_ptr(),
+                         ws_ptr if vinfo.cross_wg else None, grid, kgroups, sp)
+    for i in range(10):
+        launch(i, stream.cuda_stream)
+    us = time_launches(launch, steps, nbuf, stream, dev, graph)
+    return {"bytes_of_B": 2 * n * k, "us": round(us, 3), "gbs": round(2 * n * k / us / 1e3, 1)}
 
 
 # Untimed sustained load before a timed region: on MI355X the memory clocks
@@ -465,10 +499,15 @@ def main():
             ms_per_step * 1e3, value, avg_us, achieved, 100 * achieved / HBM_PEAK_GBS,
             HBM_PEAK_GBS))
 
-    ceiling = stream_probe(2 * n * k, args.steps, dev, not args.stream) if not args.no_probe else None
-    if ceiling:
-        log("[bench] streaming-read probe over the same bytes: %.2f us -> %.1f GB/s" % (
-            ceiling["us"], ceiling["gbs"]))
+    ceiling = access = None
+    if not args.no_probe:
+        ceiling = stream_probe(2 * n * k, args.steps, dev, not args.stream)
+        log("[bench] streaming-read probe over the same bytes: %.2f us -> %.1f GB/s (grid %d, "
+            "unroll %d)" % (ceiling["us"], ceiling["gbs"], ceiling["grid"], ceiling["unroll"]))
+        access = access_probe(vinfo, Bs, n, k, grid, kgroups, ws, args.steps, dev, not args.stream)
+        if access:
+            log("[bench] the same launch without its arithmetic: %.2f us -> %.1f GB/s of B" % (
+                access["us"], access["gbs"]))
     from memory_bound_dense_amd.profile_counters import plan_signature
     # the counter summaries are taken on plain launches (no epilogue)
     traffic = None if args.epilogue else read_traffic(name, step_bytes,
@@ -490,7 +529,7 @@ def main():
                    "variant": variant, "grid": grid, "kgroups": kgroups,
                    "rows_per_wave": vinfo.rows,
                    "unroll": vinfo.unroll, "waves_per_wg": vinfo.waves, "splits": vinfo.splits,
-                   "a_mode": {0: "lds", 1: "cached", 2: "lds_shifted"}[vinfo.a_mode],
+                   "a_mode": {0: "lds", 1: "cached", 2: "lds_shifted", 3: "shifted_window"}[vinfo.a_mode],
                    "layout": ["lanes_along_k", "row_per_lane"][vinfo.layout],
                    "rotating_buffers": nbuf, "launch": "graph" if lau.graph else "stream",
                    "entry": "gemv_run_ws",
@@ -506,6 +545,11 @@ def main():
     }
     if ceiling:
         out["stream_read_probe"] = ceiling
+    if access:
+        out["access_pattern_probe"] = access
+    # the pages' figure for the uncoalesced kernel before their fix (TileLang
+    # Case Studies, Case B, on H200): context for the coalescing, not a target
+    out["context"] = {"pages_uncoalesced_gbs_h200": 110, "pages_coalesced_tbs_h200": [3.65, 3.85]}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(B_bits, a_bits, dtype, n, k)

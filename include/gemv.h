@@ -195,7 +195,9 @@ const char* gemv_status_string(gemv_status_t s);
  * cache hierarchy with the same 16-byte loads; 2: for rows that do not start
  * on a 16-byte boundary, B is read in aligned 16-byte granules starting at
  * the 128-byte line that holds each row's first element, and a is staged in
- * LDS twice (shifted by 0 and 1 element) to line up with them.
+ * LDS twice (shifted by 0 and 1 element) to line up with them; 3: the same
+ * granules of B, and a read through the caches at each row's shift (a 4-byte
+ * aligned 16-byte load and a 2-byte load per granule, joined by a shift).
  * splits > 1 sums the k-slices of a row group in a fixed order through LDS
  * (deterministic). */
 typedef struct {

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemv.so")
 SOURCES = [os.path.join(CSRC, "gemv.hip"), os.path.join(CSRC, "gla.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("gemv_kernel.h", "gemv_staged.h", "gla_kernel.h", "handle.h")] + \
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("gemv_kernel.h", "gemv_shift.h", "gemv_staged.h", "gla_kernel.h",
+                                                     "handle.h")] + \
     [os.path.join(INCLUDE, "gemv.h"), os.path.join(INCLUDE, "gla_decode.h")]
 # measurement aid: a plain streaming read (the practical HBM read ceiling)
 PROBE_LIB = os.path.join(PKG, "libmbd_probe.so")

@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "gemv_kernel.h"
+#include "gemv_shift.h"
 #include "gemv_staged.h"
 #include "handle.h"
 
@@ -41,6 +42,10 @@ constexpr int kLanesPerWave = 64;
    {&mbd::gemv_realign_kernel<mbd::DT_F16, R, U, W, POL>,                           \
     &mbd::gemv_realign_kernel<mbd::DT_BF16, R, U, W, POL>}}
 #define MBD_REALIGN(U, W, POL) MBD_REALIGN_R(1, U, W, POL)
+#define MBD_SHIFT(R, U, W, S)                                                       \
+  {{R, U, W, S, mbd::A_SHIFTED, kPolNT, 0, 0},                                      \
+   {&mbd::gemv_shift_kernel<mbd::DT_F16, R, U, W, S, kPolNT>,                       \
+    &mbd::gemv_shift_kernel<mbd::DT_BF16, R, U, W, S, kPolNT>}}
 #define MBD_STAGED(R, U, W, P, LDS)                                                 \
   {{R, U, W, 1, mbd::A_CACHED, kPolNT, 0, 0, P, LDS},                               \
    {&mbd::gemv_staged_kernel<mbd::DT_F16, R, U, W, P, LDS, kPolNT>,                 \
@@ -65,43 +70,41 @@ const Variant kVariants[] = {
     MBD_VARIANT(2, 2, 4, 1, LDS, NT), MBD_VARIANT(2, 4, 4, 1, LDS, NT),
     MBD_VARIANT(4, 2, 4, 1, LDS, NT), MBD_VARIANT(4, 4, 4, 1, LDS, NT),
     MBD_VARIANT(2, 4, 8, 1, LDS, NT), MBD_VARIANT(4, 2, 8, 1, LDS, NT),
-    // 20..23: default cache policy (for comparison)
-    MBD_VARIANT(1, 4, 4, 1, CCH, 0), MBD_VARIANT(2, 4, 4, 1, CCH, 0),
-    MBD_VARIANT(2, 4, 4, 1, LDS, 0), MBD_VARIANT(4, 2, 4, 1, LDS, 0),
-    // 24..29: other cache-policy bits on one shape (sc0 = 1, sc1 = 16)
-    MBD_VARIANT(2, 4, 4, 1, CCH, 1), MBD_VARIANT(2, 4, 4, 1, CCH, 3),
-    MBD_VARIANT(2, 4, 4, 1, CCH, 16), MBD_VARIANT(2, 4, 4, 1, CCH, 18),
-    MBD_VARIANT(2, 4, 4, 1, CCH, 17), MBD_VARIANT(2, 4, 4, 1, CCH, 19),
-    // 30..41: split variants, a through the caches, non-temporal B
+    // 20..31: split variants, a through the caches, non-temporal B
     MBD_VARIANT(1, 2, 8, 2, CCH, NT), MBD_VARIANT(1, 4, 8, 2, CCH, NT),
     MBD_VARIANT(2, 4, 8, 2, CCH, NT), MBD_VARIANT(1, 2, 8, 4, CCH, NT),
     MBD_VARIANT(1, 4, 8, 4, CCH, NT), MBD_VARIANT(2, 4, 8, 4, CCH, NT),
     MBD_VARIANT(1, 2, 8, 8, CCH, NT), MBD_VARIANT(1, 4, 8, 8, CCH, NT),
     MBD_VARIANT(2, 4, 8, 8, CCH, NT), MBD_VARIANT(1, 4, 4, 4, CCH, NT),
     MBD_VARIANT(1, 2, 16, 16, CCH, NT), MBD_VARIANT(1, 4, 16, 16, CCH, NT),
-    // 42..47: split across workgroups as well (small n)
+    // 32..37: split across workgroups as well (small n)
     MBD_VARIANT_X(1, 4, 8, 8, CCH, NT, true), MBD_VARIANT_X(1, 2, 8, 8, CCH, NT, true),
     MBD_VARIANT_X(1, 4, 4, 4, CCH, NT, true), MBD_VARIANT_X(1, 2, 4, 4, CCH, NT, true),
     MBD_VARIANT_X(2, 4, 8, 4, CCH, NT, true), MBD_VARIANT_X(1, 4, 4, 1, CCH, NT, true),
-    // 48..51: rows not 16-byte aligned: line-aligned B granules, a realigned in LDS
+    // 38..41: rows not 16-byte aligned: line-aligned B granules, a realigned in LDS
     MBD_REALIGN(4, 4, NT), MBD_REALIGN(2, 4, NT), MBD_REALIGN(4, 8, NT), MBD_REALIGN(8, 4, NT),
-    // 52: one row per lane, one element per step (the uncoalesced layout; study only)
+    // 42: one row per lane, one element per step (the uncoalesced layout; study only)
     {{kLanesPerWave, 1, 4, 1, mbd::A_CACHED, 0, 0, 1},
      {&mbd::gemv_rowlane_kernel<mbd::DT_F16, 4>, &mbd::gemv_rowlane_kernel<mbd::DT_BF16, 4>}},
-    // 53..57: more realigning shapes (two rows per trip in 54..56)
+    // 43..47: more realigning shapes (two rows per trip in 44..46)
     MBD_REALIGN(8, 8, NT), MBD_REALIGN_R(2, 4, 4, NT), MBD_REALIGN_R(2, 4, 8, NT),
     MBD_REALIGN_R(2, 2, 8, NT),
     MBD_REALIGN(2, 8, NT),
-    // 58..62: B prefetched P items ahead through register slots (P = 1: none)
+    // 48..52: B prefetched P items ahead through register slots (P = 1: none)
     MBD_STAGED(2, 2, 8, 1, false), MBD_STAGED(2, 2, 8, 2, false), MBD_STAGED(2, 2, 8, 3, false),
     MBD_STAGED(2, 4, 8, 2, false), MBD_STAGED(1, 4, 8, 2, false),
-    // 63..66: the same through LDS slots filled by buffer loads into LDS
+    // 53..56: the same through LDS slots filled by buffer loads into LDS
     MBD_STAGED(2, 2, 8, 1, true), MBD_STAGED(2, 2, 8, 2, true), MBD_STAGED(2, 2, 8, 3, true),
     MBD_STAGED(1, 4, 4, 2, true),
-    // 67..68: realigning, 16 waves per workgroup (half the staging of a per wave)
+    // 57..58: realigning, 16 waves per workgroup (half the staging of a per wave)
     MBD_REALIGN(4, 16, NT), MBD_REALIGN(2, 16, NT),
-    // 69: two rows, four slices, one row group per (4-wave) workgroup
+    // 59: two rows, four slices, one row group per (4-wave) workgroup
     MBD_VARIANT(2, 4, 4, 4, CCH, NT),
+    // 60..66: rows not 16-byte aligned: line-aligned B granules, a read
+    // through the caches at each row's shift (no staging); two-row shapes
+    // take rows 64 apart, which share the shift
+    MBD_SHIFT(1, 2, 4, 1), MBD_SHIFT(2, 4, 4, 1), MBD_SHIFT(1, 4, 4, 4), MBD_SHIFT(2, 4, 4, 4),
+    MBD_SHIFT(2, 4, 8, 8), MBD_SHIFT(1, 4, 8, 8), MBD_SHIFT(2, 4, 2, 2),
 };
 #undef NT
 #undef LDS
@@ -119,13 +122,22 @@ size_t lds_bytes(const gemv_variant_info_t& v, int64_t k) {
   if (v.stages > 0)   // pipelined B: LDS slots of every wave, or none
     return v.b_lds ? (size_t)v.waves * v.stages * v.unroll * v.rows * mbd::kStepBytes : 0;
   size_t b = 0;
-  if (v.a_mode == mbd::A_LDS) b += (size_t)nsteps * mbd::kStepBytes;
+  if (v.a_mode == mbd::A_LDS) b += (size_t)nsteps * mbd::kStepBytes;   // (A_SHIFTED: no copy of a)
   if (v.splits > 1) b += (size_t)v.waves * v.rows * sizeof(float);
   return b;
 }
 
 // Rows a workgroup covers per trip (layout 1: rows == 64, one per lane).
 int64_t rows_per_block(const gemv_variant_info_t& v) { return (int64_t)(v.waves / v.splits) * v.rows; }
+
+// The items dealt out to the row units: rows, or for the shifted-window
+// kernel's two-row variants pair slots (slot p: rows 128 (p / 64) + p % 64
+// and 64 rows later), 64 per 128 rows or part of them.
+bool pairs_rows(const gemv_variant_info_t& v) { return v.a_mode == mbd::A_SHIFTED && v.rows == 2; }
+int64_t row_items(const gemv_variant_info_t& v, int64_t n) { return pairs_rows(v) ? 64 * ((n + 127) / 128) : n; }
+int64_t items_per_block(const gemv_variant_info_t& v) {
+  return pairs_rows(v) ? (int64_t)(v.waves / v.splits) : rows_per_block(v);
+}
 
 // Caller scratch of the cross-workgroup split (gemv_run_ws): first the
 // arrival counters, one bank of kXwgRanges per k-group count Q = 1..kXwgMaxQ
@@ -154,9 +166,6 @@ struct TunedShape {
 };
 const TunedShape kTuned[] = {
     {4096, 14336, {1, 4, 4, 1, mbd::A_CACHED, kPolNT, 512, 1}},
-    // misaligned rows (k odd): the realigning kernel in 8-wave workgroups on
-    // 1536 workgroups, 2-4% ahead of the rule's 16-wave plan on three boxes
-    {18433, 7169, {1, 4, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1536, 1}},
 };
 
 int find_variant(const Plan& p) {
@@ -172,6 +181,25 @@ int find_variant(const Plan& p) {
 }
 
 // The general rule, for shapes without a measured entry, in this order:
+//  0. rows that do not start on 16-byte boundaries, at least 768 of them:
+//     the shifted-window kernel (B in line-aligned granules, a read at each
+//     row's shift through the caches; two-row shapes pair rows 64 apart) in
+//     the shape its row length calls for, by the rows' granule steps
+//     nst = ceil((k + 63) / 512): rows of 10..17 steps two rows x four
+//     k-slices (one row, four slices below 1024 rows); of 18..40 steps by
+//     row count -- one row x eight slices below 1024 rows, two rows x eight
+//     slices below 2048, one row per wave (two load slots) below 4096, two
+//     rows x two slices below 8192 (on at most 2048 workgroups), two rows x
+//     four slices above; of more than 40 steps two rows x eight slices (one
+//     row below 1024 rows); of 4..9 steps, for 2048..8191 rows, two rows x
+//     two slices on at most 2048 workgroups; of at most 3 steps, from 12288
+//     rows, two rows per four-wave workgroup without a split.  Other short
+//     rows keep the tiers below.  (A tuner sweep under graph replay over 62
+//     misaligned shapes, n = 768..49152, k = 1025..32769, every compiled
+//     variant of the candidate kernels on full and persistent grids: 1.7%
+//     off the best compiled plan on average, 10% at worst, where the tiers
+//     below alone were 5.9% and 54% off; (18433, 7169) bf16 40.9 us against
+//     42.5 for their best, the realigning kernel on 1536 workgroups.)
 //  1. rows that do not start on 16-byte boundaries (k % 8 != 0, or B itself
 //     misaligned) and at least 3072 of them.  Up to k = 8192: for up to 8192
 //     rows (or rows of at most 3 steps) one row per wave, a staged in LDS
@@ -234,6 +262,27 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   const int64_t nfull0 = k / mbd::kStep;
   const bool misaligned = k > 0 && (k % 8 != 0 || !b_aligned);
   constexpr int64_t kShortMisaligned = 8192;   // the k range of the measured tiers of 1
+  // 0.
+  if (misaligned && n >= 768) {
+    const int64_t nst = (k + mbd::kLine - 1 + mbd::kStep - 1) / mbd::kStep;
+    auto shift = [](int R, int U, int W, int S, int grid) {
+      return Plan{R, U, W, S, mbd::A_SHIFTED, kPolNT, grid, 1};
+    };
+    if (nst > 40) return n < 1024 ? shift(1, 4, 8, 8, 0) : shift(2, 4, 8, 8, 0);
+    if (nst > 17) {
+      if (n < 1024) return shift(1, 4, 8, 8, 0);
+      if (n < 2048) return shift(2, 4, 8, 8, 0);
+      if (n < 4096) return shift(1, 2, 4, 1, 0);
+      if (n < 8192) return shift(2, 4, 2, 2, 2048);
+      return shift(2, 4, 4, 4, 0);
+    }
+    if (nst > 9) return n < 1024 ? shift(1, 4, 4, 4, 0) : shift(2, 4, 4, 4, 0);
+    if (nst > 3) {
+      if (n >= 2048 && n < 8192) return shift(2, 4, 2, 2, 2048);
+    } else if (n >= 12288) {
+      return shift(2, 4, 4, 1, 0);
+    }
+  }
   // 1.
   if (misaligned && k <= kShortMisaligned && n >= 3072) {
     const Plan pl = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 1536, 1};
@@ -422,8 +471,8 @@ static gemv_status_t shape_launch(int v, int64_t g, int64_t q, int flags, int64_
   const gemv_variant_info_t& info = kVariants[v].info;
   // the pipelined variants load whole 16-byte granules of aligned rows only
   if (info.stages > 0 && k > 0 && (k % 8 != 0 || !b_aligned)) return GEMV_ERR_UNSUPPORTED;
-  const int64_t rb = rows_per_block(info);
-  const int64_t nrb = (n + rb - 1) / rb;       // one row range per wave (or workgroup)
+  const int64_t rb = items_per_block(info);
+  const int64_t nrb = (row_items(info, n) + rb - 1) / rb;   // one row range per wave (or workgroup)
   if (g <= 0 || g > nrb) g = nrb;
   // the kernels walk their row ranges, so a smaller grid is always valid;
   // keep the launch's work-items along x (workgroups x threads, a 32-bit
@@ -659,9 +708,14 @@ extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void*
     units = (int64_t)L.grid * vi.waves;                                         // a wave per unit
   else if (vi.splits == 1 && !vi.cross_wg) units = (int64_t)L.grid * (vi.waves / vi.splits);
   else units = L.grid;                                                          // a workgroup per unit
-  p.rows_q = (int)(n / units);
-  p.rows_r = (int)(n % units);
-  const int64_t nfull = k / mbd::kStep;
+  const int64_t items = row_items(vi, n);
+  p.rows_q = (int)(items / units);
+  p.rows_r = (int)(items % units);
+  // the k-steps shared out: whole 512-element steps (the partial one goes to
+  // the last slice), or for the shifted-window kernel every granule step of
+  // the longest row, ceil((k + 63) / 512)
+  const int64_t nfull = vi.a_mode == mbd::A_SHIFTED ? (k + mbd::kLine - 1 + mbd::kStep - 1) / mbd::kStep
+                                                    : k / mbd::kStep;
   const int64_t nsl = (int64_t)vi.splits * L.kgroups;
   p.slice_q = (int)(nfull / nsl);
   p.slice_r = (int)(nfull % nsl);

@@ -49,7 +49,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
-enum { A_LDS = 0, A_CACHED = 1, A_LDS_SHIFTED = 2 };
+enum { A_LDS = 0, A_CACHED = 1, A_LDS_SHIFTED = 2, A_SHIFTED = 3 };
 
 constexpr int kLanes = 64;
 constexpr int kVec = 8;                 // 16-bit elements per 16-byte load
@@ -112,6 +112,21 @@ __device__ __forceinline__ void fma8(const u32x4& b, const u32x4& a, float& acc0
       acc0 = __builtin_fmaf(blo, alo, acc0);
       acc1 = __builtin_fmaf(bhi, ahi, acc1);
     }
+  }
+}
+
+// One 8-element step of a row: the FMAs above, or, in a PROBE build (a
+// measurement aid: the same kernel and launch with the arithmetic taken
+// out), an xor-fold of B's bits into the accumulator that keeps B's loads
+// alive -- a's loads, left unused, are then dropped by the compiler.
+template <int DT, bool PROBE>
+__device__ __forceinline__ void accumulate(const u32x4& b, const u32x4& a, float& acc0,
+                                           float& acc1) {
+  if constexpr (PROBE) {
+    const uint32_t x = b[0] ^ b[1] ^ b[2] ^ b[3];
+    acc0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, acc0) ^ x);
+  } else {
+    fma8<DT>(b, a, acc0, acc1);
   }
 }
 
@@ -212,7 +227,8 @@ __device__ __forceinline__ int share_start(int64_t u, int q, int r) {
   return (int)(u * q + (u < r ? u : (int64_t)r));
 }
 
-template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL, bool XWG>
+template <int DT, int R, int U, int WAVES, int S, int AMODE, int BPOL, bool XWG,
+          bool PROBE = false>
 __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     MBD_GEMV_PARAMS) {
   MBD_GEMV_ARGS;
@@ -328,7 +344,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-          for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
+          for (int r = 0; r < R; ++r) accumulate<DT, PROBE>(bv[u][r], av[u], acc[r][0], acc[r][1]);
         }
       }
       if (tail && (k & (kVec - 1)) != 0 && e0 < k && e0 + kVec > k) {
@@ -339,7 +355,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
           ap = load_vec_tail(arsrc, e0, k, 0u);
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r) fma8<DT>(load_vec_tail(brsrc, e0, k, soff[r]), ap, acc[r][0], acc[r][1]);
+        for (int r = 0; r < R; ++r) accumulate<DT, PROBE>(load_vec_tail(brsrc, e0, k, soff[r]), ap, acc[r][0], acc[r][1]);
       }
     } else {
       int t = t0;
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-          for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
+          for (int r = 0; r < R; ++r) accumulate<DT, PROBE>(bv[u][r], av[u], acc[r][0], acc[r][1]);
         }
       }
       // The last, partial group: the remaining full steps (fewer than U) and,
@@ -399,7 +415,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-          for (int r = 0; r < R; ++r) fma8<DT>(bv[u][r], av[u], acc[r][0], acc[r][1]);
+          for (int r = 0; r < R; ++r) accumulate<DT, PROBE>(bv[u][r], av[u], acc[r][0], acc[r][1]);
         }
         // the one vector that straddles k (rows not 16-byte aligned only)
         if (tail && (k & (kVec - 1)) != 0 && e0 < k && e0 + kVec > k) {
@@ -410,7 +426,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
             ap = load_vec_tail(arsrc, e0, k, 0u);
           }
 #pragma unroll
-          for (int r = 0; r < R; ++r) fma8<DT>(load_vec_tail(brsrc, e0, k, soff[r]), ap, acc[r][0], acc[r][1]);
+          for (int r = 0; r < R; ++r) accumulate<DT, PROBE>(load_vec_tail(brsrc, e0, k, soff[r]), ap, acc[r][0], acc[r][1]);
         }
       }
     }
@@ -471,6 +487,27 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     // then undefined).  The host gives every Q its own bank of counters, so
     // a counter only ever sees one Q.  (A __threadfence() here compiles to a
     // full L2 write-back and invalidate and made the split 10x slower.)
+    if constexpr (G == 1) {
+      // One row group: wave 0 made every store of the workgroup's partials,
+      // so it alone waits for them, counts the workgroup in and, if last,
+      // combines -- no workgroup barrier on this path (the other waves are
+      // done).
+      if (wave != 0) return;
+      __builtin_amdgcn_s_waitcnt(0);
+      unsigned old = 0;
+      if (lane == 0)
+        old = __builtin_amdgcn_atomic_inc32(&cnt[blockIdx.x], (unsigned)(Q - 1), __ATOMIC_RELAXED,
+                                            "agent");
+      if (__builtin_amdgcn_readfirstlane(old) != (unsigned)(Q - 1)) return;
+      for (int r = lo; r < hi; ++r) {
+        float s = 0.0f;
+        for (int qq = lane; qq < Q; qq += kLanes)
+          s += __hip_atomic_load(&ws[(int64_t)qq * n + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s = wave_sum(s);
+        if (lane == 0) c[r] = to_bits<DT>(finish<DT>(s, flags, alpha, bias, r));
+      }
+      return;
+    }
     __shared__ int last;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -588,7 +625,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_realign_kernel(
       const int row = row0 + r < hi ? row0 + r : row0;
       const uint16_t* rowp = B + (int64_t)row * k;
       o[r] = (int)(((uintptr_t)rowp >> 1) & (kLine - 1));  // wave-uniform
-      nv[r] = (o[r] + k + kVec - 1) / kVec;                // granules touching the row
+      nv[r] = k > 0 ? (o[r] + k + kVec - 1) / kVec : 0;    // granules touching the row
       basep[r] = rowp - o[r];                              // 128-byte aligned
       aw[r] = (o[r] & 1) ? a1w : a0w;
       // dword of the a copy lined up with element 0 of granule v: (8v - o + (o & 1) + kPadA) / 2

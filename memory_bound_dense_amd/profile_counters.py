@@ -37,7 +37,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 # the GEMV device code and the flags it is compiled with; which kernel a
 # workload runs (the plan) is recorded and checked separately
-KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemv_kernel.h", "gemv_staged.h")] + \
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemv_kernel.h", "gemv_shift.h",
+                                                          "gemv_staged.h")] + \
     [os.path.join(PKG, "build.py")]
 # the GLA step: its device code (which uses gemv_kernel.h's helpers), the host
 # code that picks its launch, and the build flags

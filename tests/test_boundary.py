@@ -53,12 +53,14 @@ def test_variant_table():
         assert s == mbd.GEMV_OK
         assert info.rows >= 1 and info.unroll >= 1 and info.waves >= 1
         assert info.splits >= 1 and info.waves % info.splits == 0
-        assert info.a_mode in (0, 1, 2)
+        assert info.a_mode in (0, 1, 2, 3)
         assert info.cross_wg in (0, 1)
         if info.cross_wg:
             assert info.a_mode == 1      # a k-chunk per workgroup reads a through the caches
         if info.a_mode == 2:
-            assert info.rows in (1, 2) and info.splits == 1 and not info.cross_wg
+            assert info.rows in (1, 2) and not info.cross_wg
+        if info.a_mode == 3:
+            assert info.rows in (1, 2) and not info.cross_wg and info.stages == 0
         assert info.layout in (0, 1)
         if info.layout == 1:
             assert info.rows == 64 and info.splits == 1 and not info.cross_wg

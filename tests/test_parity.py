@@ -524,7 +524,9 @@ def test_query_config_matches_the_host_plan(g):
                     assert (v, grid, q) == (cfg.variant, cfg.grid, cfg.kgroups), (n, k, dtype, ws)
 
 
-REALIGN = [v for v in VARIANTS if mbd.gemv_variant_info(v)[1].a_mode == 2]
+# the kernels for rows off 16-byte boundaries: a staged twice in LDS (a_mode 2)
+# or read at each row's shift through the caches (a_mode 3)
+REALIGN = [v for v in VARIANTS if mbd.gemv_variant_info(v)[1].a_mode in (2, 3)]
 
 
 @pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
@@ -557,27 +559,28 @@ def test_realigned_rows_do_not_leak(g, dtype):
 
 
 def test_auto_plan_realigns_misaligned_rows(g):
-    """Misaligned rows: from 3072 rows up to k = 8192, one row per wave with
-    a in LDS (up to 8192 rows, or rows of <= 3 steps), else the realigning
-    kernel with 8 waves per workgroup (16 for rows of more than 12 steps;
-    8 for the measured (18433, 7169)); longer rows the realigning kernel
-    with 16 waves while its LDS is <= 70 KiB, then unaligned loads (two rows
-    per one-wave workgroup); fewer rows the plan of aligned rows."""
-    for n, k, want in [(18433, 7169, (2, 8)), (3072, 7169, (0, 4)), (16384, 1025, (0, 4)),
-                       (8192, 7169, (0, 4)), (8193, 7169, (2, 16)), (8193, 6143, (2, 8)),
-                       (8192, 12289, (2, 16)), (8192, 16383, (1, 1)), (100, 1000, (1, None))]:
+    """Misaligned rows on the device handle: from 768 rows the shifted-window
+    kernel (a_mode 3) in the shape the rows' granule steps and count call
+    for; other short rows from 3072 rows one row per wave with a in LDS
+    (a_mode 0) or, from 8192 rows of 4..9 steps, the realigning kernel
+    (a_mode 2); fewer rows the plan of aligned rows."""
+    for n, k, want in [(18433, 7169, (3, 2, 4, 4)), (3072, 7169, (3, 2, 4, 4)),
+                       (1000, 16383, (3, 1, 8, 8)), (3072, 12289, (3, 1, 4, 1)),
+                       (4096, 12289, (3, 2, 2, 2)), (6144, 20993, (3, 2, 8, 8)), (6144, 4097, (3, 2, 2, 2)),
+                       (16384, 1025, (3, 2, 4, 1)), (8192, 1025, (0, 1, 4, 1)),
+                       (9000, 4097, (2, 1, 8, 1)), (768, 2049, (1, 1, 2, 1)),
+                       (100, 1000, (1, 1, 4, 1))]:
         v, grid, q = g.query_config(n, k, BF16)
         info = mbd.gemv_variant_info(v)[1]
-        assert info.a_mode == want[0], (n, k, v)
-        if want[1] is not None:
-            assert info.waves == want[1], (n, k, v)
-        if k == 16383:
-            assert info.rows == 2 and info.splits == 1, (n, k, v)
+        assert (info.a_mode, info.rows, info.waves, info.splits) == want, (n, k, v)
 
 
 LONG_MIS = [(4096, 12289, BF16, 3), (4096, 16001, F16, 1), (1000, 16383, BF16, 5),
             (6144, 4097, BF16, 2), (6400, 2049, F16, 7), (3072, 1025, F16, 0),
-            (8192, 4097, BF16, 3), (6144, 20003, BF16, 1)]
+            (8192, 4097, BF16, 3), (6144, 20003, BF16, 1), (16385, 1025, F16, 5),
+            (9000, 4097, BF16, 2), (8200, 2559, F16, 4), (1536, 9217, BF16, 6),
+            (800, 5121, F16, 1), (2000, 2049, BF16, 7), (3072, 12289, F16, 2),
+            (6144, 20993, BF16, 3)]
 
 
 @pytest.mark.parametrize("n,k,dtype,shift", LONG_MIS,

@@ -34,7 +34,8 @@ def shape_of(info):
 
 # (rows, unroll, waves, splits, a_mode, cross_wg) per configured workload;
 # a_mode 0 = a staged in LDS, 1 = a through the caches, 2 = the realigning
-# kernel's shifted LDS copies
+# kernel's shifted LDS copies, 3 = the shifted-window kernel (line-aligned
+# granules of B, a read through the caches at each row's shift)
 WORKLOAD_PLANS = {
     "tiny_256x512_f16": (1, 2, 4, 1, 1, 0),
     "gemv_18432x7168_f16": (2, 4, 4, 4, 1, 0),
@@ -51,7 +52,7 @@ WORKLOAD_PLANS = {
     "sweep_4096x14336_bf16": (1, 4, 4, 1, 1, 0),
     "ragged_64x65536_bf16": (1, 4, 8, 8, 1, 1),
     "ragged_1000x7000_bf16": (2, 4, 4, 4, 1, 0),
-    "ragged_18433x7169_bf16": (1, 4, 8, 1, 2, 0),
+    "ragged_18433x7169_bf16": (2, 4, 4, 4, 3, 0),
     "large_28672x8192_f16": (2, 4, 4, 4, 1, 0),
     "large_28672x8192_bf16": (2, 4, 4, 4, 1, 0),
     "large_57344x7168_f16": (2, 4, 4, 4, 1, 0),
@@ -75,81 +76,113 @@ def test_plan_grids_of_the_production_shapes():
     assert plan(7168, 16384, BF16)[0].grid == 3584
     # the measured entry for (4096, 14336): 512 workgroups, 2 rows per wave
     assert plan(4096, 14336, F16)[0].grid == 512
-    # the realigning kernel: persistent grids of 1024 (8192 waves of its
-    # 8-wave form for rows of 4..12 steps, 16384 of its 16-wave form for
-    # longer ones), and the measured 1536 workgroups of the 8-wave form for
-    # (18433, 7169)
-    assert plan(18433, 7169, BF16)[0].grid == 1536
+    # the shifted-window kernel pairs rows 64 apart: one pair per workgroup
+    # of 4 k-slices, 64 pairs per 128 rows (the last block of 128 partly
+    # empty), on the full grid
+    assert plan(18433, 7169, BF16)[0].grid == 9280
+    assert plan(18432, 7169, BF16)[0].grid == 9216
+    assert plan(12288, 7169, BF16)[0].grid == 6144
+    assert plan(3072, 7169, BF16)[0].grid == 1536
+    assert plan(7000, 7169, BF16)[0].grid == 3520
+    # rows of at most 3 steps from 12288 rows: 4 pairs per 4-wave workgroup
+    assert plan(16384, 1025, BF16)[0].grid == 2048
+    # 2048..8191 rows of 4..9 steps, or 4096..8191 rows of 18..40: two slices
+    # on a persistent grid of 2048
+    assert plan(4096, 2051, BF16)[0].grid == 2048
+    assert plan(7169, 14337, BF16)[0].grid == 2048
+    # the realigning kernel keeps its persistent 1024 for rows of 4..9 steps
+    # from 8192 rows; one row per wave with a in LDS keeps at most 2048
+    # workgroups (1536 for rows of at most 3 steps)
     assert plan(18433, 4097, BF16)[0].grid == 1024
-    assert plan(18432, 7169, BF16)[0].grid == 1024
-    assert plan(12288, 7169, BF16)[0].grid == 768
-    # one row per wave, a in LDS: at most 2048 workgroups (1536 for rows of
-    # at most 3 steps)
-    assert plan(3072, 7169, BF16)[0].grid == 768
     assert plan(8192, 4097, BF16)[0].grid == 2048
-    assert plan(7000, 7169, BF16)[0].grid == 1750
-    assert plan(16384, 1025, BF16)[0].grid == 1536
     assert plan(8192, 1025, BF16)[0].grid == 1536
     # 64 rows: k shared by 4 workgroups per row range
     assert plan(64, 65536, BF16)[0].kgroups == 4
 
 
+def _nst(k):
+    """Granule steps of a misaligned row: its k elements from a 16-byte
+    boundary up to 63 elements before its start, in steps of 512."""
+    return (k + 63 + 511) // 512
+
+
 @pytest.mark.parametrize("n,k,want", [
-    # >= 3072 rows of k <= 8192: up to 8192 rows, or rows of <= 3 steps, one
-    # row per wave with a in LDS and unaligned B loads
-    (3072, 7169, (1, 4, 4, 1, 0, 0)),
-    (6144, 4097, (1, 4, 4, 1, 0, 0)),
-    (6145, 1545, (1, 4, 4, 1, 0, 0)),
-    (8192, 8191, (1, 4, 4, 1, 0, 0)),
-    (16384, 1025, (1, 4, 4, 1, 0, 0)),
+    # from 768 misaligned rows: the shifted-window kernel, by granule steps
+    # nst = ceil((k + 63) / 512) and row count
+    # 10..17 steps: two rows x four slices (one row below 1024 rows)
+    (3072, 7169, (2, 4, 4, 4, 3, 0)),
+    (8192, 8191, (2, 4, 4, 4, 3, 0)),
+    (32768, 6143, (2, 4, 4, 4, 3, 0)),
+    (18432, 7169, (2, 4, 4, 4, 3, 0)),
+    (16384, 6147, (2, 4, 4, 4, 3, 0)),
+    (32768, 8121, (2, 4, 4, 4, 3, 0)),
+    (32768, 8185, (2, 4, 4, 4, 3, 0)),
+    (2048, 5121, (2, 4, 4, 4, 3, 0)),
+    (2560, 6143, (2, 4, 4, 4, 3, 0)),
+    (2048, 7169, (2, 4, 4, 4, 3, 0)),
+    (1000, 7169, (1, 4, 4, 4, 3, 0)),
+    # 18..40 steps: by row count
+    (1000, 16897, (1, 4, 8, 8, 3, 0)),
+    (800, 16385, (1, 4, 8, 8, 3, 0)),
+    (1024, 16897, (2, 4, 8, 8, 3, 0)),
+    (3072, 12289, (1, 2, 4, 1, 3, 0)),
+    (7169, 14337, (2, 4, 2, 2, 3, 0)),
+    (7169, 16383, (2, 4, 2, 2, 3, 0)),
+    (8192, 9217, (2, 4, 4, 4, 3, 0)),
+    (8192, 12289, (2, 4, 4, 4, 3, 0)),
+    (8192, 16383, (2, 4, 4, 4, 3, 0)),
+    # more than 40 steps: two rows x eight slices
+    (2048, 32769, (2, 4, 8, 8, 3, 0)),
+    (2048, 65537, (2, 4, 8, 8, 3, 0)),
+    (900, 65537, (1, 4, 8, 8, 3, 0)),
+    # 4..9 steps on 2048..8191 rows: two rows x two slices
+    (6144, 4097, (2, 4, 2, 2, 3, 0)),
+    (6145, 1545, (2, 4, 2, 2, 3, 0)),
+    (4096, 2051, (2, 4, 2, 2, 3, 0)),
+    (6144, 2053, (2, 4, 2, 2, 3, 0)),
+    (4095, 2049, (2, 4, 2, 2, 3, 0)),
+    (4096, 2561, (2, 4, 2, 2, 3, 0)),
+    (4096, 1545, (2, 4, 2, 2, 3, 0)),
+    # at most 3 steps from 12288 rows: two rows per four-wave workgroup
+    (16384, 1025, (2, 4, 4, 1, 3, 0)),
+    # other short rows keep the older tiers: from 3072 rows of at most 3
+    # steps (or up to 8192 rows) one row per wave with a in LDS ...
     (65536, 1535, (1, 4, 4, 1, 0, 0)),
-    # more rows of 4..12 steps, or from 4096 rows those of 4 full steps and a
-    # partial one: the realigning kernel, two steps per batch
+    (8192, 1025, (1, 4, 4, 1, 0, 0)),
+    # ... from 8192 rows of 4..9 steps the realigning kernel, two steps per
+    # batch ...
     (8193, 1545, (1, 2, 8, 1, 2, 0)),
-    (4096, 2051, (1, 2, 8, 1, 2, 0)),
-    (6144, 2053, (1, 2, 8, 1, 2, 0)),
     (8192, 2559, (1, 2, 8, 1, 2, 0)),
-    (4095, 2049, (1, 4, 4, 1, 0, 0)),
-    (4096, 2561, (1, 4, 4, 1, 0, 0)),
-    (4096, 1545, (1, 4, 4, 1, 0, 0)),
     (14336, 4097, (1, 2, 8, 1, 2, 0)),
-    (32768, 6143, (1, 2, 8, 1, 2, 0)),
-    # longer rows: its 16-wave form, one row per wave (the measured entry
-    # for (18433, 7169), the 8-wave form, is pinned with the workloads)
-    (18432, 7169, (1, 4, 16, 1, 2, 0)),
-    (16384, 6147, (1, 4, 16, 1, 2, 0)),
-    (32768, 8121, (1, 4, 16, 1, 2, 0)),
-    (32768, 8185, (1, 4, 16, 1, 2, 0)),
-    (32768, 6143, (1, 2, 8, 1, 2, 0)),
-    # k > 8192: the realigning kernel with 16 waves per workgroup (n >= 4096)
-    # while its LDS is <= 70 KiB
-    (8192, 9217, (1, 4, 16, 1, 2, 0)),
-    (8192, 12289, (1, 4, 16, 1, 2, 0)),
-    (7169, 14337, (1, 4, 16, 1, 2, 0)),
-    # beyond: unaligned loads, two rows per one-wave workgroup (n >= 2048)
-    (8192, 16383, (2, 4, 1, 1, 1, 0)),
-    (7169, 16383, (2, 4, 1, 1, 1, 0)),
-    (3072, 12289, (2, 4, 1, 1, 1, 0)),
-    (2048, 32769, (2, 4, 1, 1, 1, 0)),
-    (2048, 65537, (2, 4, 1, 1, 1, 0)),
-    # fewer rows: the split plan of aligned rows (two rows per wave from 896)
-    (1024, 16897, (2, 4, 8, 8, 1, 0)),
-    (1000, 16897, (2, 4, 8, 8, 1, 0)),
-    (800, 16385, (1, 4, 8, 8, 1, 0)),
-    # 768..3071 rows of at most 12 full steps: one row per two-wave workgroup
-    (2048, 5121, (1, 4, 2, 1, 1, 0)),
+    # ... 768..2047 rows of at most 12 full steps: one row per two-wave
+    # workgroup ...
     (768, 2049, (1, 4, 2, 1, 1, 0)),
-    (2560, 6143, (1, 4, 2, 1, 1, 0)),
-    # otherwise, below 3072 rows of k <= 8192, the plan of aligned rows
-    (2048, 7169, (2, 4, 4, 4, 1, 0)),
+    (1500, 4097, (1, 4, 2, 1, 1, 0)),
+    # ... and below 768 rows the plan of aligned rows
     (512, 5121, (1, 4, 4, 4, 1, 0)),
+    (700, 16385, (1, 4, 8, 8, 1, 0)),
 ])
 def test_plan_misaligned_tiers(n, k, want):
     for dtype in (F16, BF16):
         assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
     # a B pointer off 16-byte alignment makes every row misaligned, whatever k
     if k % 8 == 1:
+        assert _nst(k - 1) == _nst(k)
         assert shape_of(plan(n, k - 1, F16, aligned=False)[1]) == want, (n, k)
+
+
+def test_plan_shifted_window_only_for_misaligned_rows():
+    """The shifted-window kernel serves misaligned rows from 768 of them, and
+    aligned rows never."""
+    ns = [767, 768, 1023, 1024, 2047, 2048, 4095, 4096, 8191, 8192, 12287, 12288, 65536]
+    ks = [9, 511, 1025, 1535, 1537, 2049, 4097, 4607, 4609, 8705, 8767, 20415, 20481, 65537]
+    for n, k in itertools.product(ns, ks):
+        info = plan(n, k, BF16)[1]
+        assert (info.a_mode == 3) == (n >= 768 and (
+            _nst(k) > 9 or (_nst(k) > 3 and 2048 <= n < 8192) or (_nst(k) <= 3 and n >= 12288))), \
+            (n, k, shape_of(info))
+        ka = k - k % 8                  # aligned rows of about the same length
+        assert plan(n, ka, BF16)[1].a_mode != 3, (n, ka)
 
 
 @pytest.mark.parametrize("n,k,want", [
@@ -261,12 +294,16 @@ def test_plan_properties_over_a_sweep():
         assert cfg.grid >= 1 and cfg.kgroups >= 1
         assert info.layout == 0 and info.stages == 0, "an ablation variant was chosen"
         misaligned = k > 0 and (k % 8 != 0 or not aligned)
-        if info.a_mode == 2:
+        if info.a_mode in (2, 3):
             assert misaligned
         if info.cross_wg:
             assert n < 128
-        rows_per_block = info.rows * info.waves // info.splits
-        assert cfg.grid <= (n + rows_per_block - 1) // rows_per_block
+        if info.a_mode == 3 and info.rows == 2:
+            # pairs of rows 64 apart: 64 pairs per block of 128 rows
+            items, per_block = 64 * ((n + 127) // 128), info.waves // info.splits
+        else:
+            items, per_block = n, info.rows * info.waves // info.splits
+        assert cfg.grid <= (items + per_block - 1) // per_block
 
 
 @pytest.mark.parametrize("args,expect", [
