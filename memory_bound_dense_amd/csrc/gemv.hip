@@ -158,16 +158,6 @@ struct Plan {
   int kgroups;   // > 1: a cross-workgroup variant with this many k-groups
 };
 
-// Measured on MI355X for the listed workload shapes (several plans lie
-// within a few per cent of each other on these; the fastest median is kept).
-struct TunedShape {
-  int64_t n, k;
-  Plan plan;
-};
-const TunedShape kTuned[] = {
-    {4096, 14336, {1, 4, 4, 1, mbd::A_CACHED, kPolNT, 512, 1}},
-};
-
 int find_variant(const Plan& p) {
   const int x = p.kgroups > 1 ? 1 : 0;
   for (int v = 0; v < kNumVariants; ++v) {
@@ -180,7 +170,7 @@ int find_variant(const Plan& p) {
   return -1;
 }
 
-// The general rule, for shapes without a measured entry, in this order:
+// The automatic plan, O(1) per call, in this order:
 //  0. rows that do not start on 16-byte boundaries, at least 768 of them:
 //     the shifted-window kernel (B in line-aligned granules, a read at each
 //     row's shift through the caches; two-row shapes pair rows 64 apart) in
@@ -249,10 +239,13 @@ int find_variant(const Plan& p) {
 //     most 8 steps goes to one wave in one batch (two load slots for rows of
 //     1-2 steps); longer rows are split along k inside a workgroup until
 //     every wave has at most 4 steps (one batch of loads), further (down to
-//     two steps per slice) while the grid has fewer than 2048 waves.  Two
+//     two steps per slice) while the grid has fewer than 2048 waves.  The
 //     exceptions: rows of >= 96 steps with n >= 1536 are not split (two rows
-//     per one-wave workgroup), and up to 512 rows of 5..16 steps (768 rows of
-//     9..16) take four slices in four-wave workgroups.  (A tuner sweep under
+//     per one-wave workgroup), nor are rows of 18..28 whole steps (k a
+//     multiple of 512) on 1536..2560 rows (one row per wave) or fp16 ones of
+//     20..28 whole steps on 3072..6144 rows (two rows per one-wave
+//     workgroup); up to 512 rows of 5..16 steps (768 rows of 9..16) take
+//     four slices in four-wave workgroups.  (A tuner sweep under
 //     graph replay over n = 256..3072, k = 4096..65536, fp16 and bf16, 22
 //     candidate variants each, on MI355X: this rule is within 1.3% of the
 //     best compiled plan on average, 10% at worst; the previous one, fitted
@@ -327,6 +320,19 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // very long rows (k >= 48K) and enough of them: no split, two rows per
   // one-wave workgroup (the split's per-slice combine no longer pays)
   if (nfull >= 96 && n >= 1536) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
+  // rows of 18..28 whole steps (no partial step) on 1536..2560 rows: no
+  // split, one row per wave in two-wave workgroups; fp16 ones of 20..28 whole
+  // steps on 3072..6144 rows: no split, two rows per one-wave workgroup.
+  // (Graph replay over 170 aligned shapes, n = 1536..8192, k = 8704..16384
+  // with and without a partial step, fp16 and bf16: 0.9% off the best
+  // compiled plan on average, 7.7% at worst, where the split below alone was
+  // 1.7% and 11.8%.  With a partial step the unsplit plans lost up to 17%,
+  // at k = 11008 on every row count, so they take whole steps only.)
+  if (k % mbd::kStep == 0 && nfull >= 18 && nfull <= 28 && n >= 1536 && n <= 2560)
+    return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
+  if (dtype == GEMV_F16 && k % mbd::kStep == 0 && nfull >= 20 && nfull <= 28 && n >= 3072 &&
+      n <= 6144)
+    return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   const int R = (n >= 896 && k >= 6144) ? 2 : 1;
   // rows of one or two steps (k <= 1024): two load slots, not more slots
   // that would only be skipped (measured on MI355X under graph replay:
@@ -353,14 +359,6 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   if (dtype == GEMV_F16 && R == 2 && nfull == 32) return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
   const int W = R == 2 ? S : (S == 1 ? 4 : (S <= 8 ? 8 : 16));
   return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0, 1};
-}
-
-Plan auto_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned,
-               bool with_ws) {
-  if (b_aligned)
-    for (const TunedShape& t : kTuned)
-      if (t.n == n && t.k == k) return t.plan;
-  return rule_plan(n, k, dtype, max_lds, b_aligned, with_ws);
 }
 
 }  // namespace
@@ -513,7 +511,7 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_
     // the cross-workgroup split needs the caller's scratch
     if (kVariants[v].info.cross_wg && !with_ws) return GEMV_ERR_UNSUPPORTED;
   } else {
-    const Plan p = auto_plan(n, k, dtype, h->max_lds, b_aligned, with_ws);
+    const Plan p = rule_plan(n, k, dtype, h->max_lds, b_aligned, with_ws);
     v = find_variant(p);
     if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
     g = p.grid;
@@ -532,7 +530,7 @@ extern "C" gemv_status_t gemv_plan_config(int64_t n, int64_t k, gemv_dtype_t dty
   if (!out) return GEMV_ERR_INVALID_ARG;
   if (dtype != GEMV_F16 && dtype != GEMV_BF16) return GEMV_ERR_UNSUPPORTED_DTYPE;
   if (n <= 0 || k < 0 || n > GEMV_MAX_N || k > GEMV_MAX_K || max_lds <= 0) return GEMV_ERR_INVALID_ARG;
-  const Plan p = auto_plan(n, k, dtype, (size_t)max_lds, b_aligned != 0, with_workspace != 0);
+  const Plan p = rule_plan(n, k, dtype, (size_t)max_lds, b_aligned != 0, with_workspace != 0);
   const int v = find_variant(p);
   if (v < 0) return GEMV_ERR_UNSUPPORTED;
   Launch L;

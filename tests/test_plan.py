@@ -48,8 +48,8 @@ WORKLOAD_PLANS = {
     "sweep_4096x11008_bf16": (2, 4, 8, 8, 1, 0),
     "sweep_14336x4096_f16": (1, 8, 4, 1, 1, 0),
     "sweep_14336x4096_bf16": (1, 8, 4, 1, 1, 0),
-    "sweep_4096x14336_f16": (1, 4, 4, 1, 1, 0),
-    "sweep_4096x14336_bf16": (1, 4, 4, 1, 1, 0),
+    "sweep_4096x14336_f16": (2, 4, 1, 1, 1, 0),
+    "sweep_4096x14336_bf16": (2, 4, 8, 8, 1, 0),
     "ragged_64x65536_bf16": (1, 4, 8, 8, 1, 1),
     "ragged_1000x7000_bf16": (2, 4, 4, 4, 1, 0),
     "ragged_18433x7169_bf16": (2, 4, 4, 4, 3, 0),
@@ -74,8 +74,10 @@ def test_plan_grids_of_the_production_shapes():
     # workgroup for the headline, 2 rows (8 k-slices) for (7168, 16384)
     assert plan(18432, 7168, F16)[0].grid == 9216
     assert plan(7168, 16384, BF16)[0].grid == 3584
-    # the measured entry for (4096, 14336): 512 workgroups, 2 rows per wave
-    assert plan(4096, 14336, F16)[0].grid == 512
+    # (4096, 14336): fp16 two rows per one-wave workgroup, bf16 two rows x
+    # eight slices, both on their full grids
+    assert plan(4096, 14336, F16)[0].grid == 2048
+    assert plan(4096, 14336, BF16)[0].grid == 2048
     # the shifted-window kernel pairs rows 64 apart: one pair per workgroup
     # of 4 k-slices, 64 pairs per 128 rows (the last block of 128 partly
     # empty), on the full grid
@@ -223,6 +225,29 @@ def test_plan_bf16_short_rows(n, k, want):
     (7168, 18432, F16, (2, 4, 8, 8, 1, 0)),     # 36 steps: eight
 ])
 def test_plan_rows_of_32_steps(n, k, dtype, want):
+    assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
+
+
+@pytest.mark.parametrize("n,k,dtype,want", [
+    # 18..28 whole steps on 1536..2560 rows: one row per two-wave workgroup
+    (1536, 9216, F16, (1, 4, 2, 1, 1, 0)),
+    (2048, 14336, BF16, (1, 4, 2, 1, 1, 0)),
+    (2560, 10240, BF16, (1, 4, 2, 1, 1, 0)),
+    # fp16, 20..28 whole steps on 3072..6144 rows: two rows per one-wave
+    # workgroup; bf16 there keeps the split
+    (4096, 14336, F16, (2, 4, 1, 1, 1, 0)),
+    (6144, 10240, F16, (2, 4, 1, 1, 1, 0)),
+    (4096, 14336, BF16, (2, 4, 8, 8, 1, 0)),
+    # a partial last step, or outside those bounds: the split
+    (2048, 11008, BF16, (2, 4, 8, 8, 1, 0)),
+    (4096, 11008, F16, (2, 4, 8, 8, 1, 0)),
+    (2048, 15360, F16, (2, 4, 8, 8, 1, 0)),
+    (2048, 8704, BF16, (2, 4, 8, 8, 1, 0)),
+    (1024, 14336, BF16, (2, 4, 8, 8, 1, 0)),
+    (8192, 14336, F16, (2, 4, 8, 8, 1, 0)),
+    (3072, 9216, F16, (2, 4, 8, 8, 1, 0)),
+])
+def test_plan_whole_step_rows_unsplit(n, k, dtype, want):
     assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
 
 
