@@ -53,6 +53,12 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "achieved HBM GB/s (% of MI355X peak) and µs/call, n=18432 k=7168 fp16"
 
 
+def metric_of(n, k, dtype_name):
+    """The metric line of a GEMV workload (the default workload's is METRIC)."""
+    return "achieved HBM GB/s (%% of MI355X peak) and µs/call, n=%d k=%d %s" % (
+        n, k, {"f16": "fp16", "bf16": "bf16"}.get(dtype_name, dtype_name))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -513,7 +519,7 @@ def main():
     traffic = None if args.epilogue else read_traffic(name, step_bytes,
                                                       plan_signature(variant, grid, kgroups))
     out = {
-        "metric": METRIC,
+        "metric": metric_of(n, k, DTYPE_NAMES[dtype]),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

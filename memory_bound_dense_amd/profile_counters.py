@@ -17,13 +17,15 @@ Programs (run as the profiled program, after ``rocprofv3 ... --``):
 Summarisers (run anywhere, on the CSV files rocprofv3 wrote):
 
   ... summarize-trace --stats DIR/.._kernel_stats.csv --trace DIR/.._kernel_trace.csv
-                      --command "..." --out profiles/NAME.txt
-  ... summarize-counters --workload NAME --fetch CSV --write CSV --copy-fetch CSV
-                      --copy-write CSV --copy-bytes X --commands "..." --out profiles/...
+                      --command "..." [--kind gla] [--bench-json FILE] --out profiles/NAME.txt
+  ... summarize-counters --workload NAME --fetch CSV --write CSV --copy-fetch CSV [CSV ...]
+                      --copy-write CSV [CSV ...] --copy-bytes X [X ...] --commands "..."
+                      --out profiles/...
 
 FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  The copy kernel's reading
 fixes a scale factor per counter (known bytes / counted bytes) that is applied
-to the GEMV kernel's reading.
+to the GEMV kernel's reading; copies of several sizes give one factor each,
+and their mean is applied.
 """
 import argparse
 import csv
@@ -193,9 +195,36 @@ def counter_per_dispatch(path, kernel_substr, counter):
     return vals
 
 
-def summarize_trace(stats_csv, trace_csv, command, out, last=0):
+def _bench_line(path):
+    """The JSON line bench.py printed (the last line of `path` that parses)."""
+    import json
+    line = None
+    for raw in open(path):
+        raw = raw.strip()
+        if raw.startswith("{"):
+            try:
+                line = json.loads(raw)
+            except ValueError:
+                pass
+    if line is None:
+        raise ValueError("no JSON line in %s" % path)
+    return line
+
+
+def summarize_trace(stats_csv, trace_csv, command, out, last=0, kind="gemv", bench_json=""):
+    sources = GLA_SOURCES if kind == "gla" else None
     lines = ["# rocprofv3 kernel trace summary", "command: %s" % command,
-             "kernel_source_sha256_16: %s" % kernel_source_hash(), ""]
+             "kernel_source_sha256_16: %s" % kernel_source_hash(sources)]
+    if bench_json:
+        b = _bench_line(bench_json)
+        cfg = b.get("config", {})
+        lines.append("bench line of the same run: workload %s, kernel_us_avg %s us (HIP events "
+                     "over the timed region), value %s %s, launch %s%s" % (
+                         cfg.get("workload"), b.get("kernel_us_avg"), b.get("value"), b.get("unit"),
+                         cfg.get("launch"),
+                         "" if kind == "gla" else ", plan variant %s grid %s kgroups %s" % (
+                             cfg.get("variant"), cfg.get("grid"), cfg.get("kgroups"))))
+    lines.append("")
     stats = _rows(stats_csv)
     keys = list(stats[0].keys()) if stats else []
     lines.append("kernel_stats.csv (all kernels):")
@@ -255,9 +284,17 @@ def summarize_counters(workload, fetch, write, copy_fetch, copy_write, copy_byte
         plan = workload_plan_signature(n, k, dtype)
     f_g = statistics.median(counter_per_dispatch(fetch, kernel, "FETCH_SIZE")) * 1024
     w_g = statistics.median(counter_per_dispatch(write, kernel, "WRITE_SIZE")) * 1024
-    f_c = statistics.median(counter_per_dispatch(copy_fetch, COPY_KERNEL, "FETCH_SIZE")) * 1024
-    w_c = statistics.median(counter_per_dispatch(copy_write, COPY_KERNEL, "WRITE_SIZE")) * 1024
-    sf, sw = copy_bytes / f_c, copy_bytes / w_c
+    # one scale per counter from each copy calibration (copies of different
+    # sizes); the mean is applied, the spread says how far it can be trusted
+    if not (len(copy_fetch) == len(copy_write) == len(copy_bytes)):
+        raise ValueError("one fetch and one write CSV per copy size")
+    cal = []
+    for cf, cw, cb in zip(copy_fetch, copy_write, copy_bytes):
+        f_c = statistics.median(counter_per_dispatch(cf, COPY_KERNEL, "FETCH_SIZE")) * 1024
+        w_c = statistics.median(counter_per_dispatch(cw, COPY_KERNEL, "WRITE_SIZE")) * 1024
+        cal.append((cb, f_c, w_c, cb / f_c, cb / w_c))
+    sf = statistics.fmean(c[3] for c in cal)
+    sw = statistics.fmean(c[4] for c in cal)
     traffic = f_g * sf + w_g * sw
     lines = [
         "# HBM traffic of the %s kernel from rocprofv3 counters (median per dispatch)" % (
@@ -267,11 +304,12 @@ def summarize_counters(workload, fetch, write, copy_fetch, copy_write, copy_byte
     ] + ["  " + c for c in commands] + [
         "kernel_source_sha256_16: %s" % kernel_source_hash(sources),
         "plan: %s" % plan,
-        "copy_kernel_bytes: %d" % copy_bytes,
-        "copy_fetch_counted_bytes: %.0f" % f_c,
-        "copy_write_counted_bytes: %.0f" % w_c,
-        "fetch_scale: %.5f" % sf,
-        "write_scale: %.5f" % sw,
+    ] + ["copy_calibration: %d bytes read and written: fetch counted %.0f (scale %.5f), "
+         "write counted %.0f (scale %.5f)" % (cb, f_c, a, w_c, b) for cb, f_c, w_c, a, b in cal] + [
+        "fetch_scale: %.5f (spread %.5f over %d copy sizes)" % (
+            sf, max(c[3] for c in cal) - min(c[3] for c in cal), len(cal)),
+        "write_scale: %.5f (spread %.5f over %d copy sizes)" % (
+            sw, max(c[4] for c in cal) - min(c[4] for c in cal), len(cal)),
         "gemv_fetch_counted_bytes: %.0f" % f_g,
         "gemv_write_counted_bytes: %.0f" % w_g,
         "algorithmic_bytes_per_launch: %d" % alg,
@@ -306,13 +344,17 @@ def main():
     p.add_argument("--out", required=True)
     p.add_argument("--last", type=int, default=0,
                    help="also summarise each kernel's last N dispatches (the timed region)")
+    p.add_argument("--kind", choices=("gemv", "gla"), default="gemv",
+                   help="whose device code the summary's source hash covers")
+    p.add_argument("--bench-json", default="",
+                   help="bench.py's output of the profiled run: its line is quoted")
     p = sub.add_parser("summarize-counters")
     p.add_argument("--workload", required=True)
     p.add_argument("--fetch", required=True)
     p.add_argument("--write", required=True)
-    p.add_argument("--copy-fetch", required=True)
-    p.add_argument("--copy-write", required=True)
-    p.add_argument("--copy-bytes", type=int, required=True)
+    p.add_argument("--copy-fetch", nargs="+", required=True, help="one CSV per copy size")
+    p.add_argument("--copy-write", nargs="+", required=True, help="one CSV per copy size")
+    p.add_argument("--copy-bytes", type=int, nargs="+", required=True)
     p.add_argument("--commands", nargs="+", required=True)
     p.add_argument("--out", required=True)
     a = ap.parse_args()
@@ -323,7 +365,7 @@ def main():
     elif a.cmd == "copy":
         run_copy(a.bytes, a.launches)
     elif a.cmd == "summarize-trace":
-        summarize_trace(a.stats, a.trace, a.command, a.out, a.last)
+        summarize_trace(a.stats, a.trace, a.command, a.out, a.last, a.kind, a.bench_json)
     else:
         summarize_counters(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes,
                            a.commands, a.out)

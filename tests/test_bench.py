@@ -40,6 +40,7 @@ def test_json_line_graph_with_cpu_baseline():
     assert out["n_gpus"] == 1 and out["steps"] == 20 and out["warmup"] == 5
     assert out["unit"] == "GB/s" and out["value"] > 0 and out["dtype"] == "f16"
     assert out["config"]["workload"] == "tiny_256x512_f16" and out["config"]["launch"] == "graph"
+    assert out["metric"].endswith("n=256 k=512 fp16")
     rf = out["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert 0 < rf["frac"] < 1.2 and abs(rf["achieved"] / rf["peak"] - rf["frac"]) < 1e-3
@@ -61,6 +62,13 @@ def test_json_line_gla():
     out = _line(_bench("--op", "gla", "--steps", "20", "--warmup", "5", "--no-probe"))
     assert out["config"]["workload"] == "gla_decode_b1h32_128x128_bf16"
     assert out["config"]["launch"] == "graph" and out["roofline"]["frac"] > 0
+
+
+def test_metric_names_the_workload():
+    import bench
+    # the default workload's metric line is the headline's
+    assert bench.metric_of(18432, 7168, "f16") == bench.METRIC
+    assert bench.metric_of(7168, 16384, "bf16").endswith("n=7168 k=16384 bf16")
 
 
 def test_rotation_exceeds_the_infinity_cache():

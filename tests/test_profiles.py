@@ -5,7 +5,9 @@ arithmetic that turns rocprofv3 counter and trace CSVs into the figures the
 summaries give."""
 import csv
 import glob
+import json
 import os
+import re
 
 import pytest
 
@@ -23,6 +25,19 @@ def _kv(path):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
     return kv
+
+
+def _calibrations(path):
+    """(bytes, fetch counted, fetch scale, write counted, write scale) per
+    copy_calibration line of a counter summary."""
+    pat = re.compile(r"copy_calibration: (\d+) bytes read and written: fetch counted ([\d.]+) "
+                     r"\(scale ([\d.]+)\), write counted ([\d.]+) \(scale ([\d.]+)\)")
+    out = []
+    for line in open(path):
+        m = pat.match(line.strip())
+        if m:
+            out.append(tuple(float(x) for x in m.groups()))
+    return out
 
 
 def test_source_hash_ignores_comments_and_whitespace(tmp_path):
@@ -52,10 +67,15 @@ def test_counter_summaries_add_up(path):
         _, n, k, _, _ = find_workload(name)
         alg = algorithmic_bytes(n, k)
     assert int(kv["algorithmic_bytes_per_launch"]) == alg
-    cb = float(kv["copy_kernel_bytes"])
-    sf, sw = float(kv["fetch_scale"]), float(kv["write_scale"])
-    assert abs(sf - cb / float(kv["copy_fetch_counted_bytes"])) < 1e-4 * sf
-    assert abs(sw - cb / float(kv["copy_write_counted_bytes"])) < 1e-4 * sw
+    sf, sw = float(kv["fetch_scale"].split()[0]), float(kv["write_scale"].split()[0])
+    cal = _calibrations(path)
+    # at least two copy sizes; each line's scale is its bytes over its count,
+    # and the applied scale is their mean
+    assert len(cal) >= 2 and len({c[0] for c in cal}) == len(cal)
+    for cb, f_c, a, w_c, b in cal:
+        assert abs(a - cb / f_c) < 1e-4 * a and abs(b - cb / w_c) < 1e-4 * b
+    assert abs(sf - sum(c[2] for c in cal) / len(cal)) < 1e-4 * sf
+    assert abs(sw - sum(c[4] for c in cal) / len(cal)) < 1e-4 * sw
     traffic = float(kv["gemv_fetch_counted_bytes"]) * sf + float(kv["gemv_write_counted_bytes"]) * sw
     assert abs(traffic - float(kv["hbm_bytes_per_launch"])) <= 1e-4 * traffic
     assert abs(float(kv["traffic_over_algorithmic"]) - traffic / alg) < 1e-4
@@ -103,16 +123,27 @@ def test_counter_summary_arithmetic(tmp_path):
     _write_csv(f, hdr, [[1, gk, "FETCH_SIZE", 100], [2, other, "FETCH_SIZE", 9999],
                         [3, gk, "FETCH_SIZE", 130], [4, gk, "FETCH_SIZE", 101]])
     _write_csv(w, hdr, [[1, gk, "WRITE_SIZE", 1], [2, gk, "WRITE_SIZE", 1]])
-    copy_bytes = 1 << 20
     _write_csv(cf, hdr, [[1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 512]])    # half of 1 MiB
     _write_csv(cw, hdr, [[1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1024]])   # all of it
+    # a second copy of 4 MiB: fetch counts 2000 KiB (scale 2.048), write all
+    cf2, cw2 = tmp_path / "cf2.csv", tmp_path / "cw2.csv"
+    _write_csv(cf2, hdr, [[1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 2000]])
+    _write_csv(cw2, hdr, [[1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 4096]])
     out = tmp_path / "s.txt"
-    pc.summarize_counters(name, str(f), str(w), str(cf), str(cw), copy_bytes, ["cmd"], str(out))
+    pc.summarize_counters(name, str(f), str(w), [str(cf), str(cf2)], [str(cw), str(cw2)],
+                          [1 << 20, 4 << 20], ["cmd"], str(out))
     kv = _kv(out)
-    assert float(kv["fetch_scale"]) == pytest.approx(2.0)
-    assert float(kv["write_scale"]) == pytest.approx(1.0)
+    sf = (2.0 + 4096 / 2000) / 2
+    assert float(kv["fetch_scale"].split()[0]) == pytest.approx(sf, abs=1e-5)
+    assert "spread 0.04800 over 2 copy sizes" in kv["fetch_scale"]
+    assert float(kv["write_scale"].split()[0]) == pytest.approx(1.0)
+    assert len(_calibrations(out)) == 2
     assert float(kv["gemv_fetch_counted_bytes"]) == 101 * 1024
-    assert float(kv["hbm_bytes_per_launch"]) == pytest.approx(101 * 1024 * 2.0 + 1 * 1024)
+    assert float(kv["hbm_bytes_per_launch"]) == pytest.approx(101 * 1024 * sf + 1 * 1024, rel=1e-6)
+    # one write CSV short of the fetch CSVs: an error
+    with pytest.raises(ValueError):
+        pc.summarize_counters(name, str(f), str(w), [str(cf), str(cf2)], [str(cw)],
+                              [1 << 20, 4 << 20], ["cmd"], str(out))
     assert int(kv["algorithmic_bytes_per_launch"]) == algorithmic_bytes(n, k)
     assert kv["plan"] == pc.workload_plan_signature(n, k, dtype)
     assert kv["kernel_source_sha256_16"] == pc.kernel_source_hash()
@@ -141,3 +172,35 @@ def test_trace_summary_of_the_last_dispatches(tmp_path):
     # last 10: 1..10 us -> avg 5.5, median 5.5, p10 = t[0] = 1, p90 = t[8] = 9
     assert "k: avg 5.500 median 5.500 min 1.000 max 10.000 p10 1.000 p90 9.000" in text
     assert "contaminated" in text        # sd/median of 1..10 is far above 0.10
+
+
+def test_trace_summary_hash_and_bench_line(tmp_path):
+    """A GLA trace summary hashes the GLA step's sources, a GEMV one the
+    GEMV's; the bench line of the profiled run is quoted."""
+    stats = tmp_path / "stats.csv"
+    _write_csv(stats, ["Name", "Calls"], [["k", 1]])
+    bj = tmp_path / "bench.out"
+    line = {"value": 7000.0, "unit": "GB/s", "kernel_us_avg": 37.5,
+            "config": {"workload": "w", "launch": "graph", "variant": 3, "grid": 9, "kgroups": 1}}
+    bj.write_text("[bench] noise\n" + json.dumps(line) + "\n")
+    for kind, sources in (("gemv", None), ("gla", pc.GLA_SOURCES)):
+        out = tmp_path / ("%s.txt" % kind)
+        pc.summarize_trace(str(stats), "", "cmd", str(out), kind=kind, bench_json=str(bj))
+        kv = _kv(out)
+        assert kv["kernel_source_sha256_16"] == pc.kernel_source_hash(sources)
+        assert "kernel_us_avg 37.5 us" in out.read_text()
+    assert pc.kernel_source_hash(pc.GLA_SOURCES) != pc.kernel_source_hash()
+
+
+@pytest.mark.parametrize("path", sorted(glob.glob(os.path.join(ROOT, "profiles", "*.trace.txt"))),
+                         ids=lambda p: os.path.basename(p))
+def test_trace_summaries_name_their_code(path):
+    """Each committed trace summary gives its command and the hash of the
+    device code it ran (the GLA step's sources for a GLA summary)."""
+    kv = _kv(path)
+    assert kv["command"]
+    gla = os.path.basename(path).startswith("gla_")
+    want = pc.kernel_source_hash(pc.GLA_SOURCES if gla else None)
+    assert len(kv["kernel_source_sha256_16"]) == 16
+    if kv["kernel_source_sha256_16"] != want:
+        pytest.skip("summary taken on other device code: %s" % os.path.basename(path))
