@@ -107,12 +107,17 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
   if (active) {
     load_trip(rg, cur);
     if constexpr (!STAGE) load_scalars(rg, cg, ck, cq);
-    // v is read only when there is a state row to update: with dk == 0 the
-    // inputs other than o may be empty (null) buffers
-    if (dk > 0) {
+    // v through a descriptor over the head's dv values whose range is empty
+    // when dk == 0 (the inputs other than o may then be null buffers): a
+    // load that reads nothing there, rather than a branch around it -- a
+    // branch made the compiler widen v inside it, and so wait for every load
+    // issued before v (the first trip's state rows) before the loop
+    const __amdgpu_buffer_rsrc_t v_r =
+        make_rsrc(v + (dk > 0 ? head * dv : 0), dk > 0 ? (uint32_t)dv * 2u : 0u);
+    const auto vv = __builtin_amdgcn_raw_buffer_load_b64(v_r, (uint32_t)j0 * 2u, 0u, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) vj[c] = widen<DT>(v[head * dv + j0 + c]);
-    }
+    for (int c = 0; c < 4; ++c)
+      vj[c] = widen<DT>((uint16_t)(vv[c >> 1] >> (16 * (c & 1))));
   }
 
   extern __shared__ float gla_rows[];        // STAGE: e[0..dk), k[dk..2dk), q[2dk..3dk)
@@ -178,9 +183,8 @@ __global__ __launch_bounds__(kGlaThreads) void gla_decode_kernel(
                 nv, sout_r, ((uint32_t)i * (uint32_t)dv + (uint32_t)j0) * 4u, 0u, SPOL);
           }
         } else {
-          // every slot is updated (a row past dk holds the clamped row's
-          // scalars and a zero state) and kept by a select; only the store
-          // is conditional
+          // every slot is updated (a row past dk holds zero scalars and a
+          // zero state) and kept by a select; only the store is conditional
           const bool live = i < dk;
           u32x4 nv;
 #pragma unroll
