@@ -190,31 +190,23 @@ int find_variant(const Plan& p) {
 //     off the best compiled plan on average, 10% at worst, where the tiers
 //     below alone were 5.9% and 54% off; (18433, 7169) bf16 40.9 us against
 //     42.5 for their best, the realigning kernel on 1536 workgroups.)
-//  1. rows that do not start on 16-byte boundaries (k % 8 != 0, or B itself
-//     misaligned) and at least 3072 of them.  Up to k = 8192: for up to 8192
-//     rows (or rows of at most 3 steps) one row per wave, a staged in LDS
-//     and B read with unaligned 16-byte loads, on at most 2048 four-wave
-//     workgroups (one full occupancy; 1536 for rows of at most 3 steps, and
-//     for rows of 4..16 steps 6144 < n <= 8192 lost 2-8% on 1536 under
-//     graph replay); rows of 4 full steps and a partial one from 4096 rows
-//     (whose second batch in the one-row kernel would carry only the partial
-//     step), and any rows beyond those bounds, take the realigning kernel (aligned granules of B
-//     from each row's 128-byte line, a staged twice in LDS) in eight-wave
-//     workgroups: two steps per batch on a persistent grid of 1024 (8192
-//     waves: 32 per CU, one full occupancy); rows of more than 12 steps go
-//     to its 16-wave form (one row per wave) on 1024 workgroups (graph-
-//     replayed sweeps over n = 12288..65536, k = 6147..8001, 21 bf16 shapes:
-//     1.4% off the best compiled plan on average, 4.7% at worst; the 8-wave
-//     form on 1536 workgroups taken before: 3.7% and 8.9%; the 16-wave form
-//     on its full grid: 1.9% and 7.1%).
-//     (A tuner sweep over 70 misaligned bf16 shapes with n = 512..65536,
-//     k = 1025..8001 on MI355X: within 3.5% of the best compiled plan on
-//     average; the realigning kernel alone, with four steps per batch on a
-//     grid of 1536, 14.8%, up to 61% for few rows.)  Longer rows: the
-//     realigning kernel with 16 waves per
-//     workgroup (one row each, 2 workgroups per CU) for n >= 4096 while its
-//     LDS is <= 70 KiB (k ~ 15.8K; measured: ahead by 9% at k = 14337,
-//     behind by 7% at k = 16383);
+//  1. the misaligned rows tier 0 leaves, at least 3072 of them: short rows
+//     (4..9 granule steps from 8192 rows, at most 3 steps below 12288 rows).
+//     Up to 8192 rows, or rows of at most 3 steps: one row per wave, a
+//     staged in LDS and B read with unaligned 16-byte loads, on at most 2048
+//     four-wave workgroups (one full occupancy; 1536 for rows of at most 3
+//     steps); rows of 4 full steps and a partial one from 4096 rows (whose
+//     second batch in the one-row kernel would carry only the partial step),
+//     and more rows, the realigning kernel (aligned granules of B from each
+//     row's 128-byte line, a staged twice in LDS) in eight-wave workgroups,
+//     two steps per batch, on a persistent grid of 1024 (8192 waves: 32 per
+//     CU, one full occupancy).  (A tuner sweep over 70 misaligned bf16
+//     shapes with n = 512..65536, k = 1025..8001 on MI355X: within 3.5% of
+//     the best compiled plan on average, before tier 0 took most of them.)
+//     Misaligned rows that tier 0 leaves below 3072, from 768 rows of at
+//     most 12 full steps: one row per wave in two-wave workgroups with
+//     unaligned loads (measured under graph replay over n = 768..2560,
+//     k = 2049..6143 bf16: 2.6% off the best compiled plan on average).
 //  2. too few rows to give the GPU 2048 waves even with 16 waves per row
 //     (n < 128), with rows of at least 32 steps: one row per 8-wave
 //     workgroup, eight k-slices; for at most 64 rows of at least 128 steps
@@ -226,14 +218,8 @@ int find_variant(const Plan& p) {
 //     is within 1% of the best in-workgroup plan on every shape.  Below 8
 //     rows Q is doubled: for one row Q = 8 is within 4.5% of the best
 //     compiled plan, Q = 4 12% behind.)
-//  3. misaligned rows longer than k = 8192 and not taken by 1: unaligned
-//     16-byte loads, two rows per one-wave workgroup when n >= 2048,
-//     otherwise the plan of 4.  (Measured on MI355X over misaligned shapes
-//     with k from 4097 to 65537: the realigning kernel leads up to k ~ 14K
-//     and then falls behind, 13-40% at k >= 16K, as its LDS cuts the waves
-//     per CU.)  Misaligned rows up to k = 8192 and fewer than 3072 of them:
-//     from 768 rows with at most 12 full steps, one row per wave in two-wave
-//     workgroups; otherwise the plan of 4 as it stands, with unaligned loads.
+//  3. (misaligned rows below 768 of them take 4 as it stands, with
+//     unaligned 16-byte loads)
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
 //     wave (a read once for both) when n >= 896 and k >= 6144; a row of at
 //     most 8 steps goes to one wave in one batch (two load slots for rows of
@@ -281,24 +267,14 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     const Plan pl = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 1536, 1};
     const Plan pl2 = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 2048, 1};
     const Plan pr = {1, 2, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1024, 1};
-    const Plan p16 = {1, 4, 16, 1, mbd::A_LDS_SHIFTED, kPolNT, 1024, 1};
     const Plan& p = k <= 3 * mbd::kStep ? pl
                     : (k > 4 * mbd::kStep && k < 5 * mbd::kStep && n >= 4096) ? pr
-                    : n <= 8192 ? pl2
-                    : k > 12 * mbd::kStep ? p16 : pr;
+                    : n <= 8192 ? pl2 : pr;
     if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
   }
-  // fewer misaligned rows (768..3071) of at most 12 full steps: one row per
-  // wave in two-wave workgroups, unaligned loads (measured under graph
-  // replay over n = 768..2560, k = 2049..6143 bf16: 2.6% off the best
-  // compiled plan on average, 7.8% at worst, against 6.8% and 46% for (4))
+  // the misaligned rows tier 0 leaves below 3072 (see 1)
   if (misaligned && k <= kShortMisaligned && n >= 768 && n < 3072 && nfull0 <= 12)
     return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  if (misaligned && k > kShortMisaligned && n >= 4096) {
-    const Plan p16 = {1, 4, 16, 1, mbd::A_LDS_SHIFTED, kPolNT, 0, 1};
-    const size_t l = lds_bytes(kVariants[find_variant(p16)].info, k);
-    if (l <= (size_t)70 * 1024 && l <= max_lds) return p16;
-  }
   // 2. 8 waves per row per workgroup, Q groups sized so that every wave has
   // one batch of 4 steps (2 steps below 8 rows, to have more waves) -- only
   // with caller scratch for the partials and counters (gemv_run_ws); without
@@ -309,8 +285,6 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     if (Q * n <= (int64_t)kWsFloats) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
   if (n < 128 && nfull0 >= 32) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
-  // 3.
-  if (misaligned && k > kShortMisaligned && n >= 2048) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.
   const int64_t nfull = k / mbd::kStep;
   // rows of >= 128 steps (k >= 64K) on 1280..2048 rows: one row per wave in
