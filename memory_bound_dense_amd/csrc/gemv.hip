@@ -105,6 +105,9 @@ const Variant kVariants[] = {
     // take rows 64 apart, which share the shift
     MBD_SHIFT(1, 2, 4, 1), MBD_SHIFT(2, 4, 4, 1), MBD_SHIFT(1, 4, 4, 4), MBD_SHIFT(2, 4, 4, 4),
     MBD_SHIFT(2, 4, 8, 8), MBD_SHIFT(1, 4, 8, 8), MBD_SHIFT(2, 4, 2, 2),
+    // 67..69: two rows per wave whose k-slices fill their batch of loads:
+    // two steps per batch in eight slices, eight in four or eight slices
+    MBD_VARIANT(2, 2, 8, 8, CCH, NT), MBD_VARIANT(2, 8, 4, 4, CCH, NT), MBD_VARIANT(2, 8, 8, 8, CCH, NT),
 };
 #undef NT
 #undef LDS
@@ -227,11 +230,13 @@ int find_variant(const Plan& p) {
 //     every wave has at most 4 steps (one batch of loads), further (down to
 //     two steps per slice) while the grid has fewer than 2048 waves.  The
 //     exceptions: rows of >= 96 steps with n >= 1536 are not split (two rows
-//     per one-wave workgroup), nor are rows of 18..28 whole steps (k a
+//     per one-wave workgroup), nor are rows of 18..24 whole steps (k a
 //     multiple of 512) on 1536..2560 rows (one row per wave) or fp16 ones of
-//     20..28 whole steps on 3072..6144 rows (two rows per one-wave
+//     20..24 whole steps on 3072..6144 rows (two rows per one-wave
 //     workgroup); up to 512 rows of 5..16 steps (768 rows of 9..16) take
-//     four slices in four-wave workgroups.  (A tuner sweep under
+//     four slices in four-wave workgroups; and two-row plans of 15..80
+//     steps size their k-slices and batches so that each slice's share
+//     fills its batch of loads (see there).  (A tuner sweep under
 //     graph replay over n = 256..3072, k = 4096..65536, fp16 and bf16, 22
 //     candidate variants each, on MI355X: this rule is within 1.3% of the
 //     best compiled plan on average, 10% at worst; the previous one, fitted
@@ -294,17 +299,18 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // very long rows (k >= 48K) and enough of them: no split, two rows per
   // one-wave workgroup (the split's per-slice combine no longer pays)
   if (nfull >= 96 && n >= 1536) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  // rows of 18..28 whole steps (no partial step) on 1536..2560 rows: no
-  // split, one row per wave in two-wave workgroups; fp16 ones of 20..28 whole
+  // rows of 18..24 whole steps (no partial step) on 1536..2560 rows: no
+  // split, one row per wave in two-wave workgroups; fp16 ones of 20..24 whole
   // steps on 3072..6144 rows: no split, two rows per one-wave workgroup.
   // (Graph replay over 170 aligned shapes, n = 1536..8192, k = 8704..16384
-  // with and without a partial step, fp16 and bf16: 0.9% off the best
-  // compiled plan on average, 7.7% at worst, where the split below alone was
-  // 1.7% and 11.8%.  With a partial step the unsplit plans lost up to 17%,
-  // at k = 11008 on every row count, so they take whole steps only.)
-  if (k % mbd::kStep == 0 && nfull >= 18 && nfull <= 28 && n >= 1536 && n <= 2560)
+  // with and without a partial step, fp16 and bf16: with the split below
+  // alone 1.7% off the best compiled plan on average, 11.8% at worst.  With
+  // a partial step the unsplit plans lost up to 17%, at k = 11008 on every
+  // row count, so they take whole steps only.  From 25 steps the plan of
+  // eight-slot batches over four slices below is as good or better.)
+  if (k % mbd::kStep == 0 && nfull >= 18 && nfull <= 24 && n >= 1536 && n <= 2560)
     return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  if (dtype == GEMV_F16 && k % mbd::kStep == 0 && nfull >= 20 && nfull <= 28 && n >= 3072 &&
+  if (dtype == GEMV_F16 && k % mbd::kStep == 0 && nfull >= 20 && nfull <= 24 && n >= 3072 &&
       n <= 6144)
     return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   const int R = (n >= 896 && k >= 6144) ? 2 : 1;
@@ -331,6 +337,28 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // 28672, k = 16384: the best compiled plan or within 0.8%, where eight
   // slices were 0.8-7% behind; not so for bf16, nor for 36 steps)
   if (dtype == GEMV_F16 && R == 2 && nfull == 32) return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
+  // Two rows per wave, by the rows' steps (nsteps, the partial one
+  // included): give each k-slice a share that fills its batch of loads.
+  // A batch slot costs registers whether it is used or not (two rows x
+  // U = 2 / 4 / 8 take 55 / 73 / 121 VGPRs: 8 / 6 / 4 waves per SIMD), so a
+  // large batch pays only when the share fills it: eight slots for shares of
+  // 7-8 steps (25..28 steps over four slices, 49..64 over eight), four for
+  // shares of 3-4 (the rule above: 21..24 and 29..34 steps over eight), and
+  // two -- several batches, at full occupancy -- for the shares in between
+  // (15..20 steps, 35..48, 65..80; fp16 keeps four slices of four up to 16
+  // steps).  (Graph-replayed sweeps over 356 two-row shapes, n = 1024..18432,
+  // k = 6144..40960, fp16 and bf16, 16-20 candidate plans each: 1.1% off the
+  // best compiled plan on average, 3.2% at the 90th percentile, where the
+  // rule above alone was 2.9% and 7.7%, and up to 19% at 40 steps, whose
+  // shares of 5 left the second batch of four nearly empty.)
+  if (R == 2 && nsteps >= 15 && nsteps <= 80 && !(dtype == GEMV_F16 && nsteps <= 16)) {
+    auto two = [](int U, int Sl) { return Plan{2, U, Sl, Sl, mbd::A_CACHED, kPolNT, 0, 1}; };
+    if (nsteps <= 20) return two(2, 8);
+    if (nsteps >= 25 && nsteps <= 28) return two(8, 4);
+    if (nsteps >= 35 && nsteps <= 48) return two(2, 8);
+    if (nsteps >= 49 && nsteps <= 64) return two(8, 8);
+    if (nsteps >= 65) return two(2, 8);
+  }
   const int W = R == 2 ? S : (S == 1 ? 4 : (S <= 8 ? 8 : 16));
   return Plan{R, 4, W, S, mbd::A_CACHED, kPolNT, 0, 1};
 }

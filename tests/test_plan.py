@@ -48,13 +48,13 @@ WORKLOAD_PLANS = {
     "sweep_4096x11008_bf16": (2, 4, 8, 8, 1, 0),
     "sweep_14336x4096_f16": (1, 8, 4, 1, 1, 0),
     "sweep_14336x4096_bf16": (1, 8, 4, 1, 1, 0),
-    "sweep_4096x14336_f16": (2, 4, 1, 1, 1, 0),
-    "sweep_4096x14336_bf16": (2, 4, 8, 8, 1, 0),
+    "sweep_4096x14336_f16": (2, 8, 4, 4, 1, 0),
+    "sweep_4096x14336_bf16": (2, 8, 4, 4, 1, 0),
     "ragged_64x65536_bf16": (1, 4, 8, 8, 1, 1),
     "ragged_1000x7000_bf16": (2, 4, 4, 4, 1, 0),
     "ragged_18433x7169_bf16": (2, 4, 4, 4, 3, 0),
     "large_28672x8192_f16": (2, 4, 4, 4, 1, 0),
-    "large_28672x8192_bf16": (2, 4, 4, 4, 1, 0),
+    "large_28672x8192_bf16": (2, 2, 8, 8, 1, 0),
     "large_57344x7168_f16": (2, 4, 4, 4, 1, 0),
     "large_57344x7168_bf16": (2, 4, 4, 4, 1, 0),
     "square_1024x1024_f16": (1, 2, 4, 1, 1, 0),
@@ -74,8 +74,8 @@ def test_plan_grids_of_the_production_shapes():
     # workgroup for the headline, 2 rows (8 k-slices) for (7168, 16384)
     assert plan(18432, 7168, F16)[0].grid == 9216
     assert plan(7168, 16384, BF16)[0].grid == 3584
-    # (4096, 14336): fp16 two rows per one-wave workgroup, bf16 two rows x
-    # eight slices, both on their full grids
+    # (4096, 14336): two rows x four slices of eight-slot batches, one row
+    # group per workgroup
     assert plan(4096, 14336, F16)[0].grid == 2048
     assert plan(4096, 14336, BF16)[0].grid == 2048
     # the shifted-window kernel pairs rows 64 apart: one pair per workgroup
@@ -222,33 +222,64 @@ def test_plan_bf16_short_rows(n, k, want):
     (1024, 16384, F16, (2, 4, 8, 4, 1, 0)),
     (28672, 16384, F16, (2, 4, 8, 4, 1, 0)),
     (7168, 16384, BF16, (2, 4, 8, 8, 1, 0)),    # bf16: eight
-    (7168, 18432, F16, (2, 4, 8, 8, 1, 0)),     # 36 steps: eight
+    (7168, 18432, F16, (2, 2, 8, 8, 1, 0)),     # 36 steps: eight slices of two-slot batches
 ])
 def test_plan_rows_of_32_steps(n, k, dtype, want):
     assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
 
 
 @pytest.mark.parametrize("n,k,dtype,want", [
-    # 18..28 whole steps on 1536..2560 rows: one row per two-wave workgroup
+    # 18..24 whole steps on 1536..2560 rows: one row per two-wave workgroup
     (1536, 9216, F16, (1, 4, 2, 1, 1, 0)),
-    (2048, 14336, BF16, (1, 4, 2, 1, 1, 0)),
+    (2048, 12288, BF16, (1, 4, 2, 1, 1, 0)),
     (2560, 10240, BF16, (1, 4, 2, 1, 1, 0)),
-    # fp16, 20..28 whole steps on 3072..6144 rows: two rows per one-wave
+    # fp16, 20..24 whole steps on 3072..6144 rows: two rows per one-wave
     # workgroup; bf16 there keeps the split
-    (4096, 14336, F16, (2, 4, 1, 1, 1, 0)),
+    (4096, 12288, F16, (2, 4, 1, 1, 1, 0)),
     (6144, 10240, F16, (2, 4, 1, 1, 1, 0)),
-    (4096, 14336, BF16, (2, 4, 8, 8, 1, 0)),
-    # a partial last step, or outside those bounds: the split
+    (4096, 12288, BF16, (2, 4, 8, 8, 1, 0)),
+    # a partial last step, more steps, or outside those bounds: the split
     (2048, 11008, BF16, (2, 4, 8, 8, 1, 0)),
     (4096, 11008, F16, (2, 4, 8, 8, 1, 0)),
-    (2048, 15360, F16, (2, 4, 8, 8, 1, 0)),
-    (2048, 8704, BF16, (2, 4, 8, 8, 1, 0)),
-    (1024, 14336, BF16, (2, 4, 8, 8, 1, 0)),
-    (8192, 14336, F16, (2, 4, 8, 8, 1, 0)),
-    (3072, 9216, F16, (2, 4, 8, 8, 1, 0)),
+    (2048, 14336, BF16, (2, 8, 4, 4, 1, 0)),
+    (4096, 14336, F16, (2, 8, 4, 4, 1, 0)),
+    (1024, 12288, BF16, (2, 4, 8, 8, 1, 0)),
+    (8192, 12288, F16, (2, 4, 8, 8, 1, 0)),
+    (3072, 9216, F16, (2, 2, 8, 8, 1, 0)),
 ])
 def test_plan_whole_step_rows_unsplit(n, k, dtype, want):
     assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
+
+
+@pytest.mark.parametrize("k,dtype,want", [
+    # two rows per wave: each k-slice's share fills its batch of loads
+    (6656, BF16, (2, 4, 4, 4)),      # 13 steps: four slices of one batch of four
+    (7168, BF16, (2, 4, 4, 4)),      # 14
+    (7680, BF16, (2, 2, 8, 8)),      # 15..20: eight slices, two-slot batches
+    (7680, F16, (2, 4, 4, 4)),       # fp16 keeps four slices of four to 16 steps
+    (8192, F16, (2, 4, 4, 4)),
+    (8704, F16, (2, 2, 8, 8)),
+    (10240, BF16, (2, 2, 8, 8)),
+    (10248, BF16, (2, 4, 8, 8)),     # 21..24 (a partial 21st step counts): shares of 3
+    (12288, BF16, (2, 4, 8, 8)),
+    (12296, BF16, (2, 8, 4, 4)),     # 25..28: four slices of seven, eight-slot batches
+    (14336, F16, (2, 8, 4, 4)),
+    (14344, BF16, (2, 4, 8, 8)),     # 29..34: eight slices of four
+    (17408, BF16, (2, 4, 8, 8)),
+    (17416, BF16, (2, 2, 8, 8)),     # 35..48: eight slices, two-slot batches
+    (24576, F16, (2, 2, 8, 8)),
+    (24584, BF16, (2, 8, 8, 8)),     # 49..64: eight slices of seven or eight
+    (32768, BF16, (2, 8, 8, 8)),
+    (32776, F16, (2, 2, 8, 8)),      # 65..80
+    (40960, BF16, (2, 2, 8, 8)),
+    (40968, BF16, (2, 4, 8, 8)),     # beyond: the general split
+])
+def test_plan_batch_filling_bands(k, dtype, want):
+    assert k % 8 == 0                     # aligned rows (misaligned ones: tier 0)
+    for n in (896, 1000, 8192, 18432):
+        if n < 1024 and dtype == F16 and k <= 8192:
+            continue                          # there the general split goes deeper
+        assert shape_of(plan(n, k, dtype)[1]) == want + (1, 0), (n, k, dtype)
 
 
 @pytest.mark.parametrize("n,k,want", [
