@@ -108,6 +108,9 @@ const Variant kVariants[] = {
     // 67..69: two rows per wave whose k-slices fill their batch of loads:
     // two steps per batch in eight slices, eight in four or eight slices
     MBD_VARIANT(2, 2, 8, 8, CCH, NT), MBD_VARIANT(2, 8, 4, 4, CCH, NT), MBD_VARIANT(2, 8, 8, 8, CCH, NT),
+    // 70..71: the shifted-window kernel with two-slot batches (61 VGPRs, where
+    // its four-slot two-row forms take 88: 8 waves per SIMD instead of 5)
+    MBD_SHIFT(2, 2, 4, 4), MBD_SHIFT(2, 2, 8, 8),
 };
 #undef NT
 #undef LDS
@@ -176,25 +179,25 @@ int find_variant(const Plan& p) {
 // The automatic plan, O(1) per call, in this order:
 //  0. rows that do not start on 16-byte boundaries, at least 768 of them:
 //     the shifted-window kernel (B in line-aligned granules, a read at each
-//     row's shift through the caches; two-row shapes pair rows 64 apart) in
-//     the shape its row length calls for, by the rows' granule steps
-//     nst = ceil((k + 63) / 512): rows of 10..17 steps two rows x four
-//     k-slices (one row, four slices below 1024 rows); of 18..40 steps by
-//     row count -- one row x eight slices below 1024 rows, two rows x eight
-//     slices below 2048, one row per wave (two load slots) below 4096, two
-//     rows x two slices below 8192 (on at most 2048 workgroups), two rows x
-//     four slices above; of more than 40 steps two rows x eight slices (one
-//     row below 1024 rows); of 4..9 steps, for 2048..8191 rows, two rows x
-//     two slices on at most 2048 workgroups; of at most 3 steps, from 12288
-//     rows, two rows per four-wave workgroup without a split.  Other short
-//     rows keep the tiers below.  (A tuner sweep under graph replay over 62
-//     misaligned shapes, n = 768..49152, k = 1025..32769, every compiled
-//     variant of the candidate kernels on full and persistent grids: 1.7%
-//     off the best compiled plan on average, 10% at worst, where the tiers
-//     below alone were 5.9% and 54% off; (18433, 7169) bf16 40.9 us against
-//     42.5 for their best, the realigning kernel on 1536 workgroups.)
+//     row's shift through the caches; two-row shapes pair rows 64 apart),
+//     mostly in its two-slot forms (61 VGPRs: 8 waves per SIMD, where the
+//     four-slot two-row forms take 88: 5), by the rows' granule steps
+//     nst = ceil((k + 63) / 512) and row count.  From 6144 rows: two rows x
+//     four slices of two-slot batches up to 31 steps (four-slot batches at
+//     14..15 steps from 12288 rows), eight slices for 32..64 steps, eight
+//     slices of four-slot batches beyond; 1024..6143 rows: four slices up to
+//     9 steps, eight for 10..64 (and beyond 64 below 3072 rows; four-slot
+//     batches above); below 1024 rows: eight slices for 6..48 steps, one row
+//     x eight slices beyond.  Rows of at most 3 steps (4..5 from 12288 rows,
+//     at most 5 below 1024) keep the tiers below, except two rows per
+//     four-wave workgroup for at most 3 steps from 12288 rows.  (Graph-
+//     replayed sweeps over 78 misaligned shapes, n = 768..49152,
+//     k = 1025..32769, every candidate shape of the three misaligned kernels
+//     on full and persistent grids: 1.1% off the best compiled plan on
+//     average, 3.1% at the 90th percentile, where the previous tier 0, built
+//     on the four-slot forms, was 3.5% and 9.6%, up to 16%.)
 //  1. the misaligned rows tier 0 leaves, at least 3072 of them: short rows
-//     (4..9 granule steps from 8192 rows, at most 3 steps below 12288 rows).
+//     (at most 3 granule steps, 4..5 from 12288 rows).
 //     Up to 8192 rows, or rows of at most 3 steps: one row per wave, a
 //     staged in LDS and B read with unaligned 16-byte loads, on at most 2048
 //     four-wave workgroups (one full occupancy; 1536 for rows of at most 3
@@ -249,22 +252,23 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // 0.
   if (misaligned && n >= 768) {
     const int64_t nst = (k + mbd::kLine - 1 + mbd::kStep - 1) / mbd::kStep;
-    auto shift = [](int R, int U, int W, int S, int grid) {
-      return Plan{R, U, W, S, mbd::A_SHIFTED, kPolNT, grid, 1};
+    auto shift = [](int R, int U, int W, int S) {
+      return Plan{R, U, W, S, mbd::A_SHIFTED, kPolNT, 0, 1};
     };
-    if (nst > 40) return n < 1024 ? shift(1, 4, 8, 8, 0) : shift(2, 4, 8, 8, 0);
-    if (nst > 17) {
-      if (n < 1024) return shift(1, 4, 8, 8, 0);
-      if (n < 2048) return shift(2, 4, 8, 8, 0);
-      if (n < 4096) return shift(1, 2, 4, 1, 0);
-      if (n < 8192) return shift(2, 4, 2, 2, 2048);
-      return shift(2, 4, 4, 4, 0);
-    }
-    if (nst > 9) return n < 1024 ? shift(1, 4, 4, 4, 0) : shift(2, 4, 4, 4, 0);
-    if (nst > 3) {
-      if (n >= 2048 && n < 8192) return shift(2, 4, 2, 2, 2048);
-    } else if (n >= 12288) {
-      return shift(2, 4, 4, 1, 0);
+    if (n < 1024) {
+      if (nst >= 6 && nst <= 48) return shift(2, 2, 8, 8);
+      if (nst > 48) return shift(1, 4, 8, 8);
+    } else if (n < 6144) {
+      if (nst >= 4 && nst <= 9) return shift(2, 2, 4, 4);
+      if (nst >= 10 && nst <= 64) return shift(2, 2, 8, 8);
+      if (nst > 64) return n < 3072 ? shift(2, 2, 8, 8) : shift(2, 4, 8, 8);
+    } else if (nst >= 4 && !(nst <= 5 && n >= 12288)) {
+      if (nst <= 15 && nst >= 14 && n >= 12288) return shift(2, 4, 4, 4);
+      if (nst <= 31) return shift(2, 2, 4, 4);
+      if (nst <= 64) return shift(2, 2, 8, 8);
+      return shift(2, 4, 8, 8);
+    } else if (nst <= 3 && n >= 12288) {
+      return shift(2, 4, 4, 1);
     }
   }
   // 1.

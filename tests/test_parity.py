@@ -560,15 +560,16 @@ def test_realigned_rows_do_not_leak(g, dtype):
 
 def test_auto_plan_realigns_misaligned_rows(g):
     """Misaligned rows on the device handle: from 768 rows the shifted-window
-    kernel (a_mode 3) in the shape the rows' granule steps and count call
-    for; other short rows from 3072 rows one row per wave with a in LDS
-    (a_mode 0) or, from 8192 rows of 4..9 steps, the realigning kernel
-    (a_mode 2); fewer rows the plan of aligned rows."""
-    for n, k, want in [(18433, 7169, (3, 2, 4, 4)), (3072, 7169, (3, 2, 4, 4)),
-                       (1000, 16383, (3, 1, 8, 8)), (3072, 12289, (3, 1, 4, 1)),
-                       (4096, 12289, (3, 2, 2, 2)), (6144, 20993, (3, 2, 8, 8)), (6144, 4097, (3, 2, 2, 2)),
+    kernel (a_mode 3), mostly in its two-slot forms, by the rows' granule
+    steps and count; rows of at most 3 steps from 3072 rows one row per wave
+    with a in LDS (a_mode 0), 4..5 steps from 12288 rows the realigning
+    kernel (a_mode 2); fewer rows the plan of aligned rows."""
+    for n, k, want in [(18433, 7169, (3, 2, 4, 4)), (3072, 7169, (3, 2, 8, 8)),
+                       (1000, 16383, (3, 2, 8, 8)), (3072, 12289, (3, 2, 8, 8)),
+                       (4096, 12289, (3, 2, 8, 8)), (6144, 20993, (3, 2, 8, 8)),
+                       (6144, 4097, (3, 2, 4, 4)), (9000, 4097, (3, 2, 4, 4)),
                        (16384, 1025, (3, 2, 4, 1)), (8192, 1025, (0, 1, 4, 1)),
-                       (9000, 4097, (2, 1, 8, 1)), (768, 2049, (1, 1, 2, 1)),
+                       (12288, 2049, (2, 1, 8, 1)), (768, 2049, (1, 1, 2, 1)),
                        (100, 1000, (1, 1, 4, 1))]:
         v, grid, q = g.query_config(n, k, BF16)
         info = mbd.gemv_variant_info(v)[1]
@@ -580,7 +581,8 @@ LONG_MIS = [(4096, 12289, BF16, 3), (4096, 16001, F16, 1), (1000, 16383, BF16, 5
             (8192, 4097, BF16, 3), (6144, 20003, BF16, 1), (16385, 1025, F16, 5),
             (9000, 4097, BF16, 2), (8200, 2559, F16, 4), (1536, 9217, BF16, 6),
             (800, 5121, F16, 1), (2000, 2049, BF16, 7), (3072, 12289, F16, 2),
-            (6144, 20993, BF16, 3)]
+            (6144, 20993, BF16, 3), (12288, 2049, F16, 6), (8192, 24577, BF16, 5),
+            (900, 65537, F16, 4), (2048, 1025, BF16, 3), (4096, 32769, F16, 2)]
 
 
 @pytest.mark.parametrize("n,k,dtype,shift", LONG_MIS,

@@ -78,25 +78,22 @@ def test_plan_grids_of_the_production_shapes():
     # group per workgroup
     assert plan(4096, 14336, F16)[0].grid == 2048
     assert plan(4096, 14336, BF16)[0].grid == 2048
-    # the shifted-window kernel pairs rows 64 apart: one pair per workgroup
-    # of 4 k-slices, 64 pairs per 128 rows (the last block of 128 partly
-    # empty), on the full grid
+    # the shifted-window kernel pairs rows 64 apart: 64 pairs per 128 rows (the
+    # last block of 128 partly empty), one pair per workgroup of 4 or 8
+    # k-slices, on the full grid
     assert plan(18433, 7169, BF16)[0].grid == 9280
     assert plan(18432, 7169, BF16)[0].grid == 9216
     assert plan(12288, 7169, BF16)[0].grid == 6144
     assert plan(3072, 7169, BF16)[0].grid == 1536
     assert plan(7000, 7169, BF16)[0].grid == 3520
+    assert plan(7169, 14337, BF16)[0].grid == 3648
+    assert plan(18433, 4097, BF16)[0].grid == 9280
     # rows of at most 3 steps from 12288 rows: 4 pairs per 4-wave workgroup
     assert plan(16384, 1025, BF16)[0].grid == 2048
-    # 2048..8191 rows of 4..9 steps, or 4096..8191 rows of 18..40: two slices
-    # on a persistent grid of 2048
-    assert plan(4096, 2051, BF16)[0].grid == 2048
-    assert plan(7169, 14337, BF16)[0].grid == 2048
-    # the realigning kernel keeps its persistent 1024 for rows of 4..9 steps
-    # from 8192 rows; one row per wave with a in LDS keeps at most 2048
-    # workgroups (1536 for rows of at most 3 steps)
-    assert plan(18433, 4097, BF16)[0].grid == 1024
-    assert plan(8192, 4097, BF16)[0].grid == 2048
+    # the realigning kernel keeps its persistent 1024 for 4..5 steps from
+    # 12288 rows; one row per wave with a in LDS at most 1536 workgroups for
+    # rows of at most 3 steps
+    assert plan(12288, 2049, BF16)[0].grid == 1024
     assert plan(8192, 1025, BF16)[0].grid == 1536
     # 64 rows: k shared by 4 workgroups per row range
     assert plan(64, 65536, BF16)[0].kgroups == 4
@@ -109,57 +106,69 @@ def _nst(k):
 
 
 @pytest.mark.parametrize("n,k,want", [
-    # from 768 misaligned rows: the shifted-window kernel, by granule steps
-    # nst = ceil((k + 63) / 512) and row count
-    # 10..17 steps: two rows x four slices (one row below 1024 rows)
-    (3072, 7169, (2, 4, 4, 4, 3, 0)),
-    (8192, 8191, (2, 4, 4, 4, 3, 0)),
-    (32768, 6143, (2, 4, 4, 4, 3, 0)),
+    # from 768 misaligned rows: the shifted-window kernel (a_mode 3), by
+    # granule steps nst = ceil((k + 63) / 512) and row count
+    # from 6144 rows: two rows x four slices of two-slot batches up to 31 steps
+    (8192, 8191, (2, 2, 4, 4, 3, 0)),      # 17
+    (32768, 6143, (2, 2, 4, 4, 3, 0)),     # 13
+    (8192, 7169, (2, 2, 4, 4, 3, 0)),      # 15
+    (16384, 6147, (2, 2, 4, 4, 3, 0)),
+    (32768, 8121, (2, 2, 4, 4, 3, 0)),
+    (32768, 8185, (2, 2, 4, 4, 3, 0)),
+    (7169, 14337, (2, 2, 4, 4, 3, 0)),     # 29
+    (8192, 9217, (2, 2, 4, 4, 3, 0)),
+    (8192, 12289, (2, 2, 4, 4, 3, 0)),     # 25
+    (6144, 4097, (2, 2, 4, 4, 3, 0)),      # 9
+    (6145, 1545, (2, 2, 4, 4, 3, 0)),      # 4
+    (8193, 1545, (2, 2, 4, 4, 3, 0)),
+    (12288, 4097, (2, 2, 4, 4, 3, 0)),
+    (14336, 2559, (2, 2, 4, 4, 3, 0)),     # 6 from 12288 rows
+    # ... but four-slot batches at 14..15 steps from 12288 rows
     (18432, 7169, (2, 4, 4, 4, 3, 0)),
-    (16384, 6147, (2, 4, 4, 4, 3, 0)),
-    (32768, 8121, (2, 4, 4, 4, 3, 0)),
-    (32768, 8185, (2, 4, 4, 4, 3, 0)),
-    (2048, 5121, (2, 4, 4, 4, 3, 0)),
-    (2560, 6143, (2, 4, 4, 4, 3, 0)),
-    (2048, 7169, (2, 4, 4, 4, 3, 0)),
-    (1000, 7169, (1, 4, 4, 4, 3, 0)),
-    # 18..40 steps: by row count
-    (1000, 16897, (1, 4, 8, 8, 3, 0)),
-    (800, 16385, (1, 4, 8, 8, 3, 0)),
-    (1024, 16897, (2, 4, 8, 8, 3, 0)),
-    (3072, 12289, (1, 2, 4, 1, 3, 0)),
-    (7169, 14337, (2, 4, 2, 2, 3, 0)),
-    (7169, 16383, (2, 4, 2, 2, 3, 0)),
-    (8192, 9217, (2, 4, 4, 4, 3, 0)),
-    (8192, 12289, (2, 4, 4, 4, 3, 0)),
-    (8192, 16383, (2, 4, 4, 4, 3, 0)),
-    # more than 40 steps: two rows x eight slices
-    (2048, 32769, (2, 4, 8, 8, 3, 0)),
-    (2048, 65537, (2, 4, 8, 8, 3, 0)),
+    (12288, 7169, (2, 4, 4, 4, 3, 0)),
+    # 32..64 steps: eight slices of two-slot batches; beyond: four-slot
+    (7169, 16383, (2, 2, 8, 8, 3, 0)),     # 33
+    (8192, 16383, (2, 2, 8, 8, 3, 0)),
+    (8192, 20481, (2, 2, 8, 8, 3, 0)),     # 41
+    (8192, 24577, (2, 2, 8, 8, 3, 0)),     # 49
+    (8192, 32705, (2, 2, 8, 8, 3, 0)),     # 64
+    (8192, 32769, (2, 4, 8, 8, 3, 0)),     # 65
+    # 1024..6143 rows: four slices up to 9 steps, eight for 10..64 (and
+    # beyond below 3072 rows)
+    (4096, 2051, (2, 2, 4, 4, 3, 0)),      # 5
+    (4095, 2049, (2, 2, 4, 4, 3, 0)),
+    (4096, 2561, (2, 2, 4, 4, 3, 0)),
+    (4096, 1545, (2, 2, 4, 4, 3, 0)),
+    (1500, 4097, (2, 2, 4, 4, 3, 0)),      # 9
+    (3072, 7169, (2, 2, 8, 8, 3, 0)),      # 15
+    (2048, 5121, (2, 2, 8, 8, 3, 0)),      # 11
+    (2560, 6143, (2, 2, 8, 8, 3, 0)),
+    (2048, 7169, (2, 2, 8, 8, 3, 0)),
+    (1024, 16897, (2, 2, 8, 8, 3, 0)),     # 34
+    (3072, 12289, (2, 2, 8, 8, 3, 0)),
+    (2048, 32769, (2, 2, 8, 8, 3, 0)),     # 65 below 3072 rows
+    (2048, 65537, (2, 2, 8, 8, 3, 0)),
+    (4096, 24577, (2, 2, 8, 8, 3, 0)),     # 49
+    (4096, 32769, (2, 4, 8, 8, 3, 0)),     # 65 from 3072 rows
+    # below 1024 rows: eight slices for 6..48 steps, one row beyond
+    (1000, 7169, (2, 2, 8, 8, 3, 0)),
+    (768, 4097, (2, 2, 8, 8, 3, 0)),
+    (1000, 16897, (2, 2, 8, 8, 3, 0)),
+    (800, 16385, (2, 2, 8, 8, 3, 0)),
     (900, 65537, (1, 4, 8, 8, 3, 0)),
-    # 4..9 steps on 2048..8191 rows: two rows x two slices
-    (6144, 4097, (2, 4, 2, 2, 3, 0)),
-    (6145, 1545, (2, 4, 2, 2, 3, 0)),
-    (4096, 2051, (2, 4, 2, 2, 3, 0)),
-    (6144, 2053, (2, 4, 2, 2, 3, 0)),
-    (4095, 2049, (2, 4, 2, 2, 3, 0)),
-    (4096, 2561, (2, 4, 2, 2, 3, 0)),
-    (4096, 1545, (2, 4, 2, 2, 3, 0)),
     # at most 3 steps from 12288 rows: two rows per four-wave workgroup
     (16384, 1025, (2, 4, 4, 1, 3, 0)),
-    # other short rows keep the older tiers: from 3072 rows of at most 3
-    # steps (or up to 8192 rows) one row per wave with a in LDS ...
-    (65536, 1535, (1, 4, 4, 1, 0, 0)),
+    # the rest keep the older tiers: from 3072 rows one row per wave with a in
+    # LDS (at most 3 steps) ...
+    (65536, 1535, (1, 4, 4, 1, 0, 0)),     # 4 steps, but from 12288 rows
     (8192, 1025, (1, 4, 4, 1, 0, 0)),
-    # ... from 8192 rows of 4..9 steps the realigning kernel, two steps per
-    # batch ...
-    (8193, 1545, (1, 2, 8, 1, 2, 0)),
-    (8192, 2559, (1, 2, 8, 1, 2, 0)),
-    (14336, 4097, (1, 2, 8, 1, 2, 0)),
-    # ... 768..2047 rows of at most 12 full steps: one row per two-wave
-    # workgroup ...
+    (3072, 1025, (1, 4, 4, 1, 0, 0)),
+    # ... 4..5 steps from 12288 rows the realigning kernel ...
+    (12288, 2049, (1, 2, 8, 1, 2, 0)),
+    (16384, 2177, (1, 2, 8, 1, 2, 0)),
+    # ... below 3072 rows one row per two-wave workgroup ...
     (768, 2049, (1, 4, 2, 1, 1, 0)),
-    (1500, 4097, (1, 4, 2, 1, 1, 0)),
+    (2048, 1025, (1, 4, 2, 1, 1, 0)),
     # ... and below 768 rows the plan of aligned rows
     (512, 5121, (1, 4, 4, 4, 1, 0)),
     (700, 16385, (1, 4, 8, 8, 1, 0)),
@@ -173,16 +182,29 @@ def test_plan_misaligned_tiers(n, k, want):
         assert shape_of(plan(n, k - 1, F16, aligned=False)[1]) == want, (n, k)
 
 
+def _takes_shifted_window(n, nst):
+    """Whether tier 0 takes n misaligned rows of nst granule steps."""
+    if n < 768:
+        return False
+    if n < 1024:
+        return nst >= 6
+    if n < 6144:
+        return nst >= 4
+    if n >= 12288:
+        return nst <= 3 or nst >= 6
+    return nst >= 4
+
+
 def test_plan_shifted_window_only_for_misaligned_rows():
-    """The shifted-window kernel serves misaligned rows from 768 of them, and
-    aligned rows never."""
-    ns = [767, 768, 1023, 1024, 2047, 2048, 4095, 4096, 8191, 8192, 12287, 12288, 65536]
-    ks = [9, 511, 1025, 1535, 1537, 2049, 4097, 4607, 4609, 8705, 8767, 20415, 20481, 65537]
+    """The shifted-window kernel serves misaligned rows from 768 of them
+    (tier 0), and aligned rows never."""
+    ns = [767, 768, 1023, 1024, 2047, 2048, 4095, 4096, 6143, 6144, 8191, 8192, 12287, 12288,
+          65536]
+    ks = [9, 511, 1025, 1535, 1537, 2049, 2559, 2561, 4097, 4607, 4609, 8705, 8767, 20415,
+          20481, 65537]
     for n, k in itertools.product(ns, ks):
         info = plan(n, k, BF16)[1]
-        assert (info.a_mode == 3) == (n >= 768 and (
-            _nst(k) > 9 or (_nst(k) > 3 and 2048 <= n < 8192) or (_nst(k) <= 3 and n >= 12288))), \
-            (n, k, shape_of(info))
+        assert (info.a_mode == 3) == _takes_shifted_window(n, _nst(k)), (n, k, shape_of(info))
         ka = k - k % 8                  # aligned rows of about the same length
         assert plan(n, ka, BF16)[1].a_mode != 3, (n, ka)
 
