@@ -111,6 +111,9 @@ const Variant kVariants[] = {
     // 70..71: the shifted-window kernel with two-slot batches (61 VGPRs, where
     // its four-slot two-row forms take 88: 8 waves per SIMD instead of 5)
     MBD_SHIFT(2, 2, 4, 4), MBD_SHIFT(2, 2, 8, 8),
+    // 72..73: two-slot batches over four slices, one or two rows per wave
+    // (the plans of 513..895 rows of long rows)
+    MBD_VARIANT(1, 2, 4, 4, CCH, NT), MBD_VARIANT(2, 2, 4, 4, CCH, NT),
 };
 #undef NT
 #undef LDS
@@ -317,11 +320,23 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   if (dtype == GEMV_F16 && k % mbd::kStep == 0 && nfull >= 20 && nfull <= 24 && n >= 3072 &&
       n <= 6144)
     return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  const int R = (n >= 896 && k >= 6144) ? 2 : 1;
+  const int64_t nsteps = nfull + (k % mbd::kStep != 0 ? 1 : 0);
+  // fewer than 896 rows of at least 20 steps: what balances the workgroups
+  // over the CUs.  513..831 rows: one row per wave, four slices of two-slot
+  // batches (n workgroups, 2-3 per CU); 832..895 rows: the same with two
+  // rows per wave (n / 2 workgroups); 320..512 rows: two rows per wave in
+  // eight slices, the two-row plan below (at most 256 workgroups, one per
+  // CU; fewer than 320 rows would leave too many CUs idle).  (Graph-replayed
+  // sweeps over 184 shapes, n = 256..1088, k = 6144..49152, fp16 and bf16:
+  // 2.5% off the best compiled plan on average where one row per wave with
+  // the general split was 7.7%, up to 34%.)
+  if (n > 512 && n < 896 && nsteps >= 20)
+    return n < 832 ? Plan{1, 2, 4, 4, mbd::A_CACHED, kPolNT, 0, 1}
+                   : Plan{2, 2, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
+  const int R = ((n >= 896 && k >= 6144) || (n >= 320 && n <= 512 && nsteps >= 20)) ? 2 : 1;
   // rows of one or two steps (k <= 1024): two load slots, not more slots
   // that would only be skipped (measured on MI355X under graph replay:
   // (1024, 1024) 2.75 -> 2.45 us, (256, 512) 2.64 -> 2.35 us)
-  const int64_t nsteps = nfull + (k % mbd::kStep != 0 ? 1 : 0);
   if (R == 1 && nsteps <= 2) return Plan{1, 2, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // up to 512 rows of 5..16 steps, and up to 768 rows of 9..16: four slices
   // in four-wave workgroups
@@ -340,7 +355,8 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // batches, two row groups per 8-wave workgroup (graph replay, n = 1024 to
   // 28672, k = 16384: the best compiled plan or within 0.8%, where eight
   // slices were 0.8-7% behind; not so for bf16, nor for 36 steps)
-  if (dtype == GEMV_F16 && R == 2 && nfull == 32) return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
+  if (dtype == GEMV_F16 && R == 2 && nfull == 32 && n >= 896)
+    return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
   // Two rows per wave, by the rows' steps (nsteps, the partial one
   // included): give each k-slice a share that fills its batch of loads.
   // A batch slot costs registers whether it is used or not (two rows x

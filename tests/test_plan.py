@@ -171,7 +171,7 @@ def _nst(k):
     (2048, 1025, (1, 4, 2, 1, 1, 0)),
     # ... and below 768 rows the plan of aligned rows
     (512, 5121, (1, 4, 4, 4, 1, 0)),
-    (700, 16385, (1, 4, 8, 8, 1, 0)),
+    (700, 16385, (1, 2, 4, 4, 1, 0)),      # (the small-row plan of aligned rows)
 ])
 def test_plan_misaligned_tiers(n, k, want):
     for dtype in (F16, BF16):
@@ -302,6 +302,37 @@ def test_plan_batch_filling_bands(k, dtype, want):
         if n < 1024 and dtype == F16 and k <= 8192:
             continue                          # there the general split goes deeper
         assert shape_of(plan(n, k, dtype)[1]) == want + (1, 0), (n, k, dtype)
+
+
+@pytest.mark.parametrize("n,k,dtype,want", [
+    # fewer than 896 rows of at least 20 steps: balance the workgroups over
+    # the CUs.  320..512 rows: two rows per wave in eight slices, with the
+    # batch-filling bands of the two-row plans (at most 256 workgroups)
+    (320, 20480, BF16, (2, 2, 8, 8, 1, 0)),      # 40 steps: two-slot batches
+    (512, 12288, F16, (2, 4, 8, 8, 1, 0)),       # 24: four-slot
+    (448, 28672, BF16, (2, 8, 8, 8, 1, 0)),      # 56: eight-slot
+    (512, 14336, BF16, (2, 8, 4, 4, 1, 0)),      # 28: eight-slot, four slices
+    (384, 49152, F16, (2, 4, 8, 8, 1, 0)),       # 96: the general split
+    (512, 16384, F16, (2, 4, 8, 8, 1, 0)),       # fp16 32 steps: not the 8 x 4 plan here
+    # 513..831 rows: one row, four slices of two-slot batches
+    (576, 12288, BF16, (1, 2, 4, 4, 1, 0)),
+    (704, 40960, F16, (1, 2, 4, 4, 1, 0)),
+    (831, 10240, F16, (1, 2, 4, 4, 1, 0)),
+    # 832..895 rows: the same with two rows per wave
+    (832, 20480, BF16, (2, 2, 4, 4, 1, 0)),
+    (895, 12288, F16, (2, 2, 4, 4, 1, 0)),
+    # outside: 896 rows and more take the two-row bands, fewer than 320 rows
+    # or rows of fewer than 20 steps the one-row rule
+    (896, 20480, BF16, (2, 2, 8, 8, 1, 0)),
+    (256, 20480, BF16, (1, 4, 16, 16, 1, 0)),
+    (512, 8192, BF16, (1, 4, 4, 4, 1, 0)),
+    (700, 9216, F16, (1, 4, 8, 8, 1, 0)),
+])
+def test_plan_fewer_rows_balance(n, k, dtype, want):
+    assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
+    cfg = plan(n, k, dtype)[0]
+    rows_per_block = want[0] * want[2] // want[3]
+    assert cfg.grid == (n + rows_per_block - 1) // rows_per_block
 
 
 @pytest.mark.parametrize("n,k,want", [
