@@ -240,9 +240,12 @@ int find_variant(const Plan& p) {
 //     multiple of 512) on 1536..2560 rows (one row per wave) or fp16 ones of
 //     20..24 whole steps on 3072..6144 rows (two rows per one-wave
 //     workgroup); up to 512 rows of 5..16 steps (768 rows of 9..16) take
-//     four slices in four-wave workgroups; and two-row plans of 15..80
-//     steps size their k-slices and batches so that each slice's share
-//     fills its batch of loads (see there).  (A tuner sweep under
+//     four slices in four-wave workgroups; two-row plans of 15..80 steps
+//     size their k-slices and batches so that each slice's share fills its
+//     batch of loads; and fewer than 896 rows of at least 20 steps take the
+//     plan that balances their workgroups over the CUs -- two rows per wave
+//     for 320..512 rows, four slices of two-slot batches for 513..895 (see
+//     there).  (A tuner sweep under
 //     graph replay over n = 256..3072, k = 4096..65536, fp16 and bf16, 22
 //     candidate variants each, on MI355X: this rule is within 1.3% of the
 //     best compiled plan on average, 10% at worst; the previous one, fitted
