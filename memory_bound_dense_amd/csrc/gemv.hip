@@ -114,6 +114,9 @@ const Variant kVariants[] = {
     // 72..73: two-slot batches over four slices, one or two rows per wave
     // (the plans of 513..895 rows of long rows)
     MBD_VARIANT(1, 2, 4, 4, CCH, NT), MBD_VARIANT(2, 2, 4, 4, CCH, NT),
+    // 74..75: split across workgroups with 16 waves each (the plan of at
+    // most 64 rows of at least 128 steps)
+    MBD_VARIANT_X(1, 2, 16, 16, CCH, NT, true), MBD_VARIANT_X(1, 4, 16, 16, CCH, NT, true),
 };
 #undef NT
 #undef LDS
@@ -290,14 +293,31 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // the misaligned rows tier 0 leaves below 3072 (see 1)
   if (misaligned && k <= kShortMisaligned && n >= 768 && n < 3072 && nfull0 <= 12)
     return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  // 2. 8 waves per row per workgroup, Q groups sized so that every wave has
-  // one batch of 4 steps (2 steps below 8 rows, to have more waves) -- only
-  // with caller scratch for the partials and counters (gemv_run_ws); without
-  // it, the in-workgroup split below.
+  // 2. k split over Q workgroups as well, for at most 64 rows of at least
+  // 128 steps -- only with caller scratch for the partials and counters
+  // (gemv_run_ws); without it, the in-workgroup split below.  From 8 rows:
+  // 16 waves per row per workgroup, about one workgroup per CU
+  // (Q = 256 / n) while every wave keeps at least two steps (Q <= steps /
+  // 32), two load slots per wave, four when the share is four steps or more
+  // (graph replay over n = 1..64, k = 64K..256K, fp16 and bf16, every split
+  // plan x Q = 2..32: the best compiled plan or within 2% from 16 rows but
+  // for 16 and 24 rows at k = 256K, 4-16%; the 8-wave plan below 3-17%
+  // behind from 24 rows).  Below 8 rows: 8 waves, Q = steps / 16 (one row:
+  // 4-9% off the best, which wants four-wave workgroups of two steps).
   if (with_ws && n <= 64 && nfull0 >= 128) {
-    int64_t Q = nfull0 / (8 * (n < 8 ? 2 : 4));
+    int64_t Q;
+    int U = 4, W = 8;
+    if (n < 8) {
+      Q = nfull0 / 16;
+    } else {
+      Q = 256 / n;
+      if (Q > nfull0 / 32) Q = nfull0 / 32;
+      if (Q < 2) Q = 2;
+      W = 16;
+    }
     if (Q > kXwgMaxQ) Q = kXwgMaxQ;
-    if (Q * n <= (int64_t)kWsFloats) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
+    if (W == 16 && nfull0 / (Q * 16) < 4) U = 2;
+    if (Q * n <= (int64_t)kWsFloats) return Plan{1, U, W, W, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
   if (n < 128 && nfull0 >= 32) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.

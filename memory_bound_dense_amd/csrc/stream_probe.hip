@@ -105,7 +105,8 @@ const ProbeShape kProbeShapes[] = {
     MBD_PROBE(2, 4, 4, 4, 0), MBD_PROBE(2, 4, 8, 8, 0), MBD_PROBE(2, 4, 8, 4, 0),
     MBD_PROBE(1, 4, 4, 4, 0), MBD_PROBE(1, 4, 8, 8, 0), MBD_PROBE(2, 4, 1, 1, 0),
     MBD_PROBE(1, 4, 2, 1, 0), MBD_PROBE(1, 4, 8, 8, 1), MBD_PROBE(2, 2, 8, 8, 0),
-    MBD_PROBE(2, 8, 4, 4, 0), MBD_PROBE(2, 8, 8, 8, 0),
+    MBD_PROBE(2, 8, 4, 4, 0), MBD_PROBE(2, 8, 8, 8, 0), MBD_PROBE(1, 2, 4, 4, 0),
+    MBD_PROBE(2, 2, 4, 4, 0), MBD_PROBE(1, 2, 16, 16, 1), MBD_PROBE(1, 4, 16, 16, 1),
 };
 #undef MBD_PROBE
 
