@@ -114,8 +114,8 @@ const Variant kVariants[] = {
     // 72..73: two-slot batches over four slices, one or two rows per wave
     // (the plans of 513..895 rows of long rows)
     MBD_VARIANT(1, 2, 4, 4, CCH, NT), MBD_VARIANT(2, 2, 4, 4, CCH, NT),
-    // 74..75: split across workgroups with 16 waves each (the plan of at
-    // most 64 rows of at least 128 steps)
+    // 74..75: split across workgroups with 16 waves each (the plans of
+    // 8..256 rows of at least 128 steps)
     MBD_VARIANT_X(1, 2, 16, 16, CCH, NT, true), MBD_VARIANT_X(1, 4, 16, 16, CCH, NT, true),
 };
 #undef NT
@@ -221,15 +221,10 @@ int find_variant(const Plan& p) {
 //     k = 2049..6143 bf16: 2.6% off the best compiled plan on average).
 //  2. too few rows to give the GPU 2048 waves even with 16 waves per row
 //     (n < 128), with rows of at least 32 steps: one row per 8-wave
-//     workgroup, eight k-slices; for at most 64 rows of at least 128 steps
-//     k is split across Q workgroups as well, Q = steps / 32 (one batch of
-//     4 steps per wave).  (Measured under graph replay over n = 16..127,
-//     k = 16384..65536: the cross-workgroup split, with its combine's
-//     serial latency, wins only there -- by 3-17%, best at Q = 4 for
-//     k = 65536 -- and loses 21-52% elsewhere; the 8 x 8 in-workgroup split
-//     is within 1% of the best in-workgroup plan on every shape.  Below 8
-//     rows Q is doubled: for one row Q = 8 is within 4.5% of the best
-//     compiled plan, Q = 4 12% behind.)
+//     workgroup, eight k-slices.  With a workspace, 8..128 rows of at least
+//     128 steps (up to 256 rows of at least 512) split k across Q 16-wave
+//     workgroups as well, Q chosen by the rows on the busiest CU (below);
+//     fewer than 8 rows across 8-wave workgroups, Q = steps / 16.
 //  3. (misaligned rows below 768 of them take 4 as it stands, with
 //     unaligned 16-byte loads)
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
@@ -293,31 +288,36 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // the misaligned rows tier 0 leaves below 3072 (see 1)
   if (misaligned && k <= kShortMisaligned && n >= 768 && n < 3072 && nfull0 <= 12)
     return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  // 2. k split over Q workgroups as well, for at most 64 rows of at least
-  // 128 steps -- only with caller scratch for the partials and counters
-  // (gemv_run_ws); without it, the in-workgroup split below.  From 8 rows:
-  // 16 waves per row per workgroup, about one workgroup per CU
-  // (Q = 256 / n) while every wave keeps at least two steps (Q <= steps /
-  // 32), two load slots per wave, four when the share is four steps or more
-  // (graph replay over n = 1..64, k = 64K..256K, fp16 and bf16, every split
-  // plan x Q = 2..32: the best compiled plan or within 2% from 16 rows but
-  // for 16 and 24 rows at k = 256K, 4-16%; the 8-wave plan below 3-17%
-  // behind from 24 rows).  Below 8 rows: 8 waves, Q = steps / 16 (one row:
-  // 4-9% off the best, which wants four-wave workgroups of two steps).
-  if (with_ws && n <= 64 && nfull0 >= 128) {
-    int64_t Q;
-    int U = 4, W = 8;
-    if (n < 8) {
-      Q = nfull0 / 16;
-    } else {
-      Q = 256 / n;
-      if (Q > nfull0 / 32) Q = nfull0 / 32;
-      if (Q < 2) Q = 2;
-      W = 16;
-    }
+  // 2. k split over Q workgroups as well, for few rows of many steps -- only
+  // with caller scratch for the partials and counters (gemv_run_ws);
+  // without it, the in-workgroup split below.  From 8 rows: 16 waves per row
+  // per workgroup, one row per workgroup, at most two workgroups resident
+  // per CU.  Q (2..8, every wave at least two steps: Q <= steps / 32) makes
+  // the busiest CU's share of rows, ceil(n Q / 256) / Q, smallest; ties go
+  // to the Q nearest 4 (two resident workgroups where that fits), then the
+  // smaller.  Two load slots per wave, four when the share is four steps or
+  // more.  Taken for 8..128 rows of >= 128 steps and up to 256 rows of
+  // >= 512 steps (graph replay over n = 1..256, k = 32K..256K, every split
+  // plan x Q = 2..32: 2.0% off the best compiled plan on average over 88
+  // shapes, 12% at worst, where 65..128 rows in the in-workgroup split were
+  // up to 72% off).  Below 8 rows: 8 waves, Q = steps / 16 (one row: 4-9%
+  // off the best, which wants four-wave workgroups of two steps).
+  if (with_ws && nfull0 >= 128 && n < 8) {
+    int64_t Q = nfull0 / 16;
     if (Q > kXwgMaxQ) Q = kXwgMaxQ;
-    if (W == 16 && nfull0 / (Q * 16) < 4) U = 2;
-    if (Q * n <= (int64_t)kWsFloats) return Plan{1, U, W, W, mbd::A_CACHED, kPolNT, 0, (int)Q};
+    if (Q * n <= (int64_t)kWsFloats) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
+  }
+  if (with_ws && nfull0 >= 128 && n >= 8 && (n <= 128 || (n <= 256 && nfull0 >= 512))) {
+    int64_t Q = 0, best_c = 0;
+    for (int64_t t = 2; t <= 8 && t <= nfull0 / 32; ++t) {
+      const int64_t c = (n * t + 255) / 256;   // workgroups on the busiest CU
+      // c / t against best_c / Q; on a tie, nearer 4, then smaller
+      const int64_t lhs = c * Q, rhs = best_c * t;
+      const int64_t dt = t > 4 ? t - 4 : 4 - t, dq = Q > 4 ? Q - 4 : 4 - Q;
+      if (Q == 0 || lhs < rhs || (lhs == rhs && dt < dq)) { Q = t; best_c = c; }
+    }
+    const int U = nfull0 / (Q * 16) >= 4 ? 4 : 2;
+    if (Q * n <= (int64_t)kWsFloats) return Plan{1, U, 16, 16, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
   if (n < 128 && nfull0 >= 32) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.

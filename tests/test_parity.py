@@ -459,6 +459,33 @@ def test_cross_workgroup_split(g, n, k, dtype):
                     assert np.array_equal(goti, refi), (v, q, grid)
 
 
+AUTO_XWG_SHAPES = [(96, 131072, BF16), (100, 65544, F16), (129, 262152, BF16), (200, 262144, F16),
+                   (16, 262144, BF16), (48, 131075, F16)]
+
+
+@pytest.mark.parametrize("n,k,dtype", AUTO_XWG_SHAPES,
+                         ids=["%dx%d_%s" % (n, k, "f16" if d == F16 else "bf16")
+                              for n, k, d in AUTO_XWG_SHAPES])
+def test_auto_plan_cross_workgroup_rows(g, n, k, dtype):
+    """The automatic plan's cross-workgroup split over its whole range (8 to
+    256 rows, Q = 2..8 k-groups of 16-wave workgroups, rows with and without
+    a partial step): every row against the oracle, three calls back to back
+    (the counters return to zero between calls), and integer inputs
+    bit-exact."""
+    v, grid, q = g.query_config(n, k, dtype)
+    assert mbd.gemv_variant_info(v)[1].cross_wg and 2 <= q <= 8, (n, k, v, q)
+    B, a = random_inputs(n, k, dtype, "normal", seed=31)
+    ref, _, ab = oracle.gemv(dtype, B, a)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    for _ in range(3):
+        got = run(g, Bd, ad)
+        _check(dtype, got, ref, ab, k, v, "%dx%d auto q=%d" % (n, k, q))
+    Bi, ai = integer_inputs(n, k, dtype, seed=32)
+    refi, _, _ = oracle.gemv(dtype, Bi, ai)
+    goti = run(g, to_device(Bi, dtype), to_device(ai, dtype))
+    assert np.array_equal(goti, refi)
+
+
 def test_cross_workgroup_config_rules(g):
     nonx = [v for v in VARIANTS if not mbd.gemv_variant_info(v)[1].cross_wg][0]
     with pytest.raises(mbd.GemvError):

@@ -350,7 +350,9 @@ def test_plan_very_long_rows(n, k, want):
 
 @pytest.mark.parametrize("n,k,xwg", [
     (32, 131072, True), (64, 65536, True), (1, 65536, True), (7, 65536, True), (8, 65536, True),
-    (65, 65536, False), (127, 65536, False),    # more rows: the in-workgroup split
+    (65, 65536, True), (127, 65536, True), (128, 65536, True),
+    (129, 65536, False), (256, 131072, False),   # more rows of fewer steps: the in-workgroup split
+    (129, 262144, True), (256, 262144, True), (257, 262144, False),
     (64, 65535, False), (64, 32768, False),     # shorter rows: the in-workgroup split
     (128, 32768, False), (200, 16384, False),
     (64, 511, False), (64, 16383, False),
@@ -366,33 +368,55 @@ def test_plan_cross_workgroup_only_for_few_rows(n, k, xwg):
             assert cfg.kgroups == min(64, nfull // 16)
             assert shape_of(info) == (1, 4, 8, 8, 1, 1)
         else:
-            # 16 waves, about one workgroup per CU while every wave keeps at
-            # least two steps; four load slots when the share is four steps
-            q = max(2, min(256 // n, nfull // 32))
-            assert cfg.kgroups == q
+            # 16 waves, one row per workgroup; every wave keeps at least two
+            # steps, four load slots when its share is four steps or more
+            q = cfg.kgroups
+            assert 2 <= q <= min(8, nfull // 32)
+            assert cfg.grid == n
             assert shape_of(info) == (1, 4 if nfull // (q * 16) >= 4 else 2, 16, 16, 1, 1)
-        assert cfg.grid * cfg.kgroups <= 256 or n < 8
+            # no other Q puts fewer rows on the busiest CU (workgroups per
+            # CU over Q, 256 CUs)
+            busiest = lambda t: -(-n * t // 256) / t
+            assert all(busiest(q) <= busiest(t) for t in range(2, min(8, nfull // 32) + 1))
+
+
+@pytest.mark.parametrize("n,k,q", [
+    # hand-worked: workgroups on the busiest CU = ceil(n q / 256)
+    (64, 65536, 4),     # 1 of a quarter row each; Q = 8 ties (2 x 1/8), 4 is nearer 4
+    (80, 131072, 3),    # 240 workgroups: 1/3 row; Q = 6 ties (2 x 1/6)
+    (96, 131072, 8),    # 768 workgroups: 3 x 1/8 = 0.375, below Q = 4's 2 x 1/4
+    (128, 65536, 4),    # every even Q gives 1/2; 4 is nearest 4
+    (48, 131072, 5),    # 240 workgroups: 1/5
+    (16, 262144, 8),    # 128 workgroups: 1/8, the most Q allows
+    (256, 262144, 4),   # every Q gives one row; 4
+    (100, 65536, 4),    # Q <= 4 by steps; Q = 2 (200) and Q = 4 (400: 2 x 1/4) tie at 1/2
+])
+def test_plan_cross_workgroup_q(n, k, q):
+    cfg, info = plan(n, k, BF16)
+    assert info.cross_wg and cfg.kgroups == q, (n, k, cfg.kgroups)
 
 
 def test_plan_without_workspace_never_splits_across_workgroups():
     """gemv_run and gemv_run_ex bring no scratch: their plan is the
     workspace plan wherever that is not a cross-workgroup split, and the
-    in-workgroup split (one row per 8-wave workgroup, eight k-slices) where
-    it is."""
+    in-workgroup split where it is (below 128 rows one row per 8-wave
+    workgroup, eight k-slices)."""
     ns = [1, 7, 8, 32, 63, 64, 65, 127, 128, 1000, 18432]
     ks = [0, 511, 16384, 32768, 65535, 65536, 131072, 200000]
     for n, k, dtype in itertools.product(ns, ks, (F16, BF16)):
         cfg0, info0 = plan(n, k, dtype, ws=False)
         cfg1, info1 = plan(n, k, dtype, ws=True)
         assert not info0.cross_wg and cfg0.kgroups == 1
-        if info1.cross_wg:
+        if info1.cross_wg and n < 128:
             assert shape_of(info0) == (1, 4, 8, 8, 1, 0) and cfg0.grid == n, (n, k)
+        elif info1.cross_wg:
+            assert info0.splits > 1, (n, k, shape_of(info0))
         else:
             assert (cfg0.variant, cfg0.grid, cfg0.kgroups) == \
                 (cfg1.variant, cfg1.grid, cfg1.kgroups), (n, k, dtype)
 
 
-@pytest.mark.parametrize("n,k", [(127, 65536), (96, 65536), (64, 32768), (32, 16384), (1, 16384)])
+@pytest.mark.parametrize("n,k", [(127, 65535), (96, 60000), (64, 32768), (32, 16384), (1, 16384)])
 def test_plan_few_rows_split_in_workgroup(n, k):
     # fewer than 128 rows of >= 32 steps, not split across workgroups: one
     # row per 8-wave workgroup, eight k-slices
@@ -414,7 +438,7 @@ def test_plan_properties_over_a_sweep():
         if info.a_mode in (2, 3):
             assert misaligned
         if info.cross_wg:
-            assert n < 128
+            assert n <= 128 or (n <= 256 and k >= 512 * 512)
         if info.a_mode == 3 and info.rows == 2:
             # pairs of rows 64 apart: 64 pairs per block of 128 rows
             items, per_block = 64 * ((n + 127) // 128), info.waves // info.splits
