@@ -78,8 +78,9 @@ typedef enum {
   GEMV_ERR_MISALIGNED = 4,        /* a pointer is not 2-byte aligned */
   GEMV_ERR_ALIASING = 5,          /* c overlaps B or a */
   GEMV_ERR_TOO_LARGE = 6,         /* n > 2^30 or k > 2^27, or a forced k-split
-                                     across workgroups whose partials
-                                     (k-groups x n) exceed the scratch */
+                                     across workgroups whose partials (n x
+                                     k-groups rounded up to 32) exceed the
+                                     scratch */
   GEMV_ERR_WRONG_DEVICE = 7,      /* current HIP device != the handle's */
   GEMV_ERR_UNSUPPORTED = 8,       /* no kernel for this GPU / configuration */
   GEMV_ERR_HIP = 9,               /* a HIP runtime call failed */
@@ -91,9 +92,10 @@ typedef enum {
 #define GEMV_MAX_K 134217728LL
 
 /* Bytes of caller scratch that gemv_run_ws needs for its cross-workgroup
- * k-split: 256 KiB of arrival counters (64 banks of 1024, one bank per
- * k-group count) and 1 MiB of fp32 partial sums (k-groups x n <= 2^18). */
-#define GEMV_WORKSPACE_BYTES 1310720LL
+ * k-split: 2 MiB of arrival counters (64 banks of 256, one bank per k-group
+ * count, one counter per 128-byte line) and 1 MiB of fp32 partial sums
+ * (n rows x k-groups rounded up to a multiple of 32 <= 2^18). */
+#define GEMV_WORKSPACE_BYTES 3145728LL
 
 /* Create a handle bound to the current HIP device.  Queries the device (it
  * must be a gfx950), sets kernel attributes and fixes the variant table; it
@@ -160,8 +162,9 @@ gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void* a, void* c
  * streams, other handles, other threads) race -- their c is undefined --
  * so issue them on one stream or order them; gemv_run_ws with a workspace
  * per stream has no such limit.  A forced k-split across workgroups whose
- * partials (k-groups x n) exceed the scratch's 2^18 is GEMV_ERR_TOO_LARGE;
- * the automatic plan never needs more.  Otherwise as gemv_run_ws. */
+ * partials (n x k-groups rounded up to 32) exceed the scratch's 2^18 is
+ * GEMV_ERR_TOO_LARGE; the automatic plan never needs more.  Otherwise as
+ * gemv_run_ws. */
 gemv_status_t gemv_run_noalloc(gemv_handle_t h, const void* B, const void* a, void* c,
                                int64_t n, int64_t k, gemv_dtype_t dtype,
                                const gemv_epilogue_t* ep, hipStream_t stream);

@@ -77,7 +77,8 @@ const Variant kVariants[] = {
     MBD_VARIANT(1, 2, 8, 8, CCH, NT), MBD_VARIANT(1, 4, 8, 8, CCH, NT),
     MBD_VARIANT(2, 4, 8, 8, CCH, NT), MBD_VARIANT(1, 4, 4, 4, CCH, NT),
     MBD_VARIANT(1, 2, 16, 16, CCH, NT), MBD_VARIANT(1, 4, 16, 16, CCH, NT),
-    // 32..37: split across workgroups as well (small n)
+    // 32..37: split across workgroups as well (few rows of many steps: 33
+    // up to 96 rows, 37 up to 256)
     MBD_VARIANT_X(1, 4, 8, 8, CCH, NT, true), MBD_VARIANT_X(1, 2, 8, 8, CCH, NT, true),
     MBD_VARIANT_X(1, 4, 4, 4, CCH, NT, true), MBD_VARIANT_X(1, 2, 4, 4, CCH, NT, true),
     MBD_VARIANT_X(2, 4, 8, 4, CCH, NT, true), MBD_VARIANT_X(1, 4, 4, 1, CCH, NT, true),
@@ -114,9 +115,6 @@ const Variant kVariants[] = {
     // 72..73: two-slot batches over four slices, one or two rows per wave
     // (the plans of 513..895 rows of long rows)
     MBD_VARIANT(1, 2, 4, 4, CCH, NT), MBD_VARIANT(2, 2, 4, 4, CCH, NT),
-    // 74..75: split across workgroups with 16 waves each (the plans of
-    // 8..256 rows of at least 128 steps)
-    MBD_VARIANT_X(1, 2, 16, 16, CCH, NT, true), MBD_VARIANT_X(1, 4, 16, 16, CCH, NT, true),
 };
 #undef NT
 #undef LDS
@@ -151,14 +149,14 @@ int64_t items_per_block(const gemv_variant_info_t& v) {
   return pairs_rows(v) ? (int64_t)(v.waves / v.splits) : rows_per_block(v);
 }
 
-// Caller scratch of the cross-workgroup split (gemv_run_ws): first the
-// arrival counters, one bank of kXwgRanges per k-group count Q = 1..kXwgMaxQ
-// (so that a counter only ever sees one Q), then the fp32 partial sums, Q
-// per row (k-group q of row i at q * n + i).
-constexpr int kXwgMaxQ = 64;
-constexpr int kXwgRanges = 1024;
-constexpr size_t kWsCounterBytes = (size_t)kXwgMaxQ * kXwgRanges * sizeof(unsigned);   // 256 KiB
-constexpr size_t kWsFloats = (size_t)1 << 18;                                             // 1 MiB
+// Caller scratch of the cross-workgroup split (gemv_run_ws), laid out as
+// the kernel header states: the arrival counters, each in a 128-byte line of
+// its own, one bank per k-group count; then the fp32 partial sums, row by row
+// (k-group q of row i at i * xwg_row_stride(Q) + q).
+using mbd::kWsCounterBytes;
+using mbd::kWsFloats;
+using mbd::kXwgMaxQ;
+using mbd::kXwgRanges;
 static_assert(kWsCounterBytes + kWsFloats * sizeof(float) == (size_t)GEMV_WORKSPACE_BYTES,
               "the header's workspace size is the layout's");
 
@@ -221,10 +219,9 @@ int find_variant(const Plan& p) {
 //     k = 2049..6143 bf16: 2.6% off the best compiled plan on average).
 //  2. too few rows to give the GPU 2048 waves even with 16 waves per row
 //     (n < 128), with rows of at least 32 steps: one row per 8-wave
-//     workgroup, eight k-slices.  With a workspace, 8..128 rows of at least
-//     128 steps (up to 256 rows of at least 512) split k across Q 16-wave
-//     workgroups as well, Q chosen by the rows on the busiest CU (below);
-//     fewer than 8 rows across 8-wave workgroups, Q = steps / 16.
+//     workgroup, eight k-slices.  With a workspace, up to 192 rows of at
+//     least 128 steps (256 of at least 256) split k across Q workgroups as
+//     well (below).
 //  3. (misaligned rows below 768 of them take 4 as it stands, with
 //     unaligned 16-byte loads)
 //  4. otherwise a through the caches and non-temporal B loads, two rows per
@@ -290,34 +287,30 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // 2. k split over Q workgroups as well, for few rows of many steps -- only
   // with caller scratch for the partials and counters (gemv_run_ws);
-  // without it, the in-workgroup split below.  From 8 rows: 16 waves per row
-  // per workgroup, one row per workgroup, at most two workgroups resident
-  // per CU.  Q (2..8, every wave at least two steps: Q <= steps / 32) makes
-  // the busiest CU's share of rows, ceil(n Q / 256) / Q, smallest; ties go
-  // to the Q nearest 4 (two resident workgroups where that fits), then the
-  // smaller.  Two load slots per wave, four when the share is four steps or
-  // more.  Taken for 8..128 rows of >= 128 steps and up to 256 rows of
-  // >= 512 steps (graph replay over n = 1..256, k = 32K..256K, every split
-  // plan x Q = 2..32: 2.0% off the best compiled plan on average over 88
-  // shapes, 12% at worst, where 65..128 rows in the in-workgroup split were
-  // up to 72% off).  Below 8 rows: 8 waves, Q = steps / 16 (one row: 4-9%
-  // off the best, which wants four-wave workgroups of two steps).
-  if (with_ws && nfull0 >= 128 && n < 8) {
-    int64_t Q = nfull0 / 16;
-    if (Q > kXwgMaxQ) Q = kXwgMaxQ;
-    if (Q * n <= (int64_t)kWsFloats) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
-  }
-  if (with_ws && nfull0 >= 128 && n >= 8 && (n <= 128 || (n <= 256 && nfull0 >= 512))) {
-    int64_t Q = 0, best_c = 0;
-    for (int64_t t = 2; t <= 8 && t <= nfull0 / 32; ++t) {
-      const int64_t c = (n * t + 255) / 256;   // workgroups on the busiest CU
-      // c / t against best_c / Q; on a tie, nearer 4, then smaller
-      const int64_t lhs = c * Q, rhs = best_c * t;
-      const int64_t dt = t > 4 ? t - 4 : 4 - t, dq = Q > 4 ? Q - 4 : 4 - Q;
-      if (Q == 0 || lhs < rhs || (lhs == rhs && dt < dq)) { Q = t; best_c = c; }
+  // without it, the in-workgroup split below.  Up to 96 rows: one row per
+  // 8-wave workgroup, eight slices of two steps per wave (one batch of two
+  // load slots), Q = steps / 16 workgroups per row.  97..192 rows, or up to
+  // 256 rows of >= 256 steps: four rows per 4-wave workgroup, each wave one
+  // row's share of k, Q = steps / 8 (eight steps, two batches of four, per
+  // wave).  Q at most 64.  (Graph replay, every cross-workgroup variant x
+  // Q = 2..64 and the in-workgroup plans: 1.9% off the best compiled plan on
+  // average over 45 shapes of n = 1..256, k = 32K..256K, 10% at worst; 2.8%
+  // and 9.3% on 27 shapes outside that fit, n = 2..224, k = 96K..512K.  The
+  // combine's counters and partials sit in lines of their own, so many
+  // workgroups per row do not queue on shared lines; packed, the best Q was
+  // 4..8 and the 16-wave split, at 2.0% on average over the fit's range.)
+  if (with_ws && nfull0 >= 128 && n <= 256) {
+    if (n <= 96) {
+      int64_t Q = nfull0 / 16;
+      if (Q > kXwgMaxQ) Q = kXwgMaxQ;
+      if (n * mbd::xwg_row_stride(Q) <= (int64_t)kWsFloats)
+        return Plan{1, 2, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
+    } else if (n <= 192 || nfull0 >= 256) {
+      int64_t Q = nfull0 / 8;
+      if (Q > kXwgMaxQ) Q = kXwgMaxQ;
+      if (n * mbd::xwg_row_stride(Q) <= (int64_t)kWsFloats)
+        return Plan{1, 4, 4, 1, mbd::A_CACHED, kPolNT, 0, (int)Q};
     }
-    const int U = nfull0 / (Q * 16) >= 4 ? 4 : 2;
-    if (Q * n <= (int64_t)kWsFloats) return Plan{1, U, 16, 16, mbd::A_CACHED, kPolNT, 0, (int)Q};
   }
   if (n < 128 && nfull0 >= 32) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.
@@ -527,10 +520,11 @@ static gemv_status_t shape_launch(int v, int64_t g, int64_t q, int flags, int64_
   if (info.cross_wg) {
     if (q <= 0) q = 4;
     if (q > kXwgMaxQ) return GEMV_ERR_UNSUPPORTED;
-    // the scratch holds q partials per row and one counter per row range
-    // (a smaller grid is valid: each workgroup walks a longer row range)
+    // the scratch holds a line-padded row of q partials per row and one
+    // counter per row range (a smaller grid is valid: each workgroup walks
+    // a longer row range)
     if (g > kXwgRanges) g = kXwgRanges;
-    if (q * n > (int64_t)kWsFloats) return GEMV_ERR_TOO_LARGE;   // more partials than the scratch holds
+    if (n * mbd::xwg_row_stride(q) > (int64_t)kWsFloats) return GEMV_ERR_TOO_LARGE;   // partials beyond the scratch
   } else {
     if (q > 1) return GEMV_ERR_INVALID_ARG;
     q = 1;
@@ -729,7 +723,7 @@ extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void*
   Launch L;
   s = resolve(h, n, k, dtype, ((uintptr_t)B & 15u) == 0, workspace != nullptr, &L);
   if (s != GEMV_OK)
-    return report(h, s, s == GEMV_ERR_TOO_LARGE ? "k-groups x rows exceed the scratch's 2^18 partials"
+    return report(h, s, s == GEMV_ERR_TOO_LARGE ? "rows x k-groups (rounded up to 32) exceed the scratch's 2^18 partials"
                                                 : "no variant fits (LDS, or scratch for the k-split)");
   const Variant& var = kVariants[L.variant];
   const gemv_variant_info_t& vi = var.info;
@@ -739,7 +733,8 @@ extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void*
   p.c = (uint16_t*)c;
   p.bias = ep ? (const uint16_t*)ep->bias : nullptr;
   // the scratch: the counter bank of this k-group count, then the partials
-  p.cnt = workspace ? (unsigned*)workspace + (size_t)(L.kgroups - 1) * kXwgRanges : nullptr;
+  p.cnt = workspace ? (unsigned*)workspace + (size_t)(L.kgroups - 1) * kXwgRanges * mbd::kCntStride
+                    : nullptr;
   p.ws = workspace ? (float*)((char*)workspace + kWsCounterBytes) : nullptr;
   p.n = (int)n;
   p.k = (int)k;

@@ -140,6 +140,23 @@ constexpr int kFlagXcdContiguous = 1;
 // c = alpha * sum + bias, one fp32 FMA on the row sum before the store.
 constexpr int kFlagEpilogue = 2;
 
+// Scratch layout of the cross-workgroup split, shared with the host: each
+// arrival counter alone in a 128-byte line (kCntStride words apart), and a
+// row's Q partial sums together at row * xwg_row_stride(Q) + q, the stride Q
+// rounded up to whole 128-byte lines -- no two rows, and no two counters,
+// share a line.  Packed, the counters and partials of neighbouring rows
+// shared lines, and the atomics and stores of different workgroups queued
+// on them (measured on MI355X: 64 x 65536 bf16 5.40 -> 4.89 us).
+// The whole scratch: first the counters, one bank of kXwgRanges per k-group
+// count Q = 1..kXwgMaxQ (so that a counter only ever sees one Q), then
+// kWsFloats partials.
+constexpr int kCntStride = 32;
+constexpr int kXwgMaxQ = 64;
+constexpr int kXwgRanges = 256;
+constexpr size_t kWsCounterBytes = (size_t)kXwgMaxQ * kXwgRanges * kCntStride * sizeof(unsigned);  // 2 MiB
+constexpr size_t kWsFloats = (size_t)1 << 18;                                                      // 1 MiB
+__host__ __device__ constexpr int64_t xwg_row_stride(int64_t Q) { return (Q + 31) & ~(int64_t)31; }
+
 __device__ __forceinline__ int64_t xcd_unit(int64_t b, int64_t G) {
   const int64_t x = b % kXcds, i = b / kXcds;
   const int64_t q = G / kXcds, r = G % kXcds;
@@ -454,7 +471,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
       if constexpr (XWG) {
         // agent-scope store: written through this XCD's L2 to the point
         // where every XCD sees it
-        __hip_atomic_store(&ws[(int64_t)q * n + row0 + lane], mine, __ATOMIC_RELAXED,
+        __hip_atomic_store(&ws[(int64_t)(row0 + lane) * xwg_row_stride(Q) + q], mine, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       } else {
         c[row0 + lane] = to_bits<DT>(finish<DT>(mine, flags, alpha, bias, row0 + lane));
@@ -496,13 +513,13 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
       __builtin_amdgcn_s_waitcnt(0);
       unsigned old = 0;
       if (lane == 0)
-        old = __builtin_amdgcn_atomic_inc32(&cnt[blockIdx.x], (unsigned)(Q - 1), __ATOMIC_RELAXED,
+        old = __builtin_amdgcn_atomic_inc32(&cnt[(int64_t)blockIdx.x * kCntStride], (unsigned)(Q - 1), __ATOMIC_RELAXED,
                                             "agent");
       if (__builtin_amdgcn_readfirstlane(old) != (unsigned)(Q - 1)) return;
       for (int r = lo; r < hi; ++r) {
         float s = 0.0f;
         for (int qq = lane; qq < Q; qq += kLanes)
-          s += __hip_atomic_load(&ws[(int64_t)qq * n + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s += __hip_atomic_load(&ws[(int64_t)r * xwg_row_stride(Q) + qq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s = wave_sum(s);
         if (lane == 0) c[r] = to_bits<DT>(finish<DT>(s, flags, alpha, bias, r));
       }
@@ -512,7 +529,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-      last = __builtin_amdgcn_atomic_inc32(&cnt[blockIdx.x], (unsigned)(Q - 1), __ATOMIC_RELAXED,
+      last = __builtin_amdgcn_atomic_inc32(&cnt[(int64_t)blockIdx.x * kCntStride], (unsigned)(Q - 1), __ATOMIC_RELAXED,
                                            "agent") == (unsigned)(Q - 1);
     }
     __syncthreads();
@@ -522,7 +539,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
       for (int r = lo + wave; r < hi; r += WAVES) {
         float s = 0.0f;
         for (int qq = lane; qq < Q; qq += kLanes)
-          s += __hip_atomic_load(&ws[(int64_t)qq * n + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s += __hip_atomic_load(&ws[(int64_t)r * xwg_row_stride(Q) + qq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s = wave_sum(s);
         if (lane == 0) c[r] = to_bits<DT>(finish<DT>(s, flags, alpha, bias, r));
       }

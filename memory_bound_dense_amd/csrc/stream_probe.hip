@@ -106,7 +106,7 @@ const ProbeShape kProbeShapes[] = {
     MBD_PROBE(1, 4, 4, 4, 0), MBD_PROBE(1, 4, 8, 8, 0), MBD_PROBE(2, 4, 1, 1, 0),
     MBD_PROBE(1, 4, 2, 1, 0), MBD_PROBE(1, 4, 8, 8, 1), MBD_PROBE(2, 2, 8, 8, 0),
     MBD_PROBE(2, 8, 4, 4, 0), MBD_PROBE(2, 8, 8, 8, 0), MBD_PROBE(1, 2, 4, 4, 0),
-    MBD_PROBE(2, 2, 4, 4, 0), MBD_PROBE(1, 2, 16, 16, 1), MBD_PROBE(1, 4, 16, 16, 1),
+    MBD_PROBE(2, 2, 4, 4, 0), MBD_PROBE(1, 2, 8, 8, 1), MBD_PROBE(1, 4, 4, 1, 1),
 };
 #undef MBD_PROBE
 
@@ -175,13 +175,14 @@ extern "C" int mbd_gemv_probe(int rows, int unroll, int waves, int splits, int x
     if (p.rows == rows && p.unroll == unroll && p.waves == waves && p.splits == splits && p.xwg == xwg)
       ps = &p;
   if (!ps || !B || !out || n <= 0 || k <= 0 || k % 8 != 0 || ((uintptr_t)B % 16) != 0 ||
-      n > (1 << 30) || k > (1 << 27) || grid <= 0 || (xwg ? (!workspace || kgroups < 1 || kgroups > 64 ||
-                                                              kgroups * n > (1 << 18) || grid > 1024)
-                                                            : kgroups != 1))
+      n > (1 << 30) || k > (1 << 27) || grid <= 0 ||
+      (xwg ? (!workspace || kgroups < 1 || kgroups > mbd::kXwgMaxQ ||
+              n * mbd::xwg_row_stride(kgroups) > (int64_t)mbd::kWsFloats || grid > mbd::kXwgRanges)
+           : kgroups != 1))
     return -1;
   // the row ranges and k-slices exactly as gemv_run_ws deals them; the
-  // workspace (xwg) is laid out as gemv_run_ws's: 64 counter banks of 1024,
-  // then the partials
+  // workspace (xwg) is laid out as gemv_run_ws's: the counter banks, then
+  // the partials
   const int64_t rb = (int64_t)(waves / splits) * rows;
   if ((int64_t)grid > (n + rb - 1) / rb) return -1;
   const int64_t units = (splits == 1 && !xwg) ? (int64_t)grid * (waves / splits) : grid;
@@ -192,8 +193,9 @@ extern "C" int mbd_gemv_probe(int rows, int unroll, int waves, int splits, int x
   const uint16_t* ap = Bp;   // never read in the PROBE build
   uint16_t* cp = (uint16_t*)out;
   const uint16_t* bias = nullptr;
-  unsigned* cnt = xwg ? (unsigned*)workspace + (size_t)(kgroups - 1) * 1024 : nullptr;
-  float* ws = xwg ? (float*)((char*)workspace + (size_t)64 * 1024 * sizeof(unsigned)) : nullptr;
+  unsigned* cnt =
+      xwg ? (unsigned*)workspace + (size_t)(kgroups - 1) * mbd::kXwgRanges * mbd::kCntStride : nullptr;
+  float* ws = xwg ? (float*)((char*)workspace + mbd::kWsCounterBytes) : nullptr;
   int ni = (int)n, ki = (int)k, flags = 0;
   float alpha = 1.0f;
   void* args[] = {(void*)&Bp,      (void*)&ap,      (void*)&cp,      (void*)&ni,

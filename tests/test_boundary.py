@@ -236,7 +236,7 @@ def test_plain_c_consumer(tmp_path):
     assert out["plan_status"] == str(_lib.GEMV_OK)
     assert out["plan_shape"] == "R2 U4 W4 S4 grid 9216"      # the headline's plan
     assert out["variants"] == str(mbd.gemv_num_variants())
-    assert out["plan_ws_kgroups"] == "%d 4" % _lib.GEMV_OK   # 64 x 65536: 4 k-groups with scratch
+    assert out["plan_ws_kgroups"] == "%d 8" % _lib.GEMV_OK   # 64 x 65536: 8 k-groups with scratch
     assert out["workspace_bytes"] == str(_lib.GEMV_WORKSPACE_BYTES)
     assert out["run_ws_null_handle"] == str(_lib.GEMV_ERR_NULL_HANDLE)
     assert out["run_noalloc_null_handle"] == str(_lib.GEMV_ERR_NULL_HANDLE)

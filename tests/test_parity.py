@@ -448,7 +448,7 @@ def test_cross_workgroup_split(g, n, k, dtype):
     for v in XWG:
         for q in (1, 2, 3, 8, 33, 64):
             for grid in (0, 1, 3):
-                if q * n > (1 << 18):       # the partials' share of the workspace
+                if n * -(-q // 32) * 32 > (1 << 18):   # the partials' share of the workspace
                     continue
                 for _ in range(2):
                     got = run(g, Bd, ad, v, grid, q)
@@ -460,20 +460,20 @@ def test_cross_workgroup_split(g, n, k, dtype):
 
 
 AUTO_XWG_SHAPES = [(96, 131072, BF16), (100, 65544, F16), (129, 262152, BF16), (200, 262144, F16),
-                   (16, 262144, BF16), (48, 131075, F16)]
+                   (16, 262144, BF16), (48, 131075, F16), (3, 1048576, BF16), (194, 131073, F16)]
 
 
 @pytest.mark.parametrize("n,k,dtype", AUTO_XWG_SHAPES,
                          ids=["%dx%d_%s" % (n, k, "f16" if d == F16 else "bf16")
                               for n, k, d in AUTO_XWG_SHAPES])
 def test_auto_plan_cross_workgroup_rows(g, n, k, dtype):
-    """The automatic plan's cross-workgroup split over its whole range (8 to
-    256 rows, Q = 2..8 k-groups of 16-wave workgroups, rows with and without
-    a partial step): every row against the oracle, three calls back to back
-    (the counters return to zero between calls), and integer inputs
-    bit-exact."""
+    """The automatic plan's cross-workgroup split over its whole range (up
+    to 256 rows, 8 to 64 k-groups, one row per 8-wave workgroup or four per
+    4-wave workgroup, rows with and without a partial step): every row
+    against the oracle, three calls back to back (the counters return to
+    zero between calls), and integer inputs bit-exact."""
     v, grid, q = g.query_config(n, k, dtype)
-    assert mbd.gemv_variant_info(v)[1].cross_wg and 2 <= q <= 8, (n, k, v, q)
+    assert mbd.gemv_variant_info(v)[1].cross_wg and 2 <= q <= 64, (n, k, v, q)
     B, a = random_inputs(n, k, dtype, "normal", seed=31)
     ref, _, ab = oracle.gemv(dtype, B, a)
     Bd, ad = to_device(B, dtype), to_device(a, dtype)
@@ -500,6 +500,14 @@ def test_cross_workgroup_config_rules(g):
     g.force_config(v, 0, 64)
     with pytest.raises(mbd.GemvError) as e:
         g(B, a, c)
+    assert e.value.status == mbd._lib.GEMV_ERR_TOO_LARGE
+    g.force_config(-1)
+    # a row's partials take whole 128-byte lines: 2 k-groups take 32 slots a
+    # row, so 8192 rows fit the 2^18 partials and 8193 do not
+    g.force_config(v, 0, 2)
+    assert g.query_config(8192, 4096, mbd.GEMV_F16)[2] == 2
+    with pytest.raises(mbd.GemvError) as e:
+        g.query_config(8193, 4096, mbd.GEMV_F16)
     assert e.value.status == mbd._lib.GEMV_ERR_TOO_LARGE
     g.force_config(-1)
     torch.cuda.synchronize()

@@ -50,7 +50,7 @@ WORKLOAD_PLANS = {
     "sweep_14336x4096_bf16": (1, 8, 4, 1, 1, 0),
     "sweep_4096x14336_f16": (2, 8, 4, 4, 1, 0),
     "sweep_4096x14336_bf16": (2, 8, 4, 4, 1, 0),
-    "ragged_64x65536_bf16": (1, 2, 16, 16, 1, 1),
+    "ragged_64x65536_bf16": (1, 2, 8, 8, 1, 1),
     "ragged_1000x7000_bf16": (2, 4, 4, 4, 1, 0),
     "ragged_18433x7169_bf16": (2, 4, 4, 4, 3, 0),
     "large_28672x8192_f16": (2, 4, 4, 4, 1, 0),
@@ -95,8 +95,8 @@ def test_plan_grids_of_the_production_shapes():
     # rows of at most 3 steps
     assert plan(12288, 2049, BF16)[0].grid == 1024
     assert plan(8192, 1025, BF16)[0].grid == 1536
-    # 64 rows: k shared by 4 workgroups per row range
-    assert plan(64, 65536, BF16)[0].kgroups == 4
+    # 64 rows: k shared by 8 workgroups per row
+    assert plan(64, 65536, BF16)[0].kgroups == 8
 
 
 def _nst(k):
@@ -350,9 +350,9 @@ def test_plan_very_long_rows(n, k, want):
 
 @pytest.mark.parametrize("n,k,xwg", [
     (32, 131072, True), (64, 65536, True), (1, 65536, True), (7, 65536, True), (8, 65536, True),
-    (65, 65536, True), (127, 65536, True), (128, 65536, True),
-    (129, 65536, False), (256, 131072, False),   # more rows of fewer steps: the in-workgroup split
-    (129, 262144, True), (256, 262144, True), (257, 262144, False),
+    (65, 65536, True), (127, 65536, True), (128, 65536, True), (192, 65536, True),
+    (193, 65536, False), (256, 131071, False),   # more rows of fewer steps: the in-workgroup split
+    (193, 131072, True), (256, 131072, True), (256, 262144, True), (257, 262144, False),
     (64, 65535, False), (64, 32768, False),     # shorter rows: the in-workgroup split
     (128, 32768, False), (200, 16384, False),
     (64, 511, False), (64, 16383, False),
@@ -363,33 +363,26 @@ def test_plan_cross_workgroup_only_for_few_rows(n, k, xwg):
     assert (cfg.kgroups > 1) == xwg
     if xwg:
         nfull = k // 512
-        if n < 8:
-            # 8 waves, two steps per wave
+        if n <= 96:
+            # one row per 8-wave workgroup, two steps per wave
+            assert shape_of(info) == (1, 2, 8, 8, 1, 1)
             assert cfg.kgroups == min(64, nfull // 16)
-            assert shape_of(info) == (1, 4, 8, 8, 1, 1)
-        else:
-            # 16 waves, one row per workgroup; every wave keeps at least two
-            # steps, four load slots when its share is four steps or more
-            q = cfg.kgroups
-            assert 2 <= q <= min(8, nfull // 32)
             assert cfg.grid == n
-            assert shape_of(info) == (1, 4 if nfull // (q * 16) >= 4 else 2, 16, 16, 1, 1)
-            # no other Q puts fewer rows on the busiest CU (workgroups per
-            # CU over Q, 256 CUs)
-            busiest = lambda t: -(-n * t // 256) / t
-            assert all(busiest(q) <= busiest(t) for t in range(2, min(8, nfull // 32) + 1))
+        else:
+            # four rows per 4-wave workgroup, eight steps per wave
+            assert shape_of(info) == (1, 4, 4, 1, 1, 1)
+            assert cfg.kgroups == min(64, nfull // 8)
+            assert cfg.grid == (n + 3) // 4
 
 
 @pytest.mark.parametrize("n,k,q", [
-    # hand-worked: workgroups on the busiest CU = ceil(n q / 256)
-    (64, 65536, 4),     # 1 of a quarter row each; Q = 8 ties (2 x 1/8), 4 is nearer 4
-    (80, 131072, 3),    # 240 workgroups: 1/3 row; Q = 6 ties (2 x 1/6)
-    (96, 131072, 8),    # 768 workgroups: 3 x 1/8 = 0.375, below Q = 4's 2 x 1/4
-    (128, 65536, 4),    # every even Q gives 1/2; 4 is nearest 4
-    (48, 131072, 5),    # 240 workgroups: 1/5
-    (16, 262144, 8),    # 128 workgroups: 1/8, the most Q allows
-    (256, 262144, 4),   # every Q gives one row; 4
-    (100, 65536, 4),    # Q <= 4 by steps; Q = 2 (200) and Q = 4 (400: 2 x 1/4) tie at 1/2
+    (64, 65536, 8),      # 128 steps: 8 workgroups of 8 waves x 2 steps per row
+    (1, 65536, 8),
+    (96, 131072, 16),
+    (16, 262144, 32),
+    (8, 1048576, 64),    # 2048 steps would take 128 workgroups of 16: the cap
+    (97, 65536, 16),     # four rows per workgroup from 97 rows, 8 steps per wave
+    (256, 262144, 64),
 ])
 def test_plan_cross_workgroup_q(n, k, q):
     cfg, info = plan(n, k, BF16)
@@ -438,7 +431,7 @@ def test_plan_properties_over_a_sweep():
         if info.a_mode in (2, 3):
             assert misaligned
         if info.cross_wg:
-            assert n <= 128 or (n <= 256 and k >= 512 * 512)
+            assert n <= 192 or (n <= 256 and k >= 256 * 512)
         if info.a_mode == 3 and info.rows == 2:
             # pairs of rows 64 apart: 64 pairs per block of 128 rows
             items, per_block = 64 * ((n + 127) // 128), info.waves // info.splits
