@@ -252,7 +252,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
   const uint16_t* __restrict__ B = p.B;
   const uint16_t* __restrict__ a = p.a;
   uint16_t* c = p.c;
-  const int n = p.n, k = p.k, flags = p.flags;
+  const int k = p.k, flags = p.flags;
   const float alpha = p.alpha;
   const uint16_t* bias = p.bias;
   float* __restrict__ ws = p.ws;
