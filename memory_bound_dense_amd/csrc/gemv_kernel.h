@@ -513,13 +513,14 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
       __builtin_amdgcn_s_waitcnt(0);
       unsigned old = 0;
       if (lane == 0)
-        old = __builtin_amdgcn_atomic_inc32(&cnt[(int64_t)blockIdx.x * kCntStride], (unsigned)(Q - 1), __ATOMIC_RELAXED,
-                                            "agent");
+        old = __builtin_amdgcn_atomic_inc32(&cnt[(int64_t)blockIdx.x * kCntStride], (unsigned)(Q - 1),
+                                            __ATOMIC_RELAXED, "agent");
       if (__builtin_amdgcn_readfirstlane(old) != (unsigned)(Q - 1)) return;
       for (int r = lo; r < hi; ++r) {
         float s = 0.0f;
         for (int qq = lane; qq < Q; qq += kLanes)
-          s += __hip_atomic_load(&ws[(int64_t)r * xwg_row_stride(Q) + qq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s += __hip_atomic_load(&ws[(int64_t)r * xwg_row_stride(Q) + qq], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
         s = wave_sum(s);
         if (lane == 0) c[r] = to_bits<DT>(finish<DT>(s, flags, alpha, bias, r));
       }
@@ -529,8 +530,8 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-      last = __builtin_amdgcn_atomic_inc32(&cnt[(int64_t)blockIdx.x * kCntStride], (unsigned)(Q - 1), __ATOMIC_RELAXED,
-                                           "agent") == (unsigned)(Q - 1);
+      last = __builtin_amdgcn_atomic_inc32(&cnt[(int64_t)blockIdx.x * kCntStride], (unsigned)(Q - 1),
+                                           __ATOMIC_RELAXED, "agent") == (unsigned)(Q - 1);
     }
     __syncthreads();
     if (last) {
@@ -539,7 +540,8 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
       for (int r = lo + wave; r < hi; r += WAVES) {
         float s = 0.0f;
         for (int qq = lane; qq < Q; qq += kLanes)
-          s += __hip_atomic_load(&ws[(int64_t)r * xwg_row_stride(Q) + qq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s += __hip_atomic_load(&ws[(int64_t)r * xwg_row_stride(Q) + qq], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
         s = wave_sum(s);
         if (lane == 0) c[r] = to_bits<DT>(finish<DT>(s, flags, alpha, bias, r));
       }
