@@ -93,9 +93,10 @@ typedef enum {
 
 /* Bytes of caller scratch that gemv_run_ws needs for its cross-workgroup
  * k-split: 2 MiB of arrival counters (64 banks of 256, one bank per k-group
- * count, one counter per 128-byte line) and 1 MiB of fp32 partial sums
- * (n rows x k-groups rounded up to a multiple of 32 <= 2^18). */
-#define GEMV_WORKSPACE_BYTES 3145728LL
+ * count, one counter per 128-byte line), 1 MiB of fp32 partial sums (n rows x
+ * k-groups rounded up to a multiple of 32 <= 2^18), and 1.92 MiB of ticket
+ * lines (64 banks of 96 rows: the split with one row per workgroup). */
+#define GEMV_WORKSPACE_BYTES 5160960LL
 
 /* Create a handle bound to the current HIP device.  Queries the device (it
  * must be a gfx950), sets kernel attributes and fixes the variant table; it
@@ -140,11 +141,16 @@ gemv_status_t gemv_run_ex(gemv_handle_t h, const void* B, const void* a, void* c
  *                    the caller; the library keeps no reference after the
  *                    call's kernel completes.
  *   contents:        zero-filled once before its first use (e.g. hipMemset);
- *                    from then on every completed call leaves its counters
- *                    at zero, so it needs no clearing between calls.
+ *                    from then on every completed call leaves it in a state
+ *                    the next call accepts (each arrival counter at zero or
+ *                    at a multiple of the call's k-group count, every
+ *                    published partial tagged with a finished generation),
+ *                    so it needs no clearing between calls.
  *   concurrency:     calls that may overlap on the GPU need different
  *                    workspaces; overlapping calls on one workspace race (c
- *                    undefined), though the counters still return to zero
+ *                    undefined, possibly NaN: a combining workgroup that
+ *                    finds a partial missing gives up after a bounded number
+ *                    of polls), though the workspace is back in such a state
  *                    once those calls have completed.
  * Validation as gemv_run_ex, then (n > 0) the workspace checks above. */
 gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void* a, void* c,

@@ -33,7 +33,7 @@ GEMV_FLAG_XCD_CONTIGUOUS = 1
 
 GEMV_MAX_N = 1073741824
 GEMV_MAX_K = 134217728
-GEMV_WORKSPACE_BYTES = 3145728
+GEMV_WORKSPACE_BYTES = 5160960
 
 # every symbol include/gemv.h and include/gla_decode.h declare
 EXPORTS = ("gemv_create", "gemv_run", "gemv_run_ex", "gemv_run_ws", "gemv_run_noalloc",

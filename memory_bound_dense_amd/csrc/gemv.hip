@@ -157,7 +157,8 @@ using mbd::kWsCounterBytes;
 using mbd::kWsFloats;
 using mbd::kXwgMaxQ;
 using mbd::kXwgRanges;
-static_assert(kWsCounterBytes + kWsFloats * sizeof(float) == (size_t)GEMV_WORKSPACE_BYTES,
+static_assert(kWsCounterBytes + kWsFloats * sizeof(float) + mbd::kWsTicketBytes ==
+                  (size_t)GEMV_WORKSPACE_BYTES,
               "the header's workspace size is the layout's");
 
 // Shape of a launch plan: a variant shape plus a workgroup count (0 = one
@@ -739,6 +740,15 @@ extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void*
   p.n = (int)n;
   p.k = (int)k;
   p.flags = L.flags | (ep ? mbd::kFlagEpilogue : 0);
+  // One row per workgroup of one row group, as the automatic plan's split of
+  // up to 96 rows has it: the ticketed combine, on its own bank of the
+  // scratch (pointed to by ws; the kernel takes its row lines from there).
+  if (workspace && vi.cross_wg && vi.rows == 1 && vi.waves == vi.splits && L.grid == n &&
+      n <= mbd::kTicketRows) {
+    p.ws = (float*)((char*)workspace + kWsCounterBytes + kWsFloats * sizeof(float) +
+                    mbd::ticket_bank_offset(L.kgroups));
+    p.flags |= mbd::kFlagTicket;
+  }
   p.alpha = ep ? ep->alpha : 1.0f;
   // balanced shares: rows over the row units, full k-steps over the k-slices
   int64_t units;

@@ -157,6 +157,27 @@ constexpr size_t kWsCounterBytes = (size_t)kXwgMaxQ * kXwgRanges * kCntStride * 
 constexpr size_t kWsFloats = (size_t)1 << 18;                                                      // 1 MiB
 __host__ __device__ constexpr int64_t xwg_row_stride(int64_t Q) { return (Q + 31) & ~(int64_t)31; }
 
+// The ticketed combine (kFlagTicket: one row per workgroup, one row group)
+// has a region of its own after the partials: one bank per Q, kTicketRows
+// row lines of ticket_stride(Q) 8-byte words each -- word 0 holds the row's
+// ticket counter, word 1 + q the partial of k-group q with its tag in the
+// high half.  A line is a whole number of 128-byte lines.
+constexpr int kFlagTicket = 4;
+constexpr int kTicketRows = 96;
+constexpr int kTicketSpins = 1 << 20;   // polls before a waiting combiner gives up
+__host__ __device__ constexpr int64_t ticket_stride(int64_t Q) { return (Q + 1 + 15) & ~(int64_t)15; }
+constexpr size_t ticket_bank_offset(int Q) {   // bytes from the region's start to bank Q
+  size_t b = 0;
+  for (int j = 1; j < Q; ++j) b += (size_t)kTicketRows * (size_t)ticket_stride(j) * 8u;
+  return b;
+}
+constexpr size_t kWsTicketBytes = ticket_bank_offset(kXwgMaxQ + 1);
+// tickets count 0, 1, ..., Q * M - 1 and wrap to 0, M = floor((2^31 - 1) / Q):
+// a multiple of Q, so whole calls keep the counter at a multiple of Q
+__host__ __device__ constexpr unsigned ticket_wrap(int Q) {
+  return (unsigned)Q * (0x7fffffffu / (unsigned)Q) - 1u;
+}
+
 __device__ __forceinline__ int64_t xcd_unit(int64_t b, int64_t G) {
   const int64_t x = b % kXcds, i = b / kXcds;
   const int64_t q = G / kXcds, r = G % kXcds;
@@ -310,6 +331,30 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
   constexpr int kTrip = kWaveRanges ? R : RB;
   const int goff = kWaveRanges ? 0 : rg * R;
 
+  // The ticketed combine (below) draws its ticket once the wave's loads of
+  // B and a are consumed: its round trip then overlaps the wave's reduction
+  // and the workgroup's combine.  (Drawn before the loads, it delays them:
+  // the loads' waits count it too, returns being counted in order; drawn
+  // between them, the compiler's wait after the branch that issues it is
+  // as conservative.)
+  [[maybe_unused]] unsigned ticket = 0;
+  [[maybe_unused]] float kept = 0.0f;
+  [[maybe_unused]] uint64_t* tline = nullptr;   // this row's line in the ticket bank
+  [[maybe_unused]] bool take_ticket = false;
+  if constexpr (XWG && G == 1) {
+    tline = reinterpret_cast<uint64_t*>(ws) + (int64_t)lo * ticket_stride(Q);
+    take_ticket = (flags & kFlagTicket) && wave == 0 && lane == 0;
+  }
+  auto draw_ticket = [&]() {
+    if constexpr (XWG && G == 1) {
+      if (take_ticket) {
+        ticket = __builtin_amdgcn_atomic_inc32(reinterpret_cast<unsigned*>(tline), ticket_wrap(Q),
+                                               __ATOMIC_RELAXED, "agent");
+        take_ticket = false;
+      }
+    }
+  };
+
   for (int base = lo; base < hi; base += kTrip) {   // trip count uniform in a workgroup when S > 1
     const int row0 = base + goff;                    // may lie past hi for S > 1: computed, not stored
     const int rbase = row0 < hi ? row0 : hi - 1;
@@ -364,6 +409,7 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
           for (int r = 0; r < R; ++r) accumulate<DT, PROBE>(bv[u][r], av[u], acc[r][0], acc[r][1]);
         }
       }
+      draw_ticket();
       if (tail && (k & (kVec - 1)) != 0 && e0 < k && e0 + kVec > k) {
         u32x4 ap;
         if constexpr (AMODE == A_LDS) {
@@ -469,15 +515,22 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     }
     if (leader) {
       if constexpr (XWG) {
-        // agent-scope store: written through this XCD's L2 to the point
-        // where every XCD sees it
-        __hip_atomic_store(&ws[(int64_t)(row0 + lane) * xwg_row_stride(Q) + q], mine, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        if (G == 1 && (flags & kFlagTicket)) {
+          kept = mine;   // published below, with its tag
+        } else {
+          // agent-scope store: written through this XCD's L2 to the point
+          // where every XCD sees it
+          __hip_atomic_store(&ws[(int64_t)(row0 + lane) * xwg_row_stride(Q) + q], mine,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       } else {
         c[row0 + lane] = to_bits<DT>(finish<DT>(mine, flags, alpha, bias, row0 + lane));
       }
     }
   }
+
+
+  draw_ticket();   // (drawn above already on the one-row paths that take it)
 
   if constexpr (XWG) {
     // Publish, count, combine.  Agent-scope accesses are coherent across the
@@ -510,6 +563,53 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
       // combines -- no workgroup barrier on this path (the other waves are
       // done).
       if (wave != 0) return;
+      if (flags & kFlagTicket) {
+        // Ticketed: the workgroup that drew the last ticket of its
+        // generation (ticket % Q == Q - 1) combines.  Every other workgroup
+        // of that generation drew its ticket before it, so is already
+        // running and finishes without waiting on anything: the combiner's
+        // wait always ends.  Producers publish {partial, tag} in one 8-byte
+        // agent-scope store (single-copy atomic) and leave, with no
+        // acknowledgement wait and no second atomic; the combiner polls the
+        // other k-groups' words until each carries this generation's tag,
+        // then sums lane q = k-group q in the fixed tree, as the counted
+        // combine does (same bits).  The tag is the generation + 1, never 0
+        // (a cleared word), and the combiner clears its own k-group's word,
+        // so every call rewrites all Q words: a word with the current tag
+        // was written in this call.  Calls that raced on one workspace draw
+        // tickets from one counter; a generation may then lack a k-group,
+        // and its combiner gives up after kTicketSpins polls and writes NaN.
+        // Each call draws exactly Q tickets, so the counter stays a multiple
+        // of Q and later calls are whole generations again.
+        const unsigned t = __builtin_amdgcn_readfirstlane(ticket);
+        const unsigned gen = t / (unsigned)Q;
+        const unsigned tag = gen + 1u;
+        const float my = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                       __builtin_bit_cast(int, kept)));
+        if (t - gen * (unsigned)Q != (unsigned)(Q - 1)) {
+          if (lane == 0)
+            __hip_atomic_store(&tline[1 + q],
+                               ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, my),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;
+        }
+        float s = 0.0f;
+        if (lane == q) {
+          s = my;
+          __hip_atomic_store(&tline[1 + q], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (lane < Q) {
+          uint64_t w = 0;
+          int polls = 0;
+          do {
+            w = __hip_atomic_load(&tline[1 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } while ((uint32_t)(w >> 32) != tag && ++polls < kTicketSpins);
+          s = (uint32_t)(w >> 32) == tag ? __builtin_bit_cast(float, (uint32_t)w)
+                                         : __builtin_nanf("");
+        }
+        s = wave_sum(s);
+        if (lane == 0) c[lo] = to_bits<DT>(finish<DT>(s, flags, alpha, bias, lo));
+        return;
+      }
       __builtin_amdgcn_s_waitcnt(0);
       unsigned old = 0;
       if (lane == 0)
