@@ -167,3 +167,50 @@ def test_stress_split_and_lds_variants_repeatable():
             assert np.array_equal(to_bits(c), first), (n, k, v)
             g.force_config(-1)
     g.close()
+
+
+@pytest.mark.parametrize("grid", [0, 3], ids=["ticketed", "counted"])
+def test_racing_calls_leave_the_workspace_usable(grid):
+    """Calls that overlap on one workspace race: their c is undefined (and
+    may be NaN where a ticketed combiner found a partial missing and gave up
+    after its bounded polls).  Once they have completed, the workspace must
+    serve the next call exactly: 64 x 65536 bf16 split across 8 workgroups
+    per row, the ticketed combine (one row per workgroup, the automatic
+    plan's grid) and the counted one (a grid of 3 row ranges), raced from
+    two streams on one workspace with different inputs, then run quietly
+    and compared bit for bit with the same call on a fresh workspace."""
+    n, k, dtype = 64, 65536, BF16
+    g = mbd.Gemv(workspace=True)
+    v, _, q = g.query_config(n, k, dtype)
+    assert mbd.gemv_variant_info(v)[1].cross_wg and q > 1
+    (B1, a1), (B2, a2) = [random_inputs(n, k, dtype, seed=300 + i) for i in range(2)]
+    B1d, a1d, B2d, a2d = (to_device(x, dtype) for x in (B1, a1, B2, a2))
+    fresh = torch.zeros(mbd._lib.GEMV_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    c1 = torch.empty(n, dtype=B1d.dtype, device="cuda")
+    c2 = torch.empty(n, dtype=B1d.dtype, device="cuda")
+    ref = torch.empty(n, dtype=B1d.dtype, device="cuda")
+
+    def call(Bd, ad, c, ws, stream):
+        st = mbd.gemv_run_ws(g.h, Bd.data_ptr(), ad.data_ptr(), c.data_ptr(), n, k, mbd.GEMV_BF16,
+                             ws.data_ptr(), ws.numel(), stream=stream)
+        assert st == mbd.GEMV_OK
+
+    g.force_config(v, grid, q)
+    try:
+        torch.cuda.synchronize()
+        call(B1d, a1d, ref, fresh, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        want = to_bits(ref)
+        for _ in range(4):
+            call(B1d, a1d, c1, g.ws, s1.cuda_stream)
+            call(B2d, a2d, c2, g.ws, s2.cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            c1.fill_(float("nan"))
+            call(B1d, a1d, c1, g.ws, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(c1), want)
+    finally:
+        g.force_config(-1)
+    g.close()
