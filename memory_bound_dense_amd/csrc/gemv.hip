@@ -157,6 +157,7 @@ using mbd::kWsCounterBytes;
 using mbd::kWsFloats;
 using mbd::kXwgMaxQ;
 using mbd::kXwgRanges;
+constexpr int64_t kTicketMaxWorkgroups = 512;
 static_assert(kWsCounterBytes + kWsFloats * sizeof(float) + mbd::kWsTicketBytes ==
                   (size_t)GEMV_WORKSPACE_BYTES,
               "the header's workspace size is the layout's");
@@ -288,29 +289,43 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // 2. k split over Q workgroups as well, for few rows of many steps -- only
   // with caller scratch for the partials and counters (gemv_run_ws);
-  // without it, the in-workgroup split below.  Up to 96 rows: one row per
-  // 8-wave workgroup, eight slices of two steps per wave (one batch of two
-  // load slots), Q = steps / 16 workgroups per row.  97..192 rows, or up to
-  // 256 rows of >= 256 steps: four rows per 4-wave workgroup, each wave one
-  // row's share of k, Q = steps / 8 (eight steps, two batches of four, per
-  // wave).  Q at most 64.  (Graph replay, every cross-workgroup variant x
-  // Q = 2..64 and the in-workgroup plans: 1.9% off the best compiled plan on
-  // average over 45 shapes of n = 1..256, k = 32K..256K, 10% at worst; 2.8%
-  // and 9.3% on 27 shapes outside that fit, n = 2..224, k = 96K..512K.  The
-  // combine's counters and partials sit in lines of their own, so many
-  // workgroups per row do not queue on shared lines; packed, the best Q was
-  // 4..8 and the 16-wave split, at 2.0% on average over the fit's range.)
+  // without it, the in-workgroup split below.  Grids of about 512
+  // workgroups (two per CU) measured best, and up to 512 the ticketed
+  // combine (one row per workgroup of one row group) takes two round trips
+  // off the combine.  So, two steps per wave at most 512 workgroups where
+  // that fits: up to 64 rows, one row per 4-wave workgroup, Q = steps / 8,
+  // if n Q <= 512; else one row per 8-wave workgroup, Q = 512 / n (at most
+  // steps / 16), two load slots per wave, four when a wave has four steps or
+  // more.  65..96 rows: four rows per 4-wave workgroup, each wave one row's
+  // share of k, Q = 2048 / n (512 workgroups; at most steps / 8).  97..192
+  // rows, and up to 256 rows of >= 256 steps: the same shape, Q = steps / 8.
+  // Q at most 64.  (Graph replay, every cross-workgroup variant x Q and the
+  // in-workgroup plans: 2.7% off the best compiled plan on average over 22
+  // shapes of 1..96 rows, 7.4% at worst; 2.5% and 5.9% over 11 shapes of
+  // 128..256 rows.  The combine's counters and partials sit in lines of
+  // their own, so many workgroups per row do not queue on shared lines.)
   if (with_ws && nfull0 >= 128 && n <= 256) {
-    if (n <= 96) {
-      int64_t Q = nfull0 / 16;
+    auto fits = [&](int64_t Q) { return n * mbd::xwg_row_stride(Q) <= (int64_t)kWsFloats; };
+    if (n <= 64) {
+      int64_t Q = nfull0 / 8;
       if (Q > kXwgMaxQ) Q = kXwgMaxQ;
-      if (n * mbd::xwg_row_stride(Q) <= (int64_t)kWsFloats)
-        return Plan{1, 2, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
+      if (n * Q <= kTicketMaxWorkgroups && fits(Q)) return Plan{1, 2, 4, 4, mbd::A_CACHED, kPolNT, 0, (int)Q};
+      Q = nfull0 / 16;
+      if (Q > kXwgMaxQ) Q = kXwgMaxQ;
+      if (Q > kTicketMaxWorkgroups / n) Q = kTicketMaxWorkgroups / n;
+      if (Q < 2) Q = 2;
+      const int U = nfull0 / (Q * 8) >= 4 ? 4 : 2;
+      if (fits(Q)) return Plan{1, U, 8, 8, mbd::A_CACHED, kPolNT, 0, (int)Q};
+    } else if (n <= 96) {
+      int64_t Q = nfull0 / 8;
+      if (Q > kXwgMaxQ) Q = kXwgMaxQ;
+      if (Q > 4 * kTicketMaxWorkgroups / n) Q = 4 * kTicketMaxWorkgroups / n;
+      if (Q < 2) Q = 2;
+      if (fits(Q)) return Plan{1, 4, 4, 1, mbd::A_CACHED, kPolNT, 0, (int)Q};
     } else if (n <= 192 || nfull0 >= 256) {
       int64_t Q = nfull0 / 8;
       if (Q > kXwgMaxQ) Q = kXwgMaxQ;
-      if (n * mbd::xwg_row_stride(Q) <= (int64_t)kWsFloats)
-        return Plan{1, 4, 4, 1, mbd::A_CACHED, kPolNT, 0, (int)Q};
+      if (fits(Q)) return Plan{1, 4, 4, 1, mbd::A_CACHED, kPolNT, 0, (int)Q};
     }
   }
   if (n < 128 && nfull0 >= 32) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
@@ -741,10 +756,14 @@ extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void*
   p.k = (int)k;
   p.flags = L.flags | (ep ? mbd::kFlagEpilogue : 0);
   // One row per workgroup of one row group, as the automatic plan's split of
-  // up to 96 rows has it: the ticketed combine, on its own bank of the
-  // scratch (pointed to by ws; the kernel takes its row lines from there).
+  // up to 96 rows has it, and at most 512 workgroups: the ticketed combine,
+  // on its own bank of the scratch (pointed to by ws; the kernel takes its
+  // row lines from there).  With more workgroups than that the combiners
+  // that wait hold places that workgroups of other rows are queued for: on
+  // MI355X the ticketed combine was 2-9% faster up to 384 workgroups, even at
+  // 512-768 and 7-14% slower from 1024.
   if (workspace && vi.cross_wg && vi.rows == 1 && vi.waves == vi.splits && L.grid == n &&
-      n <= mbd::kTicketRows) {
+      n <= mbd::kTicketRows && (int64_t)L.grid * L.kgroups <= kTicketMaxWorkgroups) {
     p.ws = (float*)((char*)workspace + kWsCounterBytes + kWsFloats * sizeof(float) +
                     mbd::ticket_bank_offset(L.kgroups));
     p.flags |= mbd::kFlagTicket;

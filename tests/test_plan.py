@@ -363,25 +363,34 @@ def test_plan_cross_workgroup_only_for_few_rows(n, k, xwg):
     assert (cfg.kgroups > 1) == xwg
     if xwg:
         nfull = k // 512
-        if n <= 96:
-            # one row per 8-wave workgroup, two steps per wave
-            assert shape_of(info) == (1, 2, 8, 8, 1, 1)
-            assert cfg.kgroups == min(64, nfull // 16)
-            assert cfg.grid == n
+        q = cfg.kgroups
+        assert 2 <= q <= 64
+        if n <= 64 and n * min(64, nfull // 8) <= 512:
+            # one row per 4-wave workgroup, two steps per wave, at most 512
+            # workgroups (the ticketed combine's grid)
+            assert shape_of(info) == (1, 2, 4, 4, 1, 1)
+            assert q == min(64, nfull // 8) and cfg.grid == n
+        elif n <= 64:
+            # one row per 8-wave workgroup, about 512 workgroups
+            assert q == max(2, min(64, nfull // 16, 512 // n)) and cfg.grid == n
+            assert shape_of(info) == (1, 4 if nfull // (q * 8) >= 4 else 2, 8, 8, 1, 1)
         else:
-            # four rows per 4-wave workgroup, eight steps per wave
+            # four rows per 4-wave workgroup, each wave one row's share
             assert shape_of(info) == (1, 4, 4, 1, 1, 1)
-            assert cfg.kgroups == min(64, nfull // 8)
+            assert q == (max(2, min(64, nfull // 8, 2048 // n)) if n <= 96 else min(64, nfull // 8))
             assert cfg.grid == (n + 3) // 4
 
 
 @pytest.mark.parametrize("n,k,q", [
-    (64, 65536, 8),      # 128 steps: 8 workgroups of 8 waves x 2 steps per row
-    (1, 65536, 8),
-    (96, 131072, 16),
-    (16, 262144, 32),
-    (8, 1048576, 64),    # 2048 steps would take 128 workgroups of 16: the cap
-    (97, 65536, 16),     # four rows per workgroup from 97 rows, 8 steps per wave
+    (64, 65536, 8),      # 64 x 16 four-wave workgroups would be 1024: 8 eight-wave ones a row
+    (1, 65536, 16),      # 128 steps, two a wave over four waves: 16 workgroups
+    (32, 65536, 16),     # 512 four-wave workgroups
+    (33, 65536, 8),      # 528 would exceed 512: 8-wave workgroups, 512 // 33 = 15 > 128 / 16
+    (48, 262144, 10),    # 512 // 48 = 10 eight-wave workgroups a row
+    (16, 262144, 32),    # 16 x 64 = 1024: 8-wave, min(512 / 16, 32) = 32
+    (8, 1048576, 64),    # 8 x 64 = 512 four-wave workgroups
+    (80, 131072, 25),    # four rows a workgroup: 2048 // 80 = 25 (20 x 25 = 500 workgroups)
+    (97, 65536, 16),     # from 97 rows, steps / 8
     (256, 262144, 64),
 ])
 def test_plan_cross_workgroup_q(n, k, q):
