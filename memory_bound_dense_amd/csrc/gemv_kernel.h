@@ -529,7 +529,6 @@ __global__ __launch_bounds__(WAVES * kLanes) void gemv_kernel(
     }
   }
 
-
   draw_ticket();   // (drawn above already on the one-row paths that take it)
 
   if constexpr (XWG) {
