@@ -460,7 +460,8 @@ def test_cross_workgroup_split(g, n, k, dtype):
 
 
 AUTO_XWG_SHAPES = [(96, 131072, BF16), (100, 65544, F16), (129, 262152, BF16), (200, 262144, F16),
-                   (16, 262144, BF16), (48, 131075, F16), (3, 1048576, BF16), (194, 131073, F16)]
+                   (16, 262144, BF16), (48, 131075, F16), (3, 1048576, BF16), (194, 131073, F16),
+                   (40, 262147, F16), (8, 131072, BF16), (72, 131072, F16)]
 
 
 @pytest.mark.parametrize("n,k,dtype", AUTO_XWG_SHAPES,
