@@ -487,6 +487,28 @@ def test_auto_plan_cross_workgroup_rows(g, n, k, dtype):
     assert np.array_equal(goti, refi)
 
 
+@pytest.mark.parametrize("n,k,dtype", [(64, 65536, BF16), (7, 100003, F16), (33, 70000, BF16)],
+                         ids=["64x65536_bf16", "7x100003_f16", "33x70000_bf16"])
+def test_ticketed_and_counted_combines_agree_bitwise(g, n, k, dtype):
+    """With one row per workgroup (and at most 512 workgroups) the split
+    combines by tickets, with fewer row ranges by counting arrivals; both sum
+    a row's k-group partials in the same fixed lane order, so for the same
+    variant and k-groups c must have the same bits, on random data."""
+    B, a = random_inputs(n, k, dtype, "normal", seed=41)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    xwg1 = [v for v in XWG if mbd.gemv_variant_info(v)[1].waves == mbd.gemv_variant_info(v)[1].splits
+            and mbd.gemv_variant_info(v)[1].rows == 1]
+    assert xwg1
+    for v in xwg1:
+        for q in (2, 5, 8):
+            if n * q > 512:
+                continue
+            ticketed = run(g, Bd, ad, v, 0, q)        # grid n: one row per workgroup
+            counted = run(g, Bd, ad, v, 3, q)         # three row ranges
+            assert ticketed is not None and counted is not None
+            assert np.array_equal(ticketed, counted), (v, q)
+
+
 def test_cross_workgroup_config_rules(g):
     nonx = [v for v in VARIANTS if not mbd.gemv_variant_info(v)[1].cross_wg][0]
     with pytest.raises(mbd.GemvError):
