@@ -549,6 +549,10 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    # bytes moved per output row: the algorithmic 2k + 2 (+ a's share, 2k / n)
+    # against the counted HBM bytes, when a counter summary applies
+    out["bytes_per_output"] = {"algorithmic": round(step_bytes / n, 2),
+                               "counted": None if traffic is None else round(traffic / n, 2)}
     if ceiling:
         out["stream_read_probe"] = ceiling
     if access:

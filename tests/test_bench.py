@@ -46,6 +46,8 @@ def test_json_line_graph_with_cpu_baseline():
     assert 0 < rf["frac"] < 1.2 and abs(rf["achieved"] / rf["peak"] - rf["frac"]) < 1e-3
     cb = out["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
+    # 2k + 2 bytes per row, plus a's 2k bytes shared over the n rows
+    assert out["bytes_per_output"]["algorithmic"] == round(2 * (256 * 512 + 512 + 256) / 256, 2)
 
 
 @pytest.mark.gpu
