@@ -248,7 +248,8 @@ typedef struct {
 /* Workgroups are dispatched round-robin over the GPU's 8 XCDs.  With this
  * flag the row ranges are renumbered so that the workgroups of one XCD own
  * one contiguous block of rows (measured: no gain for the automatic plans,
- * a gain for some persistent grids). */
+ * a gain for some persistent grids).  Variants with cross_wg ignore it: their
+ * k-groups are what is dealt over the XCDs. */
 #define GEMV_FLAG_XCD_CONTIGUOUS 1
 
 /* Number of compiled variants. */

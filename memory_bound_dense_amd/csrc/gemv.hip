@@ -115,6 +115,11 @@ const Variant kVariants[] = {
     // 72..73: two-slot batches over four slices, one or two rows per wave
     // (the plans of 513..895 rows of long rows)
     MBD_VARIANT(1, 2, 4, 4, CCH, NT), MBD_VARIANT(2, 2, 4, 4, CCH, NT),
+    // 74..78: two rows per wave, batches of 3, 5 or 6 steps over four or
+    // eight slices
+    MBD_VARIANT(2, 3, 8, 8, CCH, NT), MBD_VARIANT(2, 6, 8, 8, CCH, NT),
+    MBD_VARIANT(2, 5, 4, 4, CCH, NT), MBD_VARIANT(2, 3, 4, 4, CCH, NT),
+    MBD_VARIANT(2, 5, 8, 8, CCH, NT),
 };
 #undef NT
 #undef LDS
@@ -338,20 +343,18 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // very long rows (k >= 48K) and enough of them: no split, two rows per
   // one-wave workgroup (the split's per-slice combine no longer pays)
   if (nfull >= 96 && n >= 1536) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  // rows of 18..24 whole steps (no partial step) on 1536..2560 rows: no
-  // split, one row per wave in two-wave workgroups; fp16 ones of 20..24 whole
-  // steps on 3072..6144 rows: no split, two rows per one-wave workgroup.
-  // (Graph replay over 170 aligned shapes, n = 1536..8192, k = 8704..16384
-  // with and without a partial step, fp16 and bf16: with the split below
-  // alone 1.7% off the best compiled plan on average, 11.8% at worst.  With
-  // a partial step the unsplit plans lost up to 17%, at k = 11008 on every
-  // row count, so they take whole steps only.  From 25 steps the plan of
-  // eight-slot batches over four slices below is as good or better.)
-  if (k % mbd::kStep == 0 && nfull >= 18 && nfull <= 24 && n >= 1536 && n <= 2560)
+  // rows of 12 or 18..24 whole steps (no partial step) on 1536..2560 rows:
+  // no split, one row per wave in two-wave workgroups.  (Graph replay over
+  // aligned shapes of n = 1536..8192, k = 6144..16384 with and without a
+  // partial step, fp16 and bf16: with the split plans below alone 1.2% off
+  // the best compiled plan on average at 2048 rows of 18..24 steps against
+  // 1.1% unsplit, and 3-5% behind at 12 steps; from 3072 rows the split
+  // plans are as good or better.  With a partial step the unsplit plans lost
+  // up to 17%, at k = 11008 on every row count, so they take whole steps
+  // only.)
+  if (k % mbd::kStep == 0 && (nfull == 12 || (nfull >= 18 && nfull <= 24)) && n >= 1536 &&
+      n <= 2560)
     return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  if (dtype == GEMV_F16 && k % mbd::kStep == 0 && nfull >= 20 && nfull <= 24 && n >= 3072 &&
-      n <= 6144)
-    return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
   const int64_t nsteps = nfull + (k % mbd::kStep != 0 ? 1 : 0);
   // fewer than 896 rows of at least 20 steps: what balances the workgroups
   // over the CUs.  513..831 rows: one row per wave, four slices of two-slot
@@ -383,26 +386,44 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // two rows per wave: one row group per workgroup (S waves; measured 0.4-5%
   // faster than two row groups of 8 waves at S = 4 on MI355X, the headline
   // (18432, 7168) fp16 among them)
-  // fp16 rows of 32 full steps, two rows per wave: four slices of two
-  // batches, two row groups per 8-wave workgroup (graph replay, n = 1024 to
-  // 28672, k = 16384: the best compiled plan or within 0.8%, where eight
-  // slices were 0.8-7% behind; not so for bf16, nor for 36 steps)
-  if (dtype == GEMV_F16 && R == 2 && nfull == 32 && n >= 896)
-    return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
-  // Two rows per wave, by the rows' steps (nsteps, the partial one
-  // included): give each k-slice a share that fills its batch of loads.
-  // A batch slot costs registers whether it is used or not (two rows x
-  // U = 2 / 4 / 8 take 55 / 73 / 121 VGPRs: 8 / 6 / 4 waves per SIMD), so a
-  // large batch pays only when the share fills it: eight slots for shares of
-  // 7-8 steps (25..28 steps over four slices, 49..64 over eight), four for
-  // shares of 3-4 (the rule above: 21..24 and 29..34 steps over eight), and
-  // two -- several batches, at full occupancy -- for the shares in between
-  // (15..20 steps, 35..48, 65..80; fp16 keeps four slices of four up to 16
-  // steps).  (Graph-replayed sweeps over 356 two-row shapes, n = 1024..18432,
-  // k = 6144..40960, fp16 and bf16, 16-20 candidate plans each: 1.1% off the
-  // best compiled plan on average, 3.2% at the 90th percentile, where the
-  // rule above alone was 2.9% and 7.7%, and up to 19% at 40 steps, whose
-  // shares of 5 left the second batch of four nearly empty.)
+  // Two rows per wave on at least 896 rows of 12..64 steps (nsteps, the
+  // partial one included): the k-slices S and the batch U, by the steps.
+  // The principle is one batch of loads per slice, U = the slice's share --
+  // a batch slot costs registers whether it is used or not (two rows x U = 2
+  // / 3 / 4 / 5 / 6 / 8 take 55 / 61 / 73 / 80 / 97 / 121 VGPRs for bf16: 8 /
+  // 8 / 6 / 6 / 4 / 4 waves per SIMD) -- with the measured exceptions the
+  // table keeps: 25..26 and 43..48 steps take batches of three over eight
+  // slices (two batches), 31 steps two-slot batches over four, 14 steps on
+  // fewer than 4096 rows eight slices of two, 32 steps two row groups of
+  // four slices in fp16.  (Graph-replayed sweeps over 266 shapes, n = 1024
+  // .. 16384, k = 6144..32768 with and without a partial step, fp16 and
+  // bf16, 16 candidate plans each: 0.5% off the best compiled plan on
+  // average, 1.7% at the 90th percentile, 4.7% at worst, where the previous
+  // rule, with batches of 2, 4 and 8 only, was 1.7%, 3.7% and 17%.)
+  if (R == 2 && n >= 896 && nsteps >= 12 && nsteps <= 64) {
+    // {U, S} for nsteps = 12 + i
+    static constexpr signed char kTwoRow[53][2] = {
+        {3, 4}, {4, 4}, {4, 4}, {2, 8}, {3, 8},                   // 12..16
+        {5, 4}, {5, 4}, {5, 4}, {5, 4},                           // 17..20
+        {3, 8}, {3, 8}, {3, 8}, {3, 8}, {3, 8}, {3, 8},           // 21..26
+        {8, 4}, {8, 4}, {8, 4}, {4, 8}, {2, 4}, {4, 8},           // 27..32
+        {4, 8}, {4, 8},                                           // 33..34
+        {5, 8}, {5, 8}, {5, 8}, {5, 8}, {5, 8}, {5, 8},           // 35..40
+        {6, 8}, {6, 8},                                           // 41..42
+        {3, 8}, {3, 8}, {3, 8}, {3, 8}, {3, 8}, {3, 8},           // 43..48
+        {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8},   // 49..56
+        {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}};  // 57..64
+    int U = kTwoRow[nsteps - 12][0], Sl = kTwoRow[nsteps - 12][1];
+    if (nsteps == 14 && n < 4096) U = 2, Sl = 8;
+    if (nsteps == 32 && dtype == GEMV_F16) return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
+    return Plan{2, U, Sl, Sl, mbd::A_CACHED, kPolNT, 0, 1};
+  }
+  // Two rows per wave otherwise (320..895 rows, or more than 64 steps): give
+  // each k-slice a share that fills its batch of loads -- eight slots for
+  // shares of 7-8 steps (25..28 steps over four slices, 49..64 over eight),
+  // four for shares of 3-4 (21..24 and 29..34 steps over eight), and two --
+  // several batches, at full occupancy -- for the shares in between (15..20
+  // steps, 35..48, 65..80; fp16 keeps four slices of four up to 16 steps).
   if (R == 2 && nsteps >= 15 && nsteps <= 80 && !(dtype == GEMV_F16 && nsteps <= 16)) {
     auto two = [](int U, int Sl) { return Plan{2, U, Sl, Sl, mbd::A_CACHED, kPolNT, 0, 1}; };
     if (nsteps <= 20) return two(2, 8);
@@ -791,7 +812,10 @@ extern "C" gemv_status_t gemv_run_ws(gemv_handle_t h, const void* B, const void*
                   (void*)&p.k,       (void*)&p.flags,   (void*)&p.rows_q,  (void*)&p.rows_r,
                   (void*)&p.slice_q, (void*)&p.slice_r, (void*)&p.alpha,   (void*)&p.bias,
                   (void*)&p.ws,      (void*)&p.cnt};
-  hipError_t e = hipLaunchKernel((const void*)var.fn[dtype], dim3((unsigned)L.grid, (unsigned)L.kgroups),
+  // the cross-workgroup split's grid is (k-groups, row ranges)
+  hipError_t e = hipLaunchKernel((const void*)var.fn[dtype],
+                                 vi.cross_wg ? dim3((unsigned)L.kgroups, (unsigned)L.grid)
+                                             : dim3((unsigned)L.grid),
                                  dim3((unsigned)(var.info.waves * mbd::kLanes)), args, L.lds, stream);
   if (e != hipSuccess) return report(h, GEMV_ERR_HIP, hipGetErrorString(e));
   return GEMV_OK;

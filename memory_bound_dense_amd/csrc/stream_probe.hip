@@ -203,7 +203,9 @@ extern "C" int mbd_gemv_probe(int rows, int unroll, int waves, int splits, int x
                   (void*)&slice_q, (void*)&slice_r, (void*)&alpha,   (void*)&bias,
                   (void*)&ws,      (void*)&cnt};
   const size_t lds = splits > 1 ? (size_t)waves * rows * sizeof(float) : 0;
-  hipError_t e = hipLaunchKernel((const void*)ps->fn, dim3((unsigned)grid, (unsigned)kgroups),
+  // the cross-workgroup split's grid is (k-groups, row ranges), as gemv_run_ws launches it
+  hipError_t e = hipLaunchKernel((const void*)ps->fn, xwg ? dim3((unsigned)kgroups, (unsigned)grid)
+                                                          : dim3((unsigned)grid),
                                  dim3((unsigned)(waves * mbd::kLanes)), args, lds, stream);
   return e == hipSuccess ? 0 : -2;
 }

@@ -44,17 +44,17 @@ WORKLOAD_PLANS = {
     "sweep_4096x4096_bf16": (1, 8, 4, 1, 1, 0),
     "sweep_11008x4096_f16": (1, 8, 4, 1, 1, 0),
     "sweep_11008x4096_bf16": (1, 8, 4, 1, 1, 0),
-    "sweep_4096x11008_f16": (2, 4, 8, 8, 1, 0),
-    "sweep_4096x11008_bf16": (2, 4, 8, 8, 1, 0),
+    "sweep_4096x11008_f16": (2, 3, 8, 8, 1, 0),
+    "sweep_4096x11008_bf16": (2, 3, 8, 8, 1, 0),
     "sweep_14336x4096_f16": (1, 8, 4, 1, 1, 0),
     "sweep_14336x4096_bf16": (1, 8, 4, 1, 1, 0),
     "sweep_4096x14336_f16": (2, 8, 4, 4, 1, 0),
     "sweep_4096x14336_bf16": (2, 8, 4, 4, 1, 0),
     "ragged_64x65536_bf16": (1, 2, 8, 8, 1, 1),
-    "ragged_1000x7000_bf16": (2, 4, 4, 4, 1, 0),
+    "ragged_1000x7000_bf16": (2, 2, 8, 8, 1, 0),
     "ragged_18433x7169_bf16": (2, 4, 4, 4, 3, 0),
-    "large_28672x8192_f16": (2, 4, 4, 4, 1, 0),
-    "large_28672x8192_bf16": (2, 2, 8, 8, 1, 0),
+    "large_28672x8192_f16": (2, 3, 8, 8, 1, 0),
+    "large_28672x8192_bf16": (2, 3, 8, 8, 1, 0),
     "large_57344x7168_f16": (2, 4, 4, 4, 1, 0),
     "large_57344x7168_bf16": (2, 4, 4, 4, 1, 0),
     "square_1024x1024_f16": (1, 2, 4, 1, 1, 0),
@@ -217,7 +217,7 @@ def test_plan_shifted_window_only_for_misaligned_rows():
     (768, 8192, (1, 4, 4, 4, 1, 0)),       # <= 768 rows of 9..16 steps: 4 slices, 4 waves
     (256, 5120, (1, 4, 4, 4, 1, 0)),
     (800, 8192, (1, 4, 8, 4, 1, 0)),       # more rows: the general split
-    (1000, 8192, (2, 4, 8, 8, 1, 0)),      # n >= 896, k >= 6144: two rows per wave
+    (1000, 8192, (2, 3, 8, 8, 1, 0)),      # n >= 896, k >= 6144: two rows per wave
     (768, 4096, (1, 8, 4, 1, 1, 0)),       # <= 8 steps: one wave per row
     (1024, 1024, (1, 2, 4, 1, 1, 0)),      # 1-2 steps: two load slots
     (256, 512, (1, 2, 4, 1, 1, 0)),
@@ -244,64 +244,75 @@ def test_plan_bf16_short_rows(n, k, want):
     (1024, 16384, F16, (2, 4, 8, 4, 1, 0)),
     (28672, 16384, F16, (2, 4, 8, 4, 1, 0)),
     (7168, 16384, BF16, (2, 4, 8, 8, 1, 0)),    # bf16: eight
-    (7168, 18432, F16, (2, 2, 8, 8, 1, 0)),     # 36 steps: eight slices of two-slot batches
+    (7168, 18432, F16, (2, 5, 8, 8, 1, 0)),     # 36 steps: eight slices of five-slot batches
 ])
 def test_plan_rows_of_32_steps(n, k, dtype, want):
     assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
 
 
 @pytest.mark.parametrize("n,k,dtype,want", [
-    # 18..24 whole steps on 1536..2560 rows: one row per two-wave workgroup
+    # 12 or 18..24 whole steps on 1536..2560 rows: one row per two-wave workgroup
     (1536, 9216, F16, (1, 4, 2, 1, 1, 0)),
     (2048, 12288, BF16, (1, 4, 2, 1, 1, 0)),
     (2560, 10240, BF16, (1, 4, 2, 1, 1, 0)),
-    # fp16, 20..24 whole steps on 3072..6144 rows: two rows per one-wave
-    # workgroup; bf16 there keeps the split
-    (4096, 12288, F16, (2, 4, 1, 1, 1, 0)),
-    (6144, 10240, F16, (2, 4, 1, 1, 1, 0)),
-    (4096, 12288, BF16, (2, 4, 8, 8, 1, 0)),
-    # a partial last step, more steps, or outside those bounds: the split
-    (2048, 11008, BF16, (2, 4, 8, 8, 1, 0)),
-    (4096, 11008, F16, (2, 4, 8, 8, 1, 0)),
+    (2048, 6144, F16, (1, 4, 2, 1, 1, 0)),
+    # a partial last step, other step counts, or outside those bounds: the
+    # two-row table
+    (2048, 11008, BF16, (2, 3, 8, 8, 1, 0)),
+    (2048, 6656, BF16, (2, 4, 4, 4, 1, 0)),
     (2048, 14336, BF16, (2, 8, 4, 4, 1, 0)),
-    (4096, 14336, F16, (2, 8, 4, 4, 1, 0)),
-    (1024, 12288, BF16, (2, 4, 8, 8, 1, 0)),
-    (8192, 12288, F16, (2, 4, 8, 8, 1, 0)),
-    (3072, 9216, F16, (2, 2, 8, 8, 1, 0)),
+    (4096, 12288, F16, (2, 3, 8, 8, 1, 0)),
+    (6144, 10240, F16, (2, 5, 4, 4, 1, 0)),
+    (1024, 12288, BF16, (2, 3, 8, 8, 1, 0)),
+    (3072, 9216, F16, (2, 5, 4, 4, 1, 0)),
 ])
 def test_plan_whole_step_rows_unsplit(n, k, dtype, want):
     assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
 
 
 @pytest.mark.parametrize("k,dtype,want", [
-    # two rows per wave: each k-slice's share fills its batch of loads
-    (6656, BF16, (2, 4, 4, 4)),      # 13 steps: four slices of one batch of four
-    (7168, BF16, (2, 4, 4, 4)),      # 14
-    (7680, BF16, (2, 2, 8, 8)),      # 15..20: eight slices, two-slot batches
-    (7680, F16, (2, 4, 4, 4)),       # fp16 keeps four slices of four to 16 steps
-    (8192, F16, (2, 4, 4, 4)),
-    (8704, F16, (2, 2, 8, 8)),
-    (10240, BF16, (2, 2, 8, 8)),
-    (10248, BF16, (2, 4, 8, 8)),     # 21..24 (a partial 21st step counts): shares of 3
-    (12288, BF16, (2, 4, 8, 8)),
-    (12296, BF16, (2, 8, 4, 4)),     # 25..28: four slices of seven, eight-slot batches
-    (14336, F16, (2, 8, 4, 4)),
-    (14344, BF16, (2, 4, 8, 8)),     # 29..34: eight slices of four
-    (17408, BF16, (2, 4, 8, 8)),
-    (17416, BF16, (2, 2, 8, 8)),     # 35..48: eight slices, two-slot batches
-    (24576, F16, (2, 2, 8, 8)),
+    # two rows per wave on >= 896 rows of 12..64 steps (a partial step
+    # counts): (rows, batch, waves, slices) from the measured table
+    (6144, BF16, (2, 3, 4, 4)),      # 12 steps: four slices, batches of three
+    (6656, BF16, (2, 4, 4, 4)),      # 13
+    (7680, F16, (2, 2, 8, 8)),       # 15: eight slices of two
+    (8192, BF16, (2, 3, 8, 8)),      # 16: eight slices, batches of three
+    (8200, F16, (2, 5, 4, 4)),       # 17..20: four slices, batches of five
+    (10240, BF16, (2, 5, 4, 4)),
+    (10248, BF16, (2, 3, 8, 8)),     # 21..26: eight slices, batches of three
+    (13312, F16, (2, 3, 8, 8)),
+    (13320, BF16, (2, 8, 4, 4)),     # 27..29: four slices, eight-slot batches
+    (14848, F16, (2, 8, 4, 4)),
+    (15360, BF16, (2, 4, 8, 8)),     # 30: eight slices of four
+    (15872, BF16, (2, 2, 4, 4)),     # 31: four slices, two-slot batches
+    (16384, BF16, (2, 4, 8, 8)),     # 32 (bf16)
+    (16384, F16, (2, 4, 8, 4)),      # 32 (fp16): two row groups of four slices
+    (17408, BF16, (2, 4, 8, 8)),     # 33..34
+    (17416, BF16, (2, 5, 8, 8)),     # 35..40: eight slices, batches of five
+    (20480, F16, (2, 5, 8, 8)),
+    (21504, BF16, (2, 6, 8, 8)),     # 41..42: batches of six
+    (21512, F16, (2, 3, 8, 8)),      # 43..48: batches of three (two per slice)
+    (24576, BF16, (2, 3, 8, 8)),
     (24584, BF16, (2, 8, 8, 8)),     # 49..64: eight slices of seven or eight
-    (32768, BF16, (2, 8, 8, 8)),
-    (32776, F16, (2, 2, 8, 8)),      # 65..80
+    (32768, F16, (2, 8, 8, 8)),
+    (32776, F16, (2, 2, 8, 8)),      # 65..80: two-slot batches
     (40960, BF16, (2, 2, 8, 8)),
     (40968, BF16, (2, 4, 8, 8)),     # beyond: the general split
 ])
-def test_plan_batch_filling_bands(k, dtype, want):
+def test_plan_two_row_table(k, dtype, want):
     assert k % 8 == 0                     # aligned rows (misaligned ones: tier 0)
-    for n in (896, 1000, 8192, 18432):
-        if n < 1024 and dtype == F16 and k <= 8192:
-            continue                          # there the general split goes deeper
+    for n in (896, 1000, 3072, 4096, 8192, 18432):
         assert shape_of(plan(n, k, dtype)[1]) == want + (1, 0), (n, k, dtype)
+
+
+def test_plan_two_row_table_14_steps():
+    # 14 steps: four slices of four from 4096 rows, eight slices of two below
+    for k in (7168, 7000):
+        for dtype in (F16, BF16):
+            for n in (896, 1000, 2048, 4095):
+                assert shape_of(plan(n, k, dtype)[1]) == (2, 2, 8, 8, 1, 0), (n, k, dtype)
+            for n in (4096, 18432, 57344):
+                assert shape_of(plan(n, k, dtype)[1]) == (2, 4, 4, 4, 1, 0), (n, k, dtype)
 
 
 @pytest.mark.parametrize("n,k,dtype,want", [
@@ -323,7 +334,7 @@ def test_plan_batch_filling_bands(k, dtype, want):
     (895, 12288, F16, (2, 2, 4, 4, 1, 0)),
     # outside: 896 rows and more take the two-row bands, fewer than 320 rows
     # or rows of fewer than 20 steps the one-row rule
-    (896, 20480, BF16, (2, 2, 8, 8, 1, 0)),
+    (896, 20480, BF16, (2, 5, 8, 8, 1, 0)),
     (256, 20480, BF16, (1, 4, 16, 16, 1, 0)),
     (512, 8192, BF16, (1, 4, 4, 4, 1, 0)),
     (700, 9216, F16, (1, 4, 8, 8, 1, 0)),
