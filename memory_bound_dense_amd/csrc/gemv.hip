@@ -120,6 +120,9 @@ const Variant kVariants[] = {
     MBD_VARIANT(2, 3, 8, 8, CCH, NT), MBD_VARIANT(2, 6, 8, 8, CCH, NT),
     MBD_VARIANT(2, 5, 4, 4, CCH, NT), MBD_VARIANT(2, 3, 4, 4, CCH, NT),
     MBD_VARIANT(2, 5, 8, 8, CCH, NT),
+    // 79..80: three rows per wave, eight slices of two- or three-slot batches
+    // (rows that start off 128-byte lines)
+    MBD_VARIANT(3, 2, 8, 8, CCH, NT), MBD_VARIANT(3, 3, 8, 8, CCH, NT),
 };
 #undef NT
 #undef LDS
@@ -368,6 +371,41 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   if (n > 512 && n < 896 && nsteps >= 20)
     return n < 832 ? Plan{1, 2, 4, 4, mbd::A_CACHED, kPolNT, 0, 1}
                    : Plan{2, 2, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
+  // Rows that start 16-byte but not 128-byte aligned (k not a multiple of
+  // 64), at least 6144 of them, of 13..48 steps: three rows per wave, eight
+  // k-slices, batches of two (up to 16 steps) or three.  (Graph replay, n =
+  // 6144..32768, k = 7000..20040, fp16 and bf16: the best compiled plan or
+  // within 3.2%, where the two-row plans below were 2-6% behind; on rows
+  // that start on 128-byte lines, and below 6144 rows, three rows per wave
+  // do not pay.)
+  if (k % mbd::kLine != 0 && n >= 6144 && nsteps >= 13 && nsteps <= 48)
+    return Plan{3, nsteps <= 16 ? 2 : 3, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
+  // Short rows (at most 12 steps) on at least 2048 rows: a batch no larger
+  // than the row or the slice needs.  A slot past the wave's steps still
+  // issues its B and a loads (out of range, so no memory access, but
+  // through the address units all the same), which cost up to 70% where
+  // eight-slot batches carried three steps.  1..2 steps: two rows per wave,
+  // two slots (four rows from 16384 rows of one step); 3: two rows, four
+  // slots; 4: one row, four slots; 5..6: two rows over four slices of two
+  // slots; 7..8: one row, eight slots; 9..12: two rows over four slices of
+  // three slots -- three rows over eight slices of two on rows off 128-byte
+  // lines from 6144 rows, one row of four slots below 6144 rows for 11..12.
+  // (Graph replay over 95 shapes, n = 2048..32768, k = 256..6144, fp16 and
+  // bf16: 0.8% off the best compiled plan on average, 2.9% at the 90th
+  // percentile, where the previous rule -- eight slots for every row of at
+  // most 8 steps -- was 12% and 35%, up to 70%.)
+  if (n >= 2048 && nsteps <= 12) {
+    auto pl = [](int R, int U, int W, int S) { return Plan{R, U, W, S, mbd::A_CACHED, kPolNT, 0, 1}; };
+    if (nsteps <= 1) return n >= 16384 ? pl(4, 2, 4, 1) : pl(2, 2, 4, 1);
+    if (nsteps <= 2) return pl(2, 2, 4, 1);
+    if (nsteps <= 3) return pl(2, 4, 4, 1);
+    if (nsteps <= 4) return pl(1, 4, 4, 1);
+    if (nsteps <= 6) return pl(2, 2, 4, 4);
+    if (nsteps <= 8) return pl(1, 8, 4, 1);
+    if (k % mbd::kLine != 0 && n >= 6144) return pl(3, 2, 8, 8);
+    if (nsteps >= 11 && n < 6144) return pl(1, 4, 4, 1);
+    return pl(2, 3, 4, 4);
+  }
   const int R = ((n >= 896 && k >= 6144) || (n >= 320 && n <= 512 && nsteps >= 20)) ? 2 : 1;
   // rows of one or two steps (k <= 1024): two load slots, not more slots
   // that would only be skipped (measured on MI355X under graph replay:
@@ -383,9 +421,6 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   int S = 1;
   while (S < smax && (nfull + S - 1) / S > 4) S *= 2;   // at most 4 steps per wave: one batch
   while (S < smax && ((n + R - 1) / R) * S < 2048 && nfull >= 2 * (2 * S)) S *= 2;
-  // two rows per wave: one row group per workgroup (S waves; measured 0.4-5%
-  // faster than two row groups of 8 waves at S = 4 on MI355X, the headline
-  // (18432, 7168) fp16 among them)
   // Two rows per wave on at least 896 rows of 12..64 steps (nsteps, the
   // partial one included): the k-slices S and the batch U, by the steps.
   // The principle is one batch of loads per slice, U = the slice's share --

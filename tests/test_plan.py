@@ -221,8 +221,8 @@ def test_plan_shifted_window_only_for_misaligned_rows():
     (768, 4096, (1, 8, 4, 1, 1, 0)),       # <= 8 steps: one wave per row
     (1024, 1024, (1, 2, 4, 1, 1, 0)),      # 1-2 steps: two load slots
     (256, 512, (1, 2, 4, 1, 1, 0)),
-    (3000, 1000, (1, 2, 4, 1, 1, 0)),
-    (3000, 1536, (1, 8, 4, 1, 1, 0)),      # 3 steps
+    (3000, 1000, (2, 2, 4, 1, 1, 0)),      # >= 2048 rows: the short-row rule
+    (3000, 1536, (2, 4, 4, 1, 1, 0)),      # 3 steps
     (512, 4096, (1, 4, 4, 4, 1, 0)),       # <= 512 rows of 5..8 steps: 4 slices, 4 waves
     (640, 4096, (1, 8, 4, 1, 1, 0)),
 ])
@@ -277,37 +277,39 @@ def test_plan_whole_step_rows_unsplit(n, k, dtype, want):
     (6656, BF16, (2, 4, 4, 4)),      # 13
     (7680, F16, (2, 2, 8, 8)),       # 15: eight slices of two
     (8192, BF16, (2, 3, 8, 8)),      # 16: eight slices, batches of three
-    (8200, F16, (2, 5, 4, 4)),       # 17..20: four slices, batches of five
+    (8256, F16, (2, 5, 4, 4)),       # 17..20: four slices, batches of five
     (10240, BF16, (2, 5, 4, 4)),
-    (10248, BF16, (2, 3, 8, 8)),     # 21..26: eight slices, batches of three
+    (10304, BF16, (2, 3, 8, 8)),     # 21..26: eight slices, batches of three
     (13312, F16, (2, 3, 8, 8)),
-    (13320, BF16, (2, 8, 4, 4)),     # 27..29: four slices, eight-slot batches
+    (13376, BF16, (2, 8, 4, 4)),     # 27..29: four slices, eight-slot batches
     (14848, F16, (2, 8, 4, 4)),
     (15360, BF16, (2, 4, 8, 8)),     # 30: eight slices of four
     (15872, BF16, (2, 2, 4, 4)),     # 31: four slices, two-slot batches
     (16384, BF16, (2, 4, 8, 8)),     # 32 (bf16)
     (16384, F16, (2, 4, 8, 4)),      # 32 (fp16): two row groups of four slices
     (17408, BF16, (2, 4, 8, 8)),     # 33..34
-    (17416, BF16, (2, 5, 8, 8)),     # 35..40: eight slices, batches of five
+    (17472, BF16, (2, 5, 8, 8)),     # 35..40: eight slices, batches of five
     (20480, F16, (2, 5, 8, 8)),
     (21504, BF16, (2, 6, 8, 8)),     # 41..42: batches of six
-    (21512, F16, (2, 3, 8, 8)),      # 43..48: batches of three (two per slice)
+    (21568, F16, (2, 3, 8, 8)),      # 43..48: batches of three (two per slice)
     (24576, BF16, (2, 3, 8, 8)),
-    (24584, BF16, (2, 8, 8, 8)),     # 49..64: eight slices of seven or eight
+    (24640, BF16, (2, 8, 8, 8)),     # 49..64: eight slices of seven or eight
     (32768, F16, (2, 8, 8, 8)),
-    (32776, F16, (2, 2, 8, 8)),      # 65..80: two-slot batches
+    (32832, F16, (2, 2, 8, 8)),      # 65..80: two-slot batches
     (40960, BF16, (2, 2, 8, 8)),
-    (40968, BF16, (2, 4, 8, 8)),     # beyond: the general split
+    (41024, BF16, (2, 4, 8, 8)),     # beyond: the general split
 ])
 def test_plan_two_row_table(k, dtype, want):
-    assert k % 8 == 0                     # aligned rows (misaligned ones: tier 0)
+    assert k % 64 == 0                    # rows on 128-byte lines (others: below)
     for n in (896, 1000, 3072, 4096, 8192, 18432):
+        if k <= 6144 and 2048 <= n < 6144:
+            continue                      # the short-row rule (below)
         assert shape_of(plan(n, k, dtype)[1]) == want + (1, 0), (n, k, dtype)
 
 
 def test_plan_two_row_table_14_steps():
     # 14 steps: four slices of four from 4096 rows, eight slices of two below
-    for k in (7168, 7000):
+    for k in (7168, 7040):
         for dtype in (F16, BF16):
             for n in (896, 1000, 2048, 4095):
                 assert shape_of(plan(n, k, dtype)[1]) == (2, 2, 8, 8, 1, 0), (n, k, dtype)
@@ -478,3 +480,52 @@ def test_plan_null_output():
     lib = _lib.load()
     assert lib.gemv_plan_config(4, 8, 0, 1, MAX_LDS, 0, None) == _lib.GEMV_ERR_INVALID_ARG
     assert lib.gemv_plan_config(4, 8, 0, 1, MAX_LDS, 1, None) == _lib.GEMV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("k,want", [
+    # short rows (<= 12 steps) on >= 2048 rows: a batch no larger than needed
+    (256, (2, 2, 4, 1)), (512, (2, 2, 4, 1)),           # 1 step (below 16384 rows)
+    (1024, (2, 2, 4, 1)), (984, (2, 2, 4, 1)),          # 2
+    (1280, (2, 4, 4, 1)), (1536, (2, 4, 4, 1)),         # 3
+    (2048, (1, 4, 4, 1)), (2008, (1, 4, 4, 1)),         # 4
+    (2560, (2, 2, 4, 4)), (3072, (2, 2, 4, 4)),         # 5..6: four slices of two
+    (3584, (1, 8, 4, 1)), (4096, (1, 8, 4, 1)),         # 7..8: one row, eight slots
+    (4608, (2, 3, 4, 4)), (5120, (2, 3, 4, 4)),         # 9..10: four slices of three
+])
+def test_plan_short_rows(k, want):
+    for n in (2048, 3000, 8192, 12288):
+        for dtype in (F16, BF16):
+            assert shape_of(plan(n, k, dtype)[1]) == want + (1, 0), (n, k, dtype)
+
+
+def test_plan_short_rows_edges():
+    # one step from 16384 rows: four rows per wave
+    assert shape_of(plan(16384, 512, BF16)[1]) == (4, 2, 4, 1, 1, 0)
+    assert shape_of(plan(16383, 512, BF16)[1]) == (2, 2, 4, 1, 1, 0)
+    # 11..12 steps: one row of four slots below 6144 rows, four slices of
+    # three from there; off 128-byte lines from 6144 rows: three rows, eight
+    # slices of two
+    assert shape_of(plan(4096, 5632, F16)[1]) == (1, 4, 4, 1, 1, 0)
+    assert shape_of(plan(6144, 5632, F16)[1]) == (2, 3, 4, 4, 1, 0)
+    assert shape_of(plan(6144, 5000, BF16)[1]) == (3, 2, 8, 8, 1, 0)
+    assert shape_of(plan(6143, 5000, BF16)[1]) == (2, 3, 4, 4, 1, 0)
+    # below 2048 rows the earlier rules (one row, eight slots for <= 8 steps)
+    assert shape_of(plan(2047, 2048, BF16)[1]) == (1, 8, 4, 1, 1, 0)
+
+
+@pytest.mark.parametrize("n,k,want", [
+    # rows 16-byte but not 128-byte aligned, >= 6144 of them, 13..48 steps:
+    # three rows per wave, eight slices, batches of two up to 16 steps, three
+    # beyond
+    (6144, 7000, (3, 2, 8, 8, 1, 0)),
+    (18432, 7176, (3, 2, 8, 8, 1, 0)),
+    (32768, 8200, (3, 3, 8, 8, 1, 0)),
+    (18432, 14000, (3, 3, 8, 8, 1, 0)),
+    (8192, 24568, (3, 3, 8, 8, 1, 0)),       # 48 steps
+    (8192, 24584, (2, 8, 8, 8, 1, 0)),       # 49: the two-row table
+    (6143, 7000, (2, 4, 4, 4, 1, 0)),        # fewer rows: the two-row table (14 steps)
+    (18432, 7168, (2, 4, 4, 4, 1, 0)),       # rows on 128-byte lines: the table
+])
+def test_plan_rows_off_lines(n, k, want):
+    for dtype in (F16, BF16):
+        assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
