@@ -259,9 +259,16 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
                bool with_ws) {
   const int64_t nfull0 = k / mbd::kStep;
   const bool misaligned = k > 0 && (k % 8 != 0 || !b_aligned);
+  // rows 16-byte aligned that start off 128-byte lines (k not a multiple of
+  // 64), at least 2048 of them, of at least 32 steps: the shifted-window
+  // kernel of tier 0 too, whose line-aligned granules of B suit them (graph
+  // replay, n = 2048..18432, k = 16936..40040 bf16: the best compiled plan
+  // or within 2.1%, where the two-row plans were 3-8% behind)
+  const bool off_lines = k > 0 && k % mbd::kLine != 0;
+  const bool long_off_lines = off_lines && !misaligned && n >= 2048 && (k + mbd::kStep - 1) / mbd::kStep >= 32;
   constexpr int64_t kShortMisaligned = 8192;   // the k range of the measured tiers of 1
   // 0.
-  if (misaligned && n >= 768) {
+  if ((misaligned && n >= 768) || long_off_lines) {
     const int64_t nst = (k + mbd::kLine - 1 + mbd::kStep - 1) / mbd::kStep;
     auto shift = [](int R, int U, int W, int S) {
       return Plan{R, U, W, S, mbd::A_SHIFTED, kPolNT, 0, 1};
@@ -343,9 +350,14 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // two-wave workgroups, no split (graph replay, five shapes in fp16 and
   // bf16: the best compiled plan, 0.9-13.5% ahead of the plans below)
   if (nfull >= 128 && n >= 1280 && n <= 2048) return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
-  // very long rows (k >= 48K) and enough of them: no split, two rows per
-  // one-wave workgroup (the split's per-slice combine no longer pays)
-  if (nfull >= 96 && n >= 1536) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
+  // very long rows (k >= 48K) on 1536..4095 rows: no split, two rows per
+  // one-wave workgroup (the split's per-slice combine no longer pays); rows
+  // of more than 96 steps from 4096 rows: three rows per wave over eight
+  // k-slices of three-slot batches (graph replay, n = 4096..8192, k = 51904
+  // .. 98304: the best compiled plan or within 1%, where the unsplit plan was
+  // up to 14% behind)
+  if (nfull >= 96 && n >= 1536 && n < 4096) return Plan{2, 4, 1, 1, mbd::A_CACHED, kPolNT, 0, 1};
+  if (k > 96 * mbd::kStep && n >= 4096) return Plan{3, 3, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
   // rows of 12 or 18..24 whole steps (no partial step) on 1536..2560 rows:
   // no split, one row per wave in two-wave workgroups.  (Graph replay over
   // aligned shapes of n = 1536..8192, k = 6144..16384 with and without a
@@ -372,38 +384,40 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     return n < 832 ? Plan{1, 2, 4, 4, mbd::A_CACHED, kPolNT, 0, 1}
                    : Plan{2, 2, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
   // Rows that start 16-byte but not 128-byte aligned (k not a multiple of
-  // 64), at least 6144 of them, of 13..48 steps: three rows per wave, eight
+  // 64), at least 6144 of them, of 13..31 steps: three rows per wave, eight
   // k-slices, batches of two (up to 16 steps) or three.  (Graph replay, n =
-  // 6144..32768, k = 7000..20040, fp16 and bf16: the best compiled plan or
+  // 6144..32768, k = 7000..14000, fp16 and bf16: the best compiled plan or
   // within 3.2%, where the two-row plans below were 2-6% behind; on rows
   // that start on 128-byte lines, and below 6144 rows, three rows per wave
-  // do not pay.)
-  if (k % mbd::kLine != 0 && n >= 6144 && nsteps >= 13 && nsteps <= 48)
+  // do not pay.  Longer ones went to tier 0.)
+  if (off_lines && n >= 6144 && nsteps >= 13 && nsteps <= 31)
     return Plan{3, nsteps <= 16 ? 2 : 3, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
-  // Short rows (at most 12 steps) on at least 2048 rows: a batch no larger
+  // Short rows (at most 12 steps) on at least 1024 rows: a batch no larger
   // than the row or the slice needs.  A slot past the wave's steps still
   // issues its B and a loads (out of range, so no memory access, but
   // through the address units all the same), which cost up to 70% where
   // eight-slot batches carried three steps.  1..2 steps: two rows per wave,
-  // two slots (four rows from 16384 rows of one step); 3: two rows, four
+  // two slots, from 2048 rows (four rows from 12288 rows of one step), one
+  // row below; 3: two rows, four
   // slots; 4: one row, four slots; 5..6: two rows over four slices of two
   // slots; 7..8: one row, eight slots; 9..12: two rows over four slices of
   // three slots -- three rows over eight slices of two on rows off 128-byte
-  // lines from 6144 rows, one row of four slots below 6144 rows for 11..12.
+  // lines from 6144 rows, one row of four slots on 2048..6143 rows for 11..12.
   // (Graph replay over 95 shapes, n = 2048..32768, k = 256..6144, fp16 and
   // bf16: 0.8% off the best compiled plan on average, 2.9% at the 90th
   // percentile, where the previous rule -- eight slots for every row of at
   // most 8 steps -- was 12% and 35%, up to 70%.)
-  if (n >= 2048 && nsteps <= 12) {
+  if (n >= 1024 && nsteps <= 12) {
     auto pl = [](int R, int U, int W, int S) { return Plan{R, U, W, S, mbd::A_CACHED, kPolNT, 0, 1}; };
-    if (nsteps <= 1) return n >= 16384 ? pl(4, 2, 4, 1) : pl(2, 2, 4, 1);
-    if (nsteps <= 2) return pl(2, 2, 4, 1);
+    if (nsteps <= 1 && n >= 2048) return n >= 12288 ? pl(4, 2, 4, 1) : pl(2, 2, 4, 1);
+    if (nsteps <= 2 && n >= 2048) return pl(2, 2, 4, 1);
+    if (nsteps <= 2) return pl(1, 2, 4, 1);
     if (nsteps <= 3) return pl(2, 4, 4, 1);
     if (nsteps <= 4) return pl(1, 4, 4, 1);
     if (nsteps <= 6) return pl(2, 2, 4, 4);
     if (nsteps <= 8) return pl(1, 8, 4, 1);
-    if (k % mbd::kLine != 0 && n >= 6144) return pl(3, 2, 8, 8);
-    if (nsteps >= 11 && n < 6144) return pl(1, 4, 4, 1);
+    if (off_lines && n >= 6144) return pl(3, 2, 8, 8);
+    if (nsteps >= 11 && n >= 2048 && n < 6144) return pl(1, 4, 4, 1);
     return pl(2, 3, 4, 4);
   }
   const int R = ((n >= 896 && k >= 6144) || (n >= 320 && n <= 512 && nsteps >= 20)) ? 2 : 1;
@@ -450,9 +464,15 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
         {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}};  // 57..64
     int U = kTwoRow[nsteps - 12][0], Sl = kTwoRow[nsteps - 12][1];
     if (nsteps == 14 && n < 4096) U = 2, Sl = 8;
-    if (nsteps == 32 && dtype == GEMV_F16) return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
+    if (nfull == 32 && dtype == GEMV_F16) return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
     return Plan{2, U, Sl, Sl, mbd::A_CACHED, kPolNT, 0, 1};
   }
+  // 65..80 steps on at least 896 rows: eight slices of five-slot batches
+  // (two batches each; graph replay, n = 1024..8192, k = 36864..40960: the
+  // best compiled plan or within 1.2%, where two-slot batches were 1-5%
+  // behind); 81..96 steps: eight slices of three-slot batches
+  if (R == 2 && n >= 896 && nsteps >= 65 && nsteps <= 80) return Plan{2, 5, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
+  if (R == 2 && n >= 896 && nsteps >= 81 && nsteps <= 96) return Plan{2, 3, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
   // Two rows per wave otherwise (320..895 rows, or more than 64 steps): give
   // each k-slice a share that fills its batch of loads -- eight slots for
   // shares of 7-8 steps (25..28 steps over four slices, 49..64 over eight),

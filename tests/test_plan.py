@@ -197,7 +197,8 @@ def _takes_shifted_window(n, nst):
 
 def test_plan_shifted_window_only_for_misaligned_rows():
     """The shifted-window kernel serves misaligned rows from 768 of them
-    (tier 0), and aligned rows never."""
+    (tier 0), and 16-byte aligned rows only where they start off 128-byte
+    lines, from 2048 rows of at least 32 steps."""
     ns = [767, 768, 1023, 1024, 2047, 2048, 4095, 4096, 6143, 6144, 8191, 8192, 12287, 12288,
           65536]
     ks = [9, 511, 1025, 1535, 1537, 2049, 2559, 2561, 4097, 4607, 4609, 8705, 8767, 20415,
@@ -206,7 +207,11 @@ def test_plan_shifted_window_only_for_misaligned_rows():
         info = plan(n, k, BF16)[1]
         assert (info.a_mode == 3) == _takes_shifted_window(n, _nst(k)), (n, k, shape_of(info))
         ka = k - k % 8                  # aligned rows of about the same length
-        assert plan(n, ka, BF16)[1].a_mode != 3, (n, ka)
+        off_lines_long = ka % 64 != 0 and n >= 2048 and (ka + 511) // 512 >= 32
+        assert (plan(n, ka, BF16)[1].a_mode == 3) == off_lines_long, (n, ka)
+        kl = k - k % 64                 # rows on 128-byte lines: never
+        if kl > 0:
+            assert plan(n, kl, BF16)[1].a_mode != 3, (n, kl)
 
 
 @pytest.mark.parametrize("n,k,want", [
@@ -295,9 +300,10 @@ def test_plan_whole_step_rows_unsplit(n, k, dtype, want):
     (24576, BF16, (2, 3, 8, 8)),
     (24640, BF16, (2, 8, 8, 8)),     # 49..64: eight slices of seven or eight
     (32768, F16, (2, 8, 8, 8)),
-    (32832, F16, (2, 2, 8, 8)),      # 65..80: two-slot batches
-    (40960, BF16, (2, 2, 8, 8)),
-    (41024, BF16, (2, 4, 8, 8)),     # beyond: the general split
+    (32832, F16, (2, 5, 8, 8)),      # 65..80: five-slot batches
+    (40960, BF16, (2, 5, 8, 8)),
+    (41024, BF16, (2, 3, 8, 8)),     # 81..96: three-slot batches
+    (47104, F16, (2, 3, 8, 8)),
 ])
 def test_plan_two_row_table(k, dtype, want):
     assert k % 64 == 0                    # rows on 128-byte lines (others: below)
@@ -493,15 +499,20 @@ def test_plan_null_output():
     (4608, (2, 3, 4, 4)), (5120, (2, 3, 4, 4)),         # 9..10: four slices of three
 ])
 def test_plan_short_rows(k, want):
-    for n in (2048, 3000, 8192, 12288):
+    for n in (2048, 3000, 8192, 12287):
         for dtype in (F16, BF16):
             assert shape_of(plan(n, k, dtype)[1]) == want + (1, 0), (n, k, dtype)
 
 
 def test_plan_short_rows_edges():
-    # one step from 16384 rows: four rows per wave
-    assert shape_of(plan(16384, 512, BF16)[1]) == (4, 2, 4, 1, 1, 0)
-    assert shape_of(plan(16383, 512, BF16)[1]) == (2, 2, 4, 1, 1, 0)
+    # one step from 12288 rows: four rows per wave
+    assert shape_of(plan(12288, 512, BF16)[1]) == (4, 2, 4, 1, 1, 0)
+    assert shape_of(plan(12287, 512, BF16)[1]) == (2, 2, 4, 1, 1, 0)
+    # one or two steps below 2048 rows: one row, two slots; from 1024 rows
+    # three steps and more take the short-row rule
+    assert shape_of(plan(2047, 1024, F16)[1]) == (1, 2, 4, 1, 1, 0)
+    assert shape_of(plan(1024, 1536, F16)[1]) == (2, 4, 4, 1, 1, 0)
+    assert shape_of(plan(1023, 1536, F16)[1]) == (1, 8, 4, 1, 1, 0)
     # 11..12 steps: one row of four slots below 6144 rows, four slices of
     # three from there; off 128-byte lines from 6144 rows: three rows, eight
     # slices of two
@@ -509,8 +520,9 @@ def test_plan_short_rows_edges():
     assert shape_of(plan(6144, 5632, F16)[1]) == (2, 3, 4, 4, 1, 0)
     assert shape_of(plan(6144, 5000, BF16)[1]) == (3, 2, 8, 8, 1, 0)
     assert shape_of(plan(6143, 5000, BF16)[1]) == (2, 3, 4, 4, 1, 0)
-    # below 2048 rows the earlier rules (one row, eight slots for <= 8 steps)
-    assert shape_of(plan(2047, 2048, BF16)[1]) == (1, 8, 4, 1, 1, 0)
+    # below 1024 rows the earlier rules (one row, eight slots for <= 8 steps)
+    assert shape_of(plan(1023, 2048, BF16)[1]) == (1, 8, 4, 1, 1, 0)
+    assert shape_of(plan(1024, 2048, BF16)[1]) == (1, 4, 4, 1, 1, 0)
 
 
 @pytest.mark.parametrize("n,k,want", [
@@ -521,8 +533,14 @@ def test_plan_short_rows_edges():
     (18432, 7176, (3, 2, 8, 8, 1, 0)),
     (32768, 8200, (3, 3, 8, 8, 1, 0)),
     (18432, 14000, (3, 3, 8, 8, 1, 0)),
-    (8192, 24568, (3, 3, 8, 8, 1, 0)),       # 48 steps
-    (8192, 24584, (2, 8, 8, 8, 1, 0)),       # 49: the two-row table
+    (18432, 15864, (3, 3, 8, 8, 1, 0)),      # 31 steps
+    # from 32 steps (and from 2048 rows): the shifted-window kernel, eight
+    # slices of two-slot batches (four-slot beyond 64 steps from 3072 rows)
+    (8192, 15880, (2, 2, 8, 8, 3, 0)),
+    (8192, 24584, (2, 2, 8, 8, 3, 0)),
+    (2048, 16936, (2, 2, 8, 8, 3, 0)),
+    (8192, 40040, (2, 4, 8, 8, 3, 0)),
+    (2047, 16936, (2, 4, 8, 8, 1, 0)),       # fewer rows: the two-row table (34 steps)
     (6143, 7000, (2, 4, 4, 4, 1, 0)),        # fewer rows: the two-row table (14 steps)
     (18432, 7168, (2, 4, 4, 4, 1, 0)),       # rows on 128-byte lines: the table
 ])
