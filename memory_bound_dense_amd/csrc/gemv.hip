@@ -402,7 +402,8 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // slots; 4: one row, four slots; 5..6: two rows over four slices of two
   // slots; 7..8: one row, eight slots; 9..12: two rows over four slices of
   // three slots -- three rows over eight slices of two on rows off 128-byte
-  // lines from 6144 rows, one row of four slots on 2048..6143 rows for 11..12.
+  // lines from 6144 rows, one row of four slots in two-wave workgroups on
+  // 2048..6143 rows for 11..12.
   // (Graph replay over 95 shapes, n = 2048..32768, k = 256..6144, fp16 and
   // bf16: 0.8% off the best compiled plan on average, 2.9% at the 90th
   // percentile, where the previous rule -- eight slots for every row of at
@@ -417,7 +418,7 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
     if (nsteps <= 6) return pl(2, 2, 4, 4);
     if (nsteps <= 8) return pl(1, 8, 4, 1);
     if (off_lines && n >= 6144) return pl(3, 2, 8, 8);
-    if (nsteps >= 11 && n >= 2048 && n < 6144) return pl(1, 4, 4, 1);
+    if (nsteps >= 11 && n >= 2048 && n < 6144) return pl(1, 4, 2, 1);
     return pl(2, 3, 4, 4);
   }
   const int R = ((n >= 896 && k >= 6144) || (n >= 320 && n <= 512 && nsteps >= 20)) ? 2 : 1;
@@ -439,16 +440,16 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // partial one included): the k-slices S and the batch U, by the steps.
   // The principle is one batch of loads per slice, U = the slice's share --
   // a batch slot costs registers whether it is used or not (two rows x U = 2
-  // / 3 / 4 / 5 / 6 / 8 take 55 / 61 / 73 / 80 / 97 / 121 VGPRs for bf16: 8 /
-  // 8 / 6 / 6 / 4 / 4 waves per SIMD) -- with the measured exceptions the
+  // / 3 / 4 / 5 / 6 / 8 take 55 / 61 / 73 / 85 / 97 / 121 VGPRs for bf16: 8 /
+  // 8 / 6 / 5 / 4 / 4 waves per SIMD) -- with the measured exceptions the
   // table keeps: 25..26 and 43..48 steps take batches of three over eight
   // slices (two batches), 31 steps two-slot batches over four, 14 steps on
-  // fewer than 4096 rows eight slices of two, 32 steps two row groups of
-  // four slices in fp16.  (Graph-replayed sweeps over 266 shapes, n = 1024
-  // .. 16384, k = 6144..32768 with and without a partial step, fp16 and
-  // bf16, 16 candidate plans each: 0.5% off the best compiled plan on
-  // average, 1.7% at the 90th percentile, 4.7% at worst, where the previous
-  // rule, with batches of 2, 4 and 8 only, was 1.7%, 3.7% and 17%.)
+  // fewer than 4096 rows eight slices of two, fp16 rows of 32 whole steps
+  // two row groups of four slices.  (Graph-replayed sweeps over 266 shapes,
+  // n = 1024..16384, k = 6144..32768 with and without a partial step, fp16
+  // and bf16, 16 candidate plans each: 0.4% off the best compiled plan on
+  // average, 1.5% at the 90th percentile, 4.2% at worst, where the previous
+  // rule, with batches of 2, 4 and 8 only, was 1.6%, 3.5% and 17%.)
   if (R == 2 && n >= 896 && nsteps >= 12 && nsteps <= 64) {
     // {U, S} for nsteps = 12 + i
     static constexpr signed char kTwoRow[53][2] = {

@@ -516,7 +516,7 @@ def test_plan_short_rows_edges():
     # 11..12 steps: one row of four slots below 6144 rows, four slices of
     # three from there; off 128-byte lines from 6144 rows: three rows, eight
     # slices of two
-    assert shape_of(plan(4096, 5632, F16)[1]) == (1, 4, 4, 1, 1, 0)
+    assert shape_of(plan(4096, 5632, F16)[1]) == (1, 4, 2, 1, 1, 0)
     assert shape_of(plan(6144, 5632, F16)[1]) == (2, 3, 4, 4, 1, 0)
     assert shape_of(plan(6144, 5000, BF16)[1]) == (3, 2, 8, 8, 1, 0)
     assert shape_of(plan(6143, 5000, BF16)[1]) == (2, 3, 4, 4, 1, 0)
