@@ -40,7 +40,8 @@ def test_gemv_probe_runs_the_plan_shapes():
     g = mbd.Gemv(workspace=True)
     for n, k, dtype in [(18432, 7168, mbd.GEMV_F16), (64, 65536, mbd.GEMV_BF16),
                         (1000, 7000, mbd.GEMV_BF16), (4096, 4096, mbd.GEMV_F16),
-                        (256, 512, mbd.GEMV_F16)]:
+                        (256, 512, mbd.GEMV_F16), (4096, 11008, mbd.GEMV_BF16),
+                        (8192, 7000, mbd.GEMV_BF16), (4096, 9216, mbd.GEMV_BF16)]:
         v, grid, kgroups = g.query_config(n, k, dtype)
         info = mbd.gemv_variant_info(v)[1]
         assert probe.gemv_probe_has(info), (n, k, v)
