@@ -176,7 +176,29 @@ struct Plan {
   int rows, unroll, waves, splits, a_mode, policy;
   int grid;
   int kgroups;   // > 1: a cross-workgroup variant with this many k-groups
+  int wg_cap = 0;   // > 0: at most this many workgroups per CU (padding their LDS)
 };
+
+// Workgroups per CU for the four-wave row plans that measured faster with
+// fewer of them resident, on grids of at least six full rounds at that cap:
+// two rows x four slices of four slots (the headline's plan; 7 per CU by its
+// registers) or of three slots, one row of four slots.  With fewer waves per
+// SIMD a load waits behind less of the queue, and the launch's last
+// workgroups drain sooner; on smaller grids the cap only idles slots.
+// (Graph replay, the same plan with and without its LDS padded to cap the
+// workgroups per CU at 5: (18432, 7168) fp16 37.76 -> 37.46 us, bf16 37.81 ->
+// 37.65, (57344, 7168) fp16 112.62 -> 111.88, (16384, 5120) bf16 24.80 ->
+// 24.63, (32768, 5120) bf16 46.96 -> 46.55, (32768, 2048) bf16 20.01 ->
+// 19.90; with grids of 1.6-3.2 rounds 1.6-1.8% slower, e.g. (4096, 7168)
+// bf16 10.60 -> 10.79; one row of eight slots: within 0.25%; at 4 per CU the
+// headline took 37.45, at 3 38.20; eight-wave plans: no gain.)
+constexpr int kCapRounds = 6;
+int wg_cap_of(const Plan& p) {
+  if (p.a_mode != mbd::A_CACHED || p.kgroups > 1 || p.waves != 4 || p.grid != 0) return 0;
+  if (p.rows == 2 && p.splits == 4 && (p.unroll == 4 || p.unroll == 3)) return 5;
+  if (p.rows == 1 && p.splits == 1 && p.unroll == 4) return 5;
+  return 0;
+}
 
 int find_variant(const Plan& p) {
   const int x = p.kgroups > 1 ? 1 : 0;
@@ -585,10 +607,10 @@ extern "C" gemv_status_t gemv_check_args_ex(const void* B, const void* a, const 
 
 struct Launch {
   int variant;
-  int grid;      // workgroups along x (row ranges)
-  int kgroups;   // workgroups along y (k-groups), 1 unless cross_wg
+  int grid;      // row ranges (workgroups along x; along y with cross_wg)
+  int kgroups;   // k-groups (workgroups along x with cross_wg), 1 otherwise
   int flags;     // kernel flags
-  size_t lds;
+  size_t lds;    // dynamic LDS per workgroup
 };
 static_assert(GEMV_FLAG_XCD_CONTIGUOUS == mbd::kFlagXcdContiguous, "flag values agree");
 
@@ -635,6 +657,7 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_
   int v;
   int64_t g, q;
   int flags = 0;
+  int cap = 0;   // workgroups per CU (0: what the kernel's resources allow)
   if (h->forced.variant >= 0) {
     v = h->forced.variant;
     g = h->forced.grid;
@@ -648,11 +671,18 @@ static gemv_status_t resolve(const gemv_handle_s* h, int64_t n, int64_t k, gemv_
     if (v < 0) return GEMV_ERR_UNSUPPORTED;   // a plan names a variant that is not compiled
     g = p.grid;
     q = p.kgroups;
+    cap = wg_cap_of(p);
   }
   gemv_status_t s = shape_launch(v, g, q, flags, n, k, b_aligned, L);
   if (s != GEMV_OK) return s;
   const size_t st = h->static_lds[v][0] > h->static_lds[v][1] ? h->static_lds[v][0] : h->static_lds[v][1];
   if (L->lds + st > h->max_lds) return GEMV_ERR_UNSUPPORTED;
+  if (cap > 0 && (int64_t)L->grid >= (int64_t)kCapRounds * cap * h->num_cus) {
+    // pad the dynamic LDS so that at most `cap` workgroups fit a CU's LDS
+    // (1 KiB below the even share, for the allocation granule)
+    const size_t share = h->max_lds / (size_t)cap;
+    if (share > st + 1024 && L->lds < share - 1024 - st) L->lds = share - 1024 - st;
+  }
   return GEMV_OK;
 }
 
