@@ -199,6 +199,49 @@ def test_workload_full_size(g, wl):
         _check(dtype, got, ref, ab, k, v, name)
 
 
+# One shape per branch of the automatic plan for aligned rows, with the plan
+# shape (rows, unroll, waves, splits, a_mode) that branch picks.
+RULE_BRANCH_SHAPES = [
+    (4096, 1280, F16, (2, 4, 4, 1, 1)),      # short rows: 3 steps
+    (12288, 512, BF16, (4, 2, 4, 1, 1)),     # one step from 12288 rows
+    (2048, 6104, BF16, (1, 4, 2, 1, 1)),     # 12 steps on 2048..6143 rows
+    (8192, 5000, BF16, (3, 2, 8, 8, 1)),     # short rows off 128-byte lines
+    (8192, 7000, F16, (3, 2, 8, 8, 1)),      # rows off lines, 13..16 steps
+    (6144, 9000, BF16, (3, 3, 8, 8, 1)),     # rows off lines, 17..31 steps
+    (2048, 16936, BF16, (2, 2, 8, 8, 3)),    # long rows off lines: the shifted window
+    (4096, 11008, F16, (2, 3, 8, 8, 1)),     # the two-row table
+    (1024, 20480, BF16, (2, 5, 8, 8, 1)),    # the table, 40 steps
+    (1024, 33792, F16, (2, 5, 8, 8, 1)),     # 65..80 steps
+    (4096, 51200, BF16, (3, 3, 8, 8, 1)),    # more than 96 steps from 4096 rows
+    (32768, 2048, BF16, (1, 4, 4, 1, 1)),    # one row of four slots, five workgroups per CU
+    (16384, 5120, F16, (2, 3, 4, 4, 1)),     # two rows x four slices, five workgroups per CU
+]
+
+
+@pytest.mark.parametrize("n,k,dtype,want", RULE_BRANCH_SHAPES,
+                         ids=["%dx%d_%s" % (n, k, "f16" if d == F16 else "bf16")
+                              for n, k, d, _ in RULE_BRANCH_SHAPES])
+def test_auto_plan_rule_branches(g, n, k, dtype, want):
+    """Each branch of the automatic plan on a shape that takes it: every row
+    against the oracle, integer inputs bit-exact, and the automatic launch
+    (whose workgroups per CU may be capped by padding their LDS) bit for bit
+    the same as the same variant and grid forced without the cap."""
+    v, grid, q = g.query_config(n, k, dtype)
+    i = mbd.gemv_variant_info(v)[1]
+    assert (i.rows, i.unroll, i.waves, i.splits, i.a_mode) == want, (n, k, v)
+    B, a = random_inputs(n, k, dtype, "normal", seed=51)
+    ref, _, ab = oracle.gemv(dtype, B, a)
+    Bd, ad = to_device(B, dtype), to_device(a, dtype)
+    del B
+    got = run(g, Bd, ad)
+    _check(dtype, got, ref, ab, k, v, "%dx%d auto" % (n, k))
+    forced = run(g, Bd, ad, v, grid, q)
+    assert np.array_equal(got, forced), (n, k, v)
+    Bi, ai = integer_inputs(n, k, dtype, seed=52)
+    refi, _, _ = oracle.gemv(dtype, Bi, ai)
+    assert np.array_equal(run(g, to_device(Bi, dtype), to_device(ai, dtype)), refi), (n, k, v)
+
+
 def test_deterministic(g):
     for n, k, dtype in [(7168, 16384, BF16), (64, 65536, BF16), (1000, 7000, F16)]:
         B, a = random_inputs(n, k, dtype, seed=1)
