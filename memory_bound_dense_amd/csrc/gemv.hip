@@ -213,7 +213,9 @@ int find_variant(const Plan& p) {
 }
 
 // The automatic plan, O(1) per call, in this order:
-//  0. rows that do not start on 16-byte boundaries, at least 768 of them:
+//  0. rows that do not start on 16-byte boundaries, at least 768 of them,
+//     and rows that start on 16-byte but not on 128-byte lines, at least 2048
+//     of them, of at least 32 steps:
 //     the shifted-window kernel (B in line-aligned granules, a read at each
 //     row's shift through the caches; two-row shapes pair rows 64 apart),
 //     mostly in its two-slot forms (61 VGPRs: 8 waves per SIMD, where the
@@ -256,27 +258,21 @@ int find_variant(const Plan& p) {
 //     well (below).
 //  3. (misaligned rows below 768 of them take 4 as it stands, with
 //     unaligned 16-byte loads)
-//  4. otherwise a through the caches and non-temporal B loads, two rows per
-//     wave (a read once for both) when n >= 896 and k >= 6144; a row of at
-//     most 8 steps goes to one wave in one batch (two load slots for rows of
-//     1-2 steps); longer rows are split along k inside a workgroup until
-//     every wave has at most 4 steps (one batch of loads), further (down to
-//     two steps per slice) while the grid has fewer than 2048 waves.  The
-//     exceptions: rows of >= 96 steps with n >= 1536 are not split (two rows
-//     per one-wave workgroup), nor are rows of 18..24 whole steps (k a
-//     multiple of 512) on 1536..2560 rows (one row per wave) or fp16 ones of
-//     20..24 whole steps on 3072..6144 rows (two rows per one-wave
-//     workgroup); up to 512 rows of 5..16 steps (768 rows of 9..16) take
-//     four slices in four-wave workgroups; two-row plans of 15..80 steps
-//     size their k-slices and batches so that each slice's share fills its
-//     batch of loads; and fewer than 896 rows of at least 20 steps take the
-//     plan that balances their workgroups over the CUs -- two rows per wave
-//     for 320..512 rows, four slices of two-slot batches for 513..895 (see
-//     there).  (A tuner sweep under
-//     graph replay over n = 256..3072, k = 4096..65536, fp16 and bf16, 22
-//     candidate variants each, on MI355X: this rule is within 1.3% of the
-//     best compiled plan on average, 10% at worst; the previous one, fitted
-//     to host-launched timing, 2.7% and 24%.)
+//  4. otherwise a through the caches and non-temporal B loads, each wave's
+//     (or slice's) steps in a batch of loads no larger than they need, in
+//     this order: very long rows (unsplit on 1280..4095 rows, three rows over
+//     eight slices from 4096 rows); rows of 12 or 18..24 whole steps on
+//     1536..2560 rows unsplit; fewer than 896 rows of at least 20 steps
+//     balanced over the CUs; rows off 128-byte lines from 6144 rows of 13..31
+//     steps three rows per wave; rows of at most 12 steps from 1024 rows by
+//     their step count; two rows per wave on at least 896 rows of 12..96
+//     steps from a table by step count; the rest (fewer rows) the earlier
+//     bands and the general split -- a row of at most 8 steps to one wave,
+//     longer rows split along k inside a workgroup until every wave has at
+//     most 4 steps and further while the grid has fewer than 2048 waves.
+//     Each branch states its measurements below; over 120 shapes drawn at
+//     random (n = 1024..65536, k = 256..65536) the rule is 1% off the best
+//     compiled plan on average, 8% at worst.
 Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned,
                bool with_ws) {
   const int64_t nfull0 = k / mbd::kStep;
