@@ -448,16 +448,22 @@ def test_plan_few_rows_split_in_workgroup(n, k):
 def test_plan_properties_over_a_sweep():
     ns = [1, 7, 63, 64, 127, 128, 255, 256, 1000, 1023, 1024, 2047, 2048, 4095, 4096, 7168, 18433,
           100000]
-    ks = [0, 1, 7, 8, 9, 511, 512, 513, 4096, 6143, 6144, 7169, 9217, 12289, 16383, 16384, 65536,
-          65537, 200000]
+    ks = [0, 1, 7, 8, 9, 511, 512, 513, 4096, 5000, 6143, 6144, 7000, 7169, 9217, 12289, 16383,
+          16384, 16936, 65536, 65537, 65544, 200000]
     for n, k, dtype, aligned in itertools.product(ns, ks, (F16, BF16), (True, False)):
         cfg, info = plan(n, k, dtype, aligned)
         assert 0 <= cfg.variant < mbd.gemv_num_variants()
         assert cfg.grid >= 1 and cfg.kgroups >= 1
         assert info.layout == 0 and info.stages == 0, "an ablation variant was chosen"
         misaligned = k > 0 and (k % 8 != 0 or not aligned)
-        if info.a_mode in (2, 3):
+        off_lines_long = k % 64 != 0 and n >= 2048 and (k + 511) // 512 >= 32
+        if info.a_mode == 2:
             assert misaligned
+        if info.a_mode == 3:
+            assert misaligned or off_lines_long, (n, k, aligned)
+        if info.rows == 3:
+            # three rows per wave: rows off 128-byte lines, or very long rows
+            assert k % 64 != 0 or k > 96 * 512, (n, k)
         if info.cross_wg:
             assert n <= 192 or (n <= 256 and k >= 256 * 512)
         if info.a_mode == 3 and info.rows == 2:
