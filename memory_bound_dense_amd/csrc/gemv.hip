@@ -180,7 +180,7 @@ struct Plan {
 };
 
 // Workgroups per CU for the four-wave row plans that measured faster with
-// fewer of them resident, on grids of at least six full rounds at that cap:
+// fewer of them resident, on grids of at least four full rounds at that cap:
 // two rows x four slices of four slots (the headline's plan; 7 per CU by its
 // registers) or of three slots, one row of four slots.  With fewer waves per
 // SIMD a load waits behind less of the queue, and the launch's last
@@ -189,10 +189,12 @@ struct Plan {
 // workgroups per CU at 5: (18432, 7168) fp16 37.76 -> 37.46 us, bf16 37.81 ->
 // 37.65, (57344, 7168) fp16 112.62 -> 111.88, (16384, 5120) bf16 24.80 ->
 // 24.63, (32768, 5120) bf16 46.96 -> 46.55, (32768, 2048) bf16 20.01 ->
-// 19.90; with grids of 1.6-3.2 rounds 1.6-1.8% slower, e.g. (4096, 7168)
-// bf16 10.60 -> 10.79; one row of eight slots: within 0.25%; at 4 per CU the
-// headline took 37.45, at 3 38.20; eight-wave plans: no gain.)
-constexpr int kCapRounds = 6;
+// 19.90, (12288, 7168) fp16 (4.8 rounds) 26.21 -> 26.08, (24576, 7168) fp16
+// 49.82 -> 49.32; with grids of 1.6-3.2 rounds 1.6-1.8% slower, e.g. (4096,
+// 7168) bf16 10.60 -> 10.79; one row of eight slots: within 0.25%; at 4 per
+// CU the headline took 37.45-37.53, at 3 38.20, and two rows of three slots
+// lost 4-7% at 4; eight-wave plans: no gain.)
+constexpr int kCapRounds = 4;
 int wg_cap_of(const Plan& p) {
   if (p.a_mode != mbd::A_CACHED || p.kgroups > 1 || p.waves != 4 || p.grid != 0) return 0;
   if (p.rows == 2 && p.splits == 4 && (p.unroll == 4 || p.unroll == 3)) return 5;
