@@ -123,6 +123,8 @@ const Variant kVariants[] = {
     // 79..80: three rows per wave, eight slices of two- or three-slot batches
     // (rows that start off 128-byte lines)
     MBD_VARIANT(3, 2, 8, 8, CCH, NT), MBD_VARIANT(3, 3, 8, 8, CCH, NT),
+    // 81: two rows, sixteen slices of three-slot batches (rows of 32..52 steps)
+    MBD_VARIANT(2, 3, 16, 16, CCH, NT),
 };
 #undef NT
 #undef LDS
@@ -462,30 +464,32 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // a batch slot costs registers whether it is used or not (two rows x U = 2
   // / 3 / 4 / 5 / 6 / 8 take 55 / 61 / 73 / 85 / 97 / 121 VGPRs for bf16: 8 /
   // 8 / 6 / 5 / 4 / 4 waves per SIMD) -- with the measured exceptions the
-  // table keeps: 25..26 and 43..48 steps take batches of three over eight
-  // slices (two batches), 31 steps two-slot batches over four, 14 steps on
-  // fewer than 4096 rows eight slices of two, fp16 rows of 32 whole steps
-  // two row groups of four slices.  (Graph-replayed sweeps over 266 shapes,
-  // n = 1024..16384, k = 6144..32768 with and without a partial step, fp16
-  // and bf16, 16 candidate plans each: 0.4% off the best compiled plan on
-  // average, 1.5% at the 90th percentile, 4.2% at worst, where the previous
-  // rule, with batches of 2, 4 and 8 only, was 1.6%, 3.5% and 17%.)
+  // table keeps: 25..26 steps take batches of three over eight slices
+  // (two batches), 31 steps two-slot batches over four, 14 steps on fewer
+  // than 4096 rows eight slices of two, and 32..52 steps sixteen slices of
+  // three-slot batches (one or two batches; 16-wave workgroups).  (Graph-
+  // replayed sweeps over 266 shapes, n = 1024..16384, k = 6144..32768 with
+  // and without a partial step, fp16 and bf16, 16 candidate plans each: 0.4%
+  // off the best compiled plan on average, 1.5% at the 90th percentile, 4.2%
+  // at worst, where the previous rule, with batches of 2, 4 and 8 only, was
+  // 1.6%, 3.5% and 17%; then sixteen slices, on 87 shapes of 24..92 steps:
+  // 1.0-2.8% faster than eight at 32..52 steps, (7168, 16384) bf16 35.26 ->
+  // 34.49 us.)
   if (R == 2 && n >= 896 && nsteps >= 12 && nsteps <= 64) {
     // {U, S} for nsteps = 12 + i
     static constexpr signed char kTwoRow[53][2] = {
         {3, 4}, {4, 4}, {4, 4}, {2, 8}, {3, 8},                   // 12..16
         {5, 4}, {5, 4}, {5, 4}, {5, 4},                           // 17..20
         {3, 8}, {3, 8}, {3, 8}, {3, 8}, {3, 8}, {3, 8},           // 21..26
-        {8, 4}, {8, 4}, {8, 4}, {4, 8}, {2, 4}, {4, 8},           // 27..32
-        {4, 8}, {4, 8},                                           // 33..34
-        {5, 8}, {5, 8}, {5, 8}, {5, 8}, {5, 8}, {5, 8},           // 35..40
-        {6, 8}, {6, 8},                                           // 41..42
-        {3, 8}, {3, 8}, {3, 8}, {3, 8}, {3, 8}, {3, 8},           // 43..48
-        {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8},   // 49..56
+        {8, 4}, {8, 4}, {8, 4}, {4, 8}, {2, 4},                   // 27..31
+        {3, 16}, {3, 16}, {3, 16}, {3, 16}, {3, 16}, {3, 16},     // 32..37
+        {3, 16}, {3, 16}, {3, 16}, {3, 16}, {3, 16}, {3, 16},     // 38..43
+        {3, 16}, {3, 16}, {3, 16}, {3, 16}, {3, 16}, {3, 16},     // 44..49
+        {3, 16}, {3, 16}, {3, 16},                                // 50..52
+        {8, 8}, {8, 8}, {8, 8}, {8, 8},                           // 53..56
         {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}, {8, 8}};  // 57..64
     int U = kTwoRow[nsteps - 12][0], Sl = kTwoRow[nsteps - 12][1];
     if (nsteps == 14 && n < 4096) U = 2, Sl = 8;
-    if (nfull == 32 && dtype == GEMV_F16) return Plan{2, 4, 8, 4, mbd::A_CACHED, kPolNT, 0, 1};
     return Plan{2, U, Sl, Sl, mbd::A_CACHED, kPolNT, 0, 1};
   }
   // 65..80 steps on at least 896 rows: eight slices of five-slot batches

@@ -111,6 +111,7 @@ const ProbeShape kProbeShapes[] = {
     MBD_PROBE(2, 6, 8, 8, 0), MBD_PROBE(2, 3, 4, 4, 0), MBD_PROBE(3, 2, 8, 8, 0),
     MBD_PROBE(3, 3, 8, 8, 0), MBD_PROBE(2, 2, 4, 1, 0), MBD_PROBE(2, 4, 4, 1, 0),
     MBD_PROBE(4, 2, 4, 1, 0), MBD_PROBE(1, 2, 4, 4, 0), MBD_PROBE(1, 2, 4, 4, 1),
+    MBD_PROBE(2, 3, 16, 16, 0),
 };
 #undef MBD_PROBE
 

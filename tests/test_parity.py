@@ -210,7 +210,8 @@ RULE_BRANCH_SHAPES = [
     (6144, 9000, BF16, (3, 3, 8, 8, 1)),     # rows off lines, 17..31 steps
     (2048, 16936, BF16, (2, 2, 8, 8, 3)),    # long rows off lines: the shifted window
     (4096, 11008, F16, (2, 3, 8, 8, 1)),     # the two-row table
-    (1024, 20480, BF16, (2, 5, 8, 8, 1)),    # the table, 40 steps
+    (2048, 28672, BF16, (2, 8, 8, 8, 1)),    # the table, 56 steps
+    (1024, 20480, BF16, (2, 3, 16, 16, 1)),  # the table, 40 steps: sixteen slices
     (1024, 33792, F16, (2, 5, 8, 8, 1)),     # 65..80 steps
     (4096, 51200, BF16, (3, 3, 8, 8, 1)),    # more than 96 steps from 4096 rows
     (32768, 2048, BF16, (1, 4, 4, 1, 1)),    # one row of four slots, five workgroups per CU

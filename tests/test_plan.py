@@ -39,7 +39,7 @@ def shape_of(info):
 WORKLOAD_PLANS = {
     "tiny_256x512_f16": (1, 2, 4, 1, 1, 0),
     "gemv_18432x7168_f16": (2, 4, 4, 4, 1, 0),
-    "gemv_7168x16384_bf16": (2, 4, 8, 8, 1, 0),
+    "gemv_7168x16384_bf16": (2, 3, 16, 16, 1, 0),
     "sweep_4096x4096_f16": (1, 8, 4, 1, 1, 0),
     "sweep_4096x4096_bf16": (1, 8, 4, 1, 1, 0),
     "sweep_11008x4096_f16": (1, 8, 4, 1, 1, 0),
@@ -245,11 +245,11 @@ def test_plan_bf16_short_rows(n, k, want):
 
 
 @pytest.mark.parametrize("n,k,dtype,want", [
-    (7168, 16384, F16, (2, 4, 8, 4, 1, 0)),     # fp16, 32 full steps: four slices
-    (1024, 16384, F16, (2, 4, 8, 4, 1, 0)),
-    (28672, 16384, F16, (2, 4, 8, 4, 1, 0)),
-    (7168, 16384, BF16, (2, 4, 8, 8, 1, 0)),    # bf16: eight
-    (7168, 18432, F16, (2, 5, 8, 8, 1, 0)),     # 36 steps: eight slices of five-slot batches
+    (7168, 16384, F16, (2, 3, 16, 16, 1, 0)),   # 32 steps: sixteen slices of three-slot batches
+    (1024, 16384, F16, (2, 3, 16, 16, 1, 0)),
+    (28672, 16384, F16, (2, 3, 16, 16, 1, 0)),
+    (7168, 16384, BF16, (2, 3, 16, 16, 1, 0)),
+    (7168, 18432, F16, (2, 3, 16, 16, 1, 0)),   # 36 steps
 ])
 def test_plan_rows_of_32_steps(n, k, dtype, want):
     assert shape_of(plan(n, k, dtype)[1]) == want, (n, k, dtype)
@@ -290,15 +290,13 @@ def test_plan_whole_step_rows_unsplit(n, k, dtype, want):
     (14848, F16, (2, 8, 4, 4)),
     (15360, BF16, (2, 4, 8, 8)),     # 30: eight slices of four
     (15872, BF16, (2, 2, 4, 4)),     # 31: four slices, two-slot batches
-    (16384, BF16, (2, 4, 8, 8)),     # 32 (bf16)
-    (16384, F16, (2, 4, 8, 4)),      # 32 (fp16): two row groups of four slices
-    (17408, BF16, (2, 4, 8, 8)),     # 33..34
-    (17472, BF16, (2, 5, 8, 8)),     # 35..40: eight slices, batches of five
-    (20480, F16, (2, 5, 8, 8)),
-    (21504, BF16, (2, 6, 8, 8)),     # 41..42: batches of six
-    (21568, F16, (2, 3, 8, 8)),      # 43..48: batches of three (two per slice)
-    (24576, BF16, (2, 3, 8, 8)),
-    (24640, BF16, (2, 8, 8, 8)),     # 49..64: eight slices of seven or eight
+    (16384, BF16, (2, 3, 16, 16)),   # 32..52: sixteen slices of three-slot batches
+    (16384, F16, (2, 3, 16, 16)),
+    (17472, BF16, (2, 3, 16, 16)),
+    (21568, F16, (2, 3, 16, 16)),
+    (24640, BF16, (2, 3, 16, 16)),
+    (26624, F16, (2, 3, 16, 16)),    # 52
+    (26688, BF16, (2, 8, 8, 8)),     # 53..64: eight slices of seven or eight
     (32768, F16, (2, 8, 8, 8)),
     (32832, F16, (2, 5, 8, 8)),      # 65..80: five-slot batches
     (40960, BF16, (2, 5, 8, 8)),
@@ -342,7 +340,7 @@ def test_plan_two_row_table_14_steps():
     (895, 12288, F16, (2, 2, 4, 4, 1, 0)),
     # outside: 896 rows and more take the two-row bands, fewer than 320 rows
     # or rows of fewer than 20 steps the one-row rule
-    (896, 20480, BF16, (2, 5, 8, 8, 1, 0)),
+    (896, 20480, BF16, (2, 3, 16, 16, 1, 0)),
     (256, 20480, BF16, (1, 4, 16, 16, 1, 0)),
     (512, 8192, BF16, (1, 4, 4, 4, 1, 0)),
     (700, 9216, F16, (1, 4, 8, 8, 1, 0)),
@@ -546,7 +544,7 @@ def test_plan_short_rows_edges():
     (8192, 24584, (2, 2, 8, 8, 3, 0)),
     (2048, 16936, (2, 2, 8, 8, 3, 0)),
     (8192, 40040, (2, 4, 8, 8, 3, 0)),
-    (2047, 16936, (2, 4, 8, 8, 1, 0)),       # fewer rows: the two-row table (34 steps)
+    (2047, 16936, (2, 3, 16, 16, 1, 0)),     # fewer rows: the two-row table (34 steps)
     (6143, 7000, (2, 4, 4, 4, 1, 0)),        # fewer rows: the two-row table (14 steps)
     (18432, 7168, (2, 4, 4, 4, 1, 0)),       # rows on 128-byte lines: the table
 ])
