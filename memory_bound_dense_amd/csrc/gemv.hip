@@ -274,7 +274,7 @@ int find_variant(const Plan& p) {
 //     bands and the general split -- a row of at most 8 steps to one wave,
 //     longer rows split along k inside a workgroup until every wave has at
 //     most 4 steps and further while the grid has fewer than 2048 waves.
-//     Each branch states its measurements below; over 120 shapes drawn at
+//     Each branch states its measurements below; over 180 shapes drawn at
 //     random (n = 1024..65536, k = 256..65536) the rule is 1% off the best
 //     compiled plan on average, 8% at worst.
 Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_aligned,
