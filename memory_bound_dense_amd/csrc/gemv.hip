@@ -230,31 +230,26 @@ int find_variant(const Plan& p) {
 //     slices of four-slot batches beyond; 1024..6143 rows: four slices up to
 //     9 steps, eight for 10..64 (and beyond 64 below 3072 rows; four-slot
 //     batches above); below 1024 rows: eight slices for 6..48 steps, one row
-//     x eight slices beyond.  Rows of at most 3 steps (4..5 from 12288 rows,
-//     at most 5 below 1024) keep the tiers below, except two rows per
-//     four-wave workgroup for at most 3 steps from 12288 rows.  (Graph-
-//     replayed sweeps over 78 misaligned shapes, n = 768..49152,
+//     x eight slices beyond.  Rows of at most 4 steps: at most 2 from 8192
+//     rows in the realigning kernel (aligned granules of B from each row's
+//     128-byte line, a staged twice in LDS), two rows per trip of an
+//     eight-wave workgroup; 3, and 4 from 8192 rows, two rows per four-wave
+//     workgroup of the shifted-window kernel; the rest one row per wave of
+//     it.  Rows of 5 steps from 12288 rows, and below 1024 rows, go to 1.
+//     (Graph-replayed sweeps over 78 misaligned shapes, n = 768..49152,
 //     k = 1025..32769, every candidate shape of the three misaligned kernels
 //     on full and persistent grids: 1.1% off the best compiled plan on
 //     average, 3.1% at the 90th percentile, where the previous tier 0, built
-//     on the four-slot forms, was 3.5% and 9.6%, up to 16%.)
-//  1. the misaligned rows tier 0 leaves, at least 3072 of them: short rows
-//     (at most 3 granule steps, 4..5 from 12288 rows).
-//     Up to 8192 rows, or rows of at most 3 steps: one row per wave, a
-//     staged in LDS and B read with unaligned 16-byte loads, on at most 2048
-//     four-wave workgroups (one full occupancy; 1536 for rows of at most 3
-//     steps); rows of 4 full steps and a partial one from 4096 rows (whose
-//     second batch in the one-row kernel would carry only the partial step),
-//     and more rows, the realigning kernel (aligned granules of B from each
-//     row's 128-byte line, a staged twice in LDS) in eight-wave workgroups,
-//     two steps per batch, on a persistent grid of 1024 (8192 waves: 32 per
-//     CU, one full occupancy).  (A tuner sweep over 70 misaligned bf16
-//     shapes with n = 512..65536, k = 1025..8001 on MI355X: within 3.5% of
-//     the best compiled plan on average, before tier 0 took most of them.)
-//     Misaligned rows that tier 0 leaves below 3072, from 768 rows of at
-//     most 12 full steps: one row per wave in two-wave workgroups with
-//     unaligned loads (measured under graph replay over n = 768..2560,
-//     k = 2049..6143 bf16: 2.6% off the best compiled plan on average).
+//     on the four-slot forms, was 3.5% and 9.6%, up to 16%.  Rows of at most
+//     4 steps from 48 shapes drawn at random, below.)
+//  1. the misaligned rows tier 0 leaves, of 5 granule steps: from 12288
+//     rows the realigning kernel in eight-wave workgroups, two steps per
+//     batch, on a persistent grid of 1024 (8192 waves: 32 per CU, one full
+//     occupancy); on 768..1023 rows one row per wave in two-wave workgroups
+//     with unaligned 16-byte loads.  (Graph replay over random misaligned
+//     shapes: within 0.7% of the best compiled plan on the two of 28747 and
+//     30066 rows; 2.6% off on average over n = 768..2560, k = 2049..6143
+//     bf16 for the two-wave plan.)
 //  2. too few rows to give the GPU 2048 waves even with 16 waves per row
 //     (n < 128), with rows of at least 32 steps: one row per 8-wave
 //     workgroup, eight k-slices.  With a workspace, up to 192 rows of at
@@ -288,13 +283,27 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // or within 2.1%, where the two-row plans were 3-8% behind)
   const bool off_lines = k > 0 && k % mbd::kLine != 0;
   const bool long_off_lines = off_lines && !misaligned && n >= 2048 && (k + mbd::kStep - 1) / mbd::kStep >= 32;
-  constexpr int64_t kShortMisaligned = 8192;   // the k range of the measured tiers of 1
   // 0.
   if ((misaligned && n >= 768) || long_off_lines) {
     const int64_t nst = (k + mbd::kLine - 1 + mbd::kStep - 1) / mbd::kStep;
     auto shift = [](int R, int U, int W, int S) {
       return Plan{R, U, W, S, mbd::A_SHIFTED, kPolNT, 0, 1};
     };
+    // misaligned rows of at most four granule steps (k < 1986): at most two
+    // from 8192 rows in the realigning kernel, two rows per trip, eight-wave
+    // workgroups; three, and four from 8192 rows, two rows per four-wave
+    // workgroup of the shifted-window kernel; the rest one row per wave of
+    // it.  (Graph replay over 48 shapes drawn at random, n = 768..60051, k =
+    // 411..1905, fp16 and bf16: at most two steps from 8192 rows the best
+    // compiled plan on all 16, below the best or within 8%; three steps
+    // within 6%; four the best from 16136 rows and below 4096.  The tiers
+    // below, from an earlier kernel, were 13-47% behind at most two steps.)
+    if (misaligned && nst <= 4) {
+      const Plan pr = {2, 2, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 0, 1};
+      if (nst <= 2 && n >= 8192 && lds_bytes(kVariants[find_variant(pr)].info, k) <= max_lds) return pr;
+      if (nst == 3 || (nst == 4 && n >= 8192)) return shift(2, 4, 4, 1);
+      return shift(1, 2, 4, 1);
+    }
     if (n < 1024) {
       if (nst >= 6 && nst <= 48) return shift(2, 2, 8, 8);
       if (nst > 48) return shift(1, 4, 8, 8);
@@ -307,23 +316,17 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
       if (nst <= 31) return shift(2, 2, 4, 4);
       if (nst <= 64) return shift(2, 2, 8, 8);
       return shift(2, 4, 8, 8);
-    } else if (nst <= 3 && n >= 12288) {
-      return shift(2, 4, 4, 1);
     }
   }
-  // 1.
-  if (misaligned && k <= kShortMisaligned && n >= 3072) {
-    const Plan pl = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 1536, 1};
-    const Plan pl2 = {1, 4, 4, 1, mbd::A_LDS, kPolNT, 2048, 1};
+  // 1. the misaligned rows tier 0 leaves, of five granule steps: from 12288
+  // rows the realigning kernel on a persistent grid of 1024 eight-wave
+  // workgroups (8192 waves: 32 per CU), 768..1023 rows one row per wave in
+  // two-wave workgroups with unaligned 16-byte loads.
+  if (misaligned && n >= 12288) {
     const Plan pr = {1, 2, 8, 1, mbd::A_LDS_SHIFTED, kPolNT, 1024, 1};
-    const Plan& p = k <= 3 * mbd::kStep ? pl
-                    : (k > 4 * mbd::kStep && k < 5 * mbd::kStep && n >= 4096) ? pr
-                    : n <= 8192 ? pl2 : pr;
-    if (lds_bytes(kVariants[find_variant(p)].info, k) <= max_lds) return p;
+    if (lds_bytes(kVariants[find_variant(pr)].info, k) <= max_lds) return pr;
   }
-  // the misaligned rows tier 0 leaves below 3072 (see 1)
-  if (misaligned && k <= kShortMisaligned && n >= 768 && n < 3072 && nfull0 <= 12)
-    return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
+  if (misaligned && n >= 768 && n < 1024) return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // 2. k split over Q workgroups as well, for few rows of many steps -- only
   // with caller scratch for the partials and counters (gemv_run_ws);
   // without it, the in-workgroup split below.  Grids of about 512

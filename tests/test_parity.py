@@ -663,14 +663,15 @@ def test_realigned_rows_do_not_leak(g, dtype):
 def test_auto_plan_realigns_misaligned_rows(g):
     """Misaligned rows on the device handle: from 768 rows the shifted-window
     kernel (a_mode 3), mostly in its two-slot forms, by the rows' granule
-    steps and count; rows of at most 3 steps from 3072 rows one row per wave
-    with a in LDS (a_mode 0), 4..5 steps from 12288 rows the realigning
-    kernel (a_mode 2); fewer rows the plan of aligned rows."""
+    steps and count; rows of at most 2 steps from 8192 rows two rows per trip
+    of the realigning kernel (a_mode 2), and 5 steps from 12288 rows one; 5
+    steps below 1024 rows and fewer than 768 rows the plan of aligned rows."""
     for n, k, want in [(18433, 7169, (3, 2, 4, 4)), (3072, 7169, (3, 2, 8, 8)),
                        (1000, 16383, (3, 2, 8, 8)), (3072, 12289, (3, 2, 8, 8)),
                        (4096, 12289, (3, 2, 8, 8)), (6144, 20993, (3, 2, 8, 8)),
                        (6144, 4097, (3, 2, 4, 4)), (9000, 4097, (3, 2, 4, 4)),
-                       (16384, 1025, (3, 2, 4, 1)), (8192, 1025, (0, 1, 4, 1)),
+                       (16384, 1025, (3, 2, 4, 1)), (8192, 1025, (3, 2, 4, 1)),
+                       (8192, 961, (2, 2, 8, 1)), (4040, 641, (3, 1, 4, 1)),
                        (12288, 2049, (2, 1, 8, 1)), (768, 2049, (1, 1, 2, 1)),
                        (100, 1000, (1, 1, 4, 1))]:
         v, grid, q = g.query_config(n, k, BF16)
@@ -684,7 +685,10 @@ LONG_MIS = [(4096, 12289, BF16, 3), (4096, 16001, F16, 1), (1000, 16383, BF16, 5
             (9000, 4097, BF16, 2), (8200, 2559, F16, 4), (1536, 9217, BF16, 6),
             (800, 5121, F16, 1), (2000, 2049, BF16, 7), (3072, 12289, F16, 2),
             (6144, 20993, BF16, 3), (12288, 2049, F16, 6), (8192, 24577, BF16, 5),
-            (900, 65537, F16, 4), (2048, 1025, BF16, 3), (4096, 32769, F16, 2)]
+            (900, 65537, F16, 4), (2048, 1025, BF16, 3), (4096, 32769, F16, 2),
+            (8192, 961, BF16, 3), (30001, 719, F16, 5), (4040, 641, BF16, 1),
+            (768, 9, F16, 2), (65536, 9, BF16, 1), (8193, 1545, F16, 6),
+            (6145, 1545, BF16, 7)]
 
 
 @pytest.mark.parametrize("n,k,dtype,shift", LONG_MIS,

@@ -94,7 +94,6 @@ def test_plan_grids_of_the_production_shapes():
     # 12288 rows; one row per wave with a in LDS at most 1536 workgroups for
     # rows of at most 3 steps
     assert plan(12288, 2049, BF16)[0].grid == 1024
-    assert plan(8192, 1025, BF16)[0].grid == 1536
     # 64 rows: k shared by 8 workgroups per row
     assert plan(64, 65536, BF16)[0].kgroups == 8
 
@@ -119,8 +118,7 @@ def _nst(k):
     (8192, 9217, (2, 2, 4, 4, 3, 0)),
     (8192, 12289, (2, 2, 4, 4, 3, 0)),     # 25
     (6144, 4097, (2, 2, 4, 4, 3, 0)),      # 9
-    (6145, 1545, (2, 2, 4, 4, 3, 0)),      # 4
-    (8193, 1545, (2, 2, 4, 4, 3, 0)),
+    (8193, 2051, (2, 2, 4, 4, 3, 0)),      # 5
     (12288, 4097, (2, 2, 4, 4, 3, 0)),
     (14336, 2559, (2, 2, 4, 4, 3, 0)),     # 6 from 12288 rows
     # ... but four-slot batches at 14..15 steps from 12288 rows
@@ -138,7 +136,6 @@ def _nst(k):
     (4096, 2051, (2, 2, 4, 4, 3, 0)),      # 5
     (4095, 2049, (2, 2, 4, 4, 3, 0)),
     (4096, 2561, (2, 2, 4, 4, 3, 0)),
-    (4096, 1545, (2, 2, 4, 4, 3, 0)),
     (1500, 4097, (2, 2, 4, 4, 3, 0)),      # 9
     (3072, 7169, (2, 2, 8, 8, 3, 0)),      # 15
     (2048, 5121, (2, 2, 8, 8, 3, 0)),      # 11
@@ -156,19 +153,30 @@ def _nst(k):
     (1000, 16897, (2, 2, 8, 8, 3, 0)),
     (800, 16385, (2, 2, 8, 8, 3, 0)),
     (900, 65537, (1, 4, 8, 8, 3, 0)),
-    # at most 3 steps from 12288 rows: two rows per four-wave workgroup
-    (16384, 1025, (2, 4, 4, 1, 3, 0)),
-    # the rest keep the older tiers: from 3072 rows one row per wave with a in
-    # LDS (at most 3 steps) ...
-    (65536, 1535, (1, 4, 4, 1, 0, 0)),     # 4 steps, but from 12288 rows
-    (8192, 1025, (1, 4, 4, 1, 0, 0)),
-    (3072, 1025, (1, 4, 4, 1, 0, 0)),
-    # ... 4..5 steps from 12288 rows the realigning kernel ...
+    # at most 4 steps: 1..2 from 8192 rows two rows per trip of the
+    # realigning kernel (a_mode 2) in eight-wave workgroups ...
+    (8192, 961, (2, 2, 8, 1, 2, 0)),       # 2
+    (30000, 719, (2, 2, 8, 1, 2, 0)),
+    (65536, 9, (2, 2, 8, 1, 2, 0)),        # 1
+    # ... 3, and 4 from 8192 rows, two rows per four-wave workgroup ...
+    (16384, 1025, (2, 4, 4, 1, 3, 0)),     # 3
+    (8192, 1025, (2, 4, 4, 1, 3, 0)),
+    (3072, 1025, (2, 4, 4, 1, 3, 0)),
+    (2048, 1025, (2, 4, 4, 1, 3, 0)),
+    (768, 1473, (2, 4, 4, 1, 3, 0)),
+    (65536, 1535, (2, 4, 4, 1, 3, 0)),     # 4
+    (8193, 1545, (2, 4, 4, 1, 3, 0)),
+    # ... the rest one row per four-wave workgroup
+    (8191, 961, (1, 2, 4, 1, 3, 0)),       # 2
+    (4040, 641, (1, 2, 4, 1, 3, 0)),
+    (768, 9, (1, 2, 4, 1, 3, 0)),          # 1
+    (6145, 1545, (1, 2, 4, 1, 3, 0)),      # 4
+    (4096, 1545, (1, 2, 4, 1, 3, 0)),
+    # 5 steps from 12288 rows: the realigning kernel, one row per trip ...
     (12288, 2049, (1, 2, 8, 1, 2, 0)),
     (16384, 2177, (1, 2, 8, 1, 2, 0)),
-    # ... below 3072 rows one row per two-wave workgroup ...
+    # ... below 1024 rows one row per two-wave workgroup ...
     (768, 2049, (1, 4, 2, 1, 1, 0)),
-    (2048, 1025, (1, 4, 2, 1, 1, 0)),
     # ... and below 768 rows the plan of aligned rows
     (512, 5121, (1, 4, 4, 4, 1, 0)),
     (700, 16385, (1, 2, 4, 4, 1, 0)),      # (the small-row plan of aligned rows)
@@ -186,13 +194,11 @@ def _takes_shifted_window(n, nst):
     """Whether tier 0 takes n misaligned rows of nst granule steps."""
     if n < 768:
         return False
-    if n < 1024:
-        return nst >= 6
-    if n < 6144:
-        return nst >= 4
-    if n >= 12288:
-        return nst <= 3 or nst >= 6
-    return nst >= 4
+    if nst <= 2:
+        return n < 8192         # from 8192 rows the realigning kernel
+    if nst == 5:
+        return 1024 <= n < 12288
+    return True
 
 
 def test_plan_shifted_window_only_for_misaligned_rows():
