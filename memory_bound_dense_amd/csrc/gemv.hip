@@ -368,6 +368,14 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
       if (fits(Q)) return Plan{1, 4, 4, 1, mbd::A_CACHED, kPolNT, 0, (int)Q};
     }
   }
+  // misaligned rows of at least 24 granule steps on 96..319 rows (where the
+  // split across workgroups above does not take them): the shifted-window
+  // kernel, one row over eight k-slices of four-slot batches (graph replay,
+  // random shapes of 137..237 rows, k = 11919..79545: the best compiled plan
+  // on all three, where the unaligned loads of the plans below were 6-22%
+  // behind; from 49 to 81 rows it was 0-4% either way)
+  if (misaligned && n >= 96 && n < 320 && (k + mbd::kLine - 1 + mbd::kStep - 1) / mbd::kStep >= 24)
+    return Plan{1, 4, 8, 8, mbd::A_SHIFTED, kPolNT, 0, 1};
   if (n < 128 && nfull0 >= 32) return Plan{1, 4, 8, 8, mbd::A_CACHED, kPolNT, 0, 1};
   // 4.
   const int64_t nfull = k / mbd::kStep;
@@ -451,8 +459,16 @@ Plan rule_plan(int64_t n, int64_t k, gemv_dtype_t dtype, size_t max_lds, bool b_
   // that would only be skipped (measured on MI355X under graph replay:
   // (1024, 1024) 2.75 -> 2.45 us, (256, 512) 2.64 -> 2.35 us)
   if (R == 1 && nsteps <= 2) return Plan{1, 2, 4, 1, mbd::A_CACHED, kPolNT, 0, 1};
+  // rows of 3..4 steps: one batch of four slots, two-wave workgroups (graph
+  // replay, random shapes of 221..448 rows, k = 1216..1664: the best
+  // compiled plan on all four, where one eight-slot batch was 9-11% behind)
+  if (R == 1 && nsteps <= 4) return Plan{1, 4, 2, 1, mbd::A_CACHED, kPolNT, 0, 1};
   // up to 512 rows of 5..16 steps, and up to 768 rows of 9..16: four slices
-  // in four-wave workgroups
+  // in four-wave workgroups, in batches of two up to 8 steps (graph replay,
+  // random shapes of 49..432 rows of 5..8 steps: the best compiled plan on
+  // all four, where four-slot batches, or one of eight, were 2.6-6.9%
+  // behind)
+  if (R == 1 && n <= 512 && nsteps >= 5 && nsteps <= 8) return Plan{1, 2, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
   if (R == 1 && nfull <= 16 && ((n <= 512 && nfull >= 5) || (n <= 768 && nfull > 8)))
     return Plan{1, 4, 4, 4, mbd::A_CACHED, kPolNT, 0, 1};
   // otherwise a row of at most 8 steps goes to one wave, in one batch

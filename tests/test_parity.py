@@ -216,6 +216,8 @@ RULE_BRANCH_SHAPES = [
     (4096, 51200, BF16, (3, 3, 8, 8, 1)),    # more than 96 steps from 4096 rows
     (32768, 2048, BF16, (1, 4, 4, 1, 1)),    # one row of four slots, five workgroups per CU
     (16384, 5120, F16, (2, 3, 4, 4, 1)),     # two rows x four slices, five workgroups per CU
+    (448, 1216, F16, (1, 4, 2, 1, 1)),       # 3..4 steps below 1024 rows: four slots, two waves
+    (408, 3200, BF16, (1, 2, 4, 4, 1)),      # 5..8 steps up to 512 rows: four slices of two slots
 ]
 
 
@@ -688,7 +690,7 @@ LONG_MIS = [(4096, 12289, BF16, 3), (4096, 16001, F16, 1), (1000, 16383, BF16, 5
             (900, 65537, F16, 4), (2048, 1025, BF16, 3), (4096, 32769, F16, 2),
             (8192, 961, BF16, 3), (30001, 719, F16, 5), (4040, 641, BF16, 1),
             (768, 9, F16, 2), (65536, 9, BF16, 1), (8193, 1545, F16, 6),
-            (6145, 1545, BF16, 7)]
+            (6145, 1545, BF16, 7), (137, 11919, F16, 3), (237, 79545, BF16, 1)]
 
 
 @pytest.mark.parametrize("n,k,dtype,shift", LONG_MIS,

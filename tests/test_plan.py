@@ -234,11 +234,26 @@ def test_plan_shifted_window_only_for_misaligned_rows():
     (256, 512, (1, 2, 4, 1, 1, 0)),
     (3000, 1000, (2, 2, 4, 1, 1, 0)),      # >= 2048 rows: the short-row rule
     (3000, 1536, (2, 4, 4, 1, 1, 0)),      # 3 steps
-    (512, 4096, (1, 4, 4, 4, 1, 0)),       # <= 512 rows of 5..8 steps: 4 slices, 4 waves
+    (512, 4096, (1, 2, 4, 4, 1, 0)),       # <= 512 rows of 5..8 steps: 4 slices of two-slot batches
+    (256, 2049, (1, 2, 4, 4, 1, 0)),       # (4 full steps and a partial one)
     (640, 4096, (1, 8, 4, 1, 1, 0)),
+    (448, 1216, (1, 4, 2, 1, 1, 0)),       # 3..4 steps below 1024 rows: four slots, two waves
+    (900, 2048, (1, 4, 2, 1, 1, 0)),
+    (64, 1537, (1, 4, 2, 1, 1, 0)),
 ])
 def test_plan_aligned_rules(n, k, want):
     assert shape_of(plan(n, k, F16)[1]) == want, (n, k)
+
+
+def test_plan_long_misaligned_rows_below_320():
+    """Misaligned rows of at least 24 granule steps on 96..319 rows: one row
+    over eight slices of the shifted-window kernel; fewer rows, or shorter
+    ones, the plans of aligned rows with unaligned loads."""
+    for n, k in [(96, 11777), (137, 11919), (237, 79545), (319, 20001)]:
+        for dtype in (F16, BF16):
+            assert shape_of(plan(n, k, dtype)[1]) == (1, 4, 8, 8, 3, 0), (n, k)
+    for n, k in [(95, 11777), (320, 20001), (200, 11201), (96, 11713)]:
+        assert plan(n, k, BF16)[1].a_mode != 3, (n, k)
 
 
 @pytest.mark.parametrize("n,k,want", [
@@ -441,7 +456,7 @@ def test_plan_without_workspace_never_splits_across_workgroups():
                 (cfg1.variant, cfg1.grid, cfg1.kgroups), (n, k, dtype)
 
 
-@pytest.mark.parametrize("n,k", [(127, 65535), (96, 60000), (64, 32768), (32, 16384), (1, 16384)])
+@pytest.mark.parametrize("n,k", [(127, 65528), (96, 60000), (64, 32768), (32, 16384), (1, 16384), (95, 65535)])
 def test_plan_few_rows_split_in_workgroup(n, k):
     # fewer than 128 rows of >= 32 steps, not split across workgroups: one
     # row per 8-wave workgroup, eight k-slices
@@ -522,7 +537,7 @@ def test_plan_short_rows_edges():
     # three steps and more take the short-row rule
     assert shape_of(plan(2047, 1024, F16)[1]) == (1, 2, 4, 1, 1, 0)
     assert shape_of(plan(1024, 1536, F16)[1]) == (2, 4, 4, 1, 1, 0)
-    assert shape_of(plan(1023, 1536, F16)[1]) == (1, 8, 4, 1, 1, 0)
+    assert shape_of(plan(1023, 1536, F16)[1]) == (1, 4, 2, 1, 1, 0)    # below: four slots, two waves
     # 11..12 steps: one row of four slots below 6144 rows, four slices of
     # three from there; off 128-byte lines from 6144 rows: three rows, eight
     # slices of two
@@ -530,8 +545,10 @@ def test_plan_short_rows_edges():
     assert shape_of(plan(6144, 5632, F16)[1]) == (2, 3, 4, 4, 1, 0)
     assert shape_of(plan(6144, 5000, BF16)[1]) == (3, 2, 8, 8, 1, 0)
     assert shape_of(plan(6143, 5000, BF16)[1]) == (2, 3, 4, 4, 1, 0)
-    # below 1024 rows the earlier rules (one row, eight slots for <= 8 steps)
-    assert shape_of(plan(1023, 2048, BF16)[1]) == (1, 8, 4, 1, 1, 0)
+    # below 1024 rows the earlier rules (one row: four slots in two-wave
+    # workgroups for 3..4 steps, eight slots for 5..8 steps above 512 rows)
+    assert shape_of(plan(1023, 2048, BF16)[1]) == (1, 4, 2, 1, 1, 0)
+    assert shape_of(plan(1023, 3072, BF16)[1]) == (1, 8, 4, 1, 1, 0)
     assert shape_of(plan(1024, 2048, BF16)[1]) == (1, 4, 4, 1, 1, 0)
 
 
